@@ -1,0 +1,136 @@
+"""The CPU oracle for paged-KV attention decode.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The GPU library's code shares
+nothing with it, and nothing in the GPU library imports it.
+
+  * `paged_decode` -- fp64 gather + textbook softmax attention (oracle.c);
+  * `replay`       -- integer replays of block allocation, slots and split-K
+                      partitions (replay.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from . import replay  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+F16, BF16 = 0, 1
+
+
+def compile_c(src: str, out: str) -> str:
+    """gcc build of an oracle source: plain IEEE double, no FMA contraction."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                           "-ffp-contract=off", "-fno-fast-math", src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+        compile_c(SRC_PATH, LIB_PATH)
+    return LIB_PATH
+
+
+class OracleLib:
+    """ctypes view of one build of oracle.c (tests may load a planted-mistake copy)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.oracle_paged_decode.argtypes = [i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P,
+                                            ctypes.c_float, P, P, i]
+        lib.oracle_paged_decode.restype = i
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i
+        lib.oracle_decode_value.argtypes = [ctypes.c_uint16, i]
+        lib.oracle_decode_value.restype = ctypes.c_double
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return self.lib.oracle_max_threads()
+
+    def decode_value(self, bits: int, dtype: int) -> float:
+        return self.lib.oracle_decode_value(bits, dtype)
+
+    def paged_decode(self, q_bits, k_bits, v_bits, block_tables, context_lens, scale, *,
+                     num_kv_heads, block_size, dtype, tok_lo=None, tok_hi=None,
+                     nthreads=None, table_width=None):
+        """fp64 reference output [B][Hq][D] and lse [B][Hq] (natural log).
+
+        q_bits [B][Hq][D], k_bits/v_bits [NB][Hkv][bs][D]: raw uint16 storage of
+        fp16 (dtype=F16) or bf16 (dtype=BF16) values.  block_tables int32 [B][W],
+        context_lens int32 [B].  scale: the fp32 scale the GPU call receives.
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+        tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+        B, Hq, D = q_bits.shape
+        NB = k_bits.shape[0]
+        assert k_bits.shape == (NB, num_kv_heads, block_size, D) == v_bits.shape
+        assert tables.ndim == 2 and tables.shape[0] == B and ctx.shape == (B,)
+        lo = None if tok_lo is None else np.ascontiguousarray(tok_lo, dtype=np.int32)
+        hi = None if tok_hi is None else np.ascontiguousarray(tok_hi, dtype=np.int32)
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        width = tables.shape[1] if table_width is None else table_width
+        nt = self.max_threads() if nthreads is None else int(nthreads)
+        rc = self.lib.oracle_paged_decode(
+            B, Hq, num_kv_heads, D, block_size, NB, tables.shape[1], width, dtype,
+            _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(tables), _ptr(ctx), _ptr(lo), _ptr(hi),
+            ctypes.c_float(scale), _ptr(out), _ptr(lse), nt)
+        if rc != 0:
+            raise ValueError(f"oracle_paged_decode failed with status {rc}")
+        return out, lse
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    global _default
+    if _default is None:
+        _default = OracleLib(build())
+    return _default
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def decode_value(bits: int, dtype: int) -> float:
+    return default().decode_value(bits, dtype)
+
+
+def paged_decode(*args, **kw):
+    return default().paged_decode(*args, **kw)
+
+
+def _bits16(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def paged_decode_workload(wl, q, k, v, lib: OracleLib = None, **kw):
+    """Oracle on a DecodeWorkload with torch tensors q, k, v (any device)."""
+    dt = BF16 if wl.dtype == "bf16" else F16
+    lib = default() if lib is None else lib
+    return lib.paged_decode(_bits16(q), _bits16(k), _bits16(v), wl.block_tables, wl.context_lens,
+                        wl.scale, num_kv_heads=wl.num_kv_heads, block_size=wl.block_size,
+                        dtype=dt, **kw)

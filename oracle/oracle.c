@@ -1,0 +1,195 @@
+/*
+ * oracle.c -- the fp64 CPU oracle for paged-KV attention decode.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this file's library.  The GPU library shares no code,
+ * header, table or helper with it.
+ *
+ * What it computes (plain definition, written out):
+ *
+ *   For every sequence s and q head h, with kv head g = h / (Hq / Hkv):
+ *     1. gather: for each logical token t of the context, physical block
+ *        b = block_tables[s][t / bs] and slot t % bs give the rows
+ *        Kc[t] = k_cache[b][g][t % bs][:] and Vc[t] likewise.  The K/V of a
+ *        sequence sit in fixed-size physical blocks found through a per-sequence
+ *        logical->physical table and addressed indirectly
+ *        ("架构解构：推理引擎的四层抽象", PagedAttention section; the block count
+ *        ceil(n / block_size) is "LLM+Agent 全栈推理底座" 4.2, BlockManager.allocate).
+ *     2. textbook scaled dot-product attention for the one query row:
+ *        z[t] = scale * sum_d q[s][h][d] * Kc[t][d];  weights = softmax(z)
+ *        computed stably by subtracting max z;  out = sum_t weights[t] * Vc[t]
+ *        ("从零开始构建LLM推理引擎：模型执行器深度解析" 3.1, scaled_dot_product_attention:
+ *        scores q k^T / sqrt(d), stable softmax, weights times v).  Decode has a
+ *        single query at the newest position, so no causal mask applies.
+ *     3. lse[s][h] = max z + log(sum_t exp(z[t] - max z)), natural log.
+ *
+ *   All arithmetic is IEEE double.  The fp16/bf16 inputs are widened exactly by
+ *   decoding their bits here.  `scale` is the fp32 value the caller passes,
+ *   widened.  Tokens are summed in logical order t = lo, lo+1, ..., hi-1.
+ *
+ *   An optional token range [tok_lo[s], tok_hi[s]) restricts step 1 to part of
+ *   the context (clipped to [0, context_lens[s])).  An empty range gives
+ *   out = 0 and lse = -inf.  That reading of an empty context (the pages do not
+ *   speak of one) is also what the GPU library writes.
+ *
+ * Return value: 0 on success; -1 if a table entry that the context reaches is
+ * outside [0, num_blocks) or a context length is negative or exceeds the table
+ * width times block_size; -2 on a bad argument.  No output is defined on error.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+
+/* IEEE-754 binary16: 1 sign, 5 exponent, 10 fraction bits. */
+static double half_bits_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f + 1024), e - 25);     /* (1 + f/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent, 7 fraction bits (the top half of a binary32). */
+static double bf16_bits_to_double(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int f = b & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* f * 2^-126 * 2^-7 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f + 128), e - 134);     /* (1 + f/2^7) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_value(uint16_t bits, int dtype) {
+    return dtype == ORACLE_BF16 ? bf16_bits_to_double(bits) : half_bits_to_double(bits);
+}
+
+int oracle_paged_decode(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, int table_stride, int table_width, int dtype,
+    const uint16_t* q,            /* [B][Hq][D] */
+    const uint16_t* k_cache,      /* [NB][Hkv][bs][D] */
+    const uint16_t* v_cache,      /* [NB][Hkv][bs][D] */
+    const int32_t* block_tables,  /* [B][table_stride], table_width used */
+    const int32_t* context_lens,  /* [B] */
+    const int32_t* tok_lo,        /* nullable [B] */
+    const int32_t* tok_hi,        /* nullable [B] */
+    float scale,
+    double* out,                  /* [B][Hq][D] */
+    double* lse,                  /* [B][Hq], nullable */
+    int nthreads)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_q_heads % num_kv_heads != 0 || table_width > table_stride)
+        return -2;
+    const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads, D = head_dim;
+    const int bs = block_size, G = Hq / Hkv;
+    const double sc = (double)scale;
+
+    /* Check every table entry a context reaches before computing anything. */
+    for (int s = 0; s < B; ++s) {
+        int c = context_lens[s];
+        if (c < 0 || (int64_t)c > (int64_t)table_width * bs) return -1;
+        for (int j = 0; j < (c + bs - 1) / bs; ++j) {
+            int32_t b = block_tables[(int64_t)s * table_stride + j];
+            if (b < 0 || b >= num_blocks) return -1;
+        }
+    }
+
+    int status = 0;
+    const int64_t npairs = (int64_t)B * Hkv;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t pair = 0; pair < npairs; ++pair) {
+        const int s = (int)(pair / Hkv), g = (int)(pair % Hkv);
+        int lo = 0, hi = context_lens[s];
+        if (tok_lo && tok_lo[s] > lo) lo = tok_lo[s];
+        if (tok_hi && tok_hi[s] < hi) hi = tok_hi[s];
+        const int n = hi > lo ? hi - lo : 0;
+
+        if (n == 0) {
+            for (int hh = 0; hh < G; ++hh) {
+                int h = g * G + hh;
+                for (int d = 0; d < D; ++d) out[((int64_t)s * Hq + h) * D + d] = 0.0;
+                if (lse) lse[(int64_t)s * Hq + h] = -INFINITY;
+            }
+            continue;
+        }
+
+        /* Step 1: gather this sequence's K/V rows for kv head g into contiguous
+           fp64 arrays, token by token through the block table. */
+        double* Kc = (double*)malloc(sizeof(double) * (size_t)n * D);
+        double* Vc = (double*)malloc(sizeof(double) * (size_t)n * D);
+        double* z = (double*)malloc(sizeof(double) * (size_t)n);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!Kc || !Vc || !z || !acc) {
+            free(Kc); free(Vc); free(z); free(acc);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            status = -2;
+            continue;
+        }
+        for (int i = 0; i < n; ++i) {
+            const int t = lo + i;
+            const int64_t b = block_tables[(int64_t)s * table_stride + t / bs];
+            const int64_t row = ((b * Hkv + g) * bs + (t % bs)) * D;
+            for (int d = 0; d < D; ++d) {
+                Kc[(int64_t)i * D + d] = oracle_decode_value(k_cache[row + d], dtype);
+                Vc[(int64_t)i * D + d] = oracle_decode_value(v_cache[row + d], dtype);
+            }
+        }
+
+        /* Steps 2-3 for each q head of the group. */
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const uint16_t* qh = q + ((int64_t)s * Hq + h) * D;
+            double m = -INFINITY;
+            for (int i = 0; i < n; ++i) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += oracle_decode_value(qh[d], dtype) * Kc[(int64_t)i * D + d];
+                z[i] = sc * dot;
+                if (z[i] > m) m = z[i];
+            }
+            double Z = 0.0;
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int i = 0; i < n; ++i) {
+                const double w = exp(z[i] - m);
+                Z += w;
+                for (int d = 0; d < D; ++d) acc[d] += w * Vc[(int64_t)i * D + d];
+            }
+            for (int d = 0; d < D; ++d) out[((int64_t)s * Hq + h) * D + d] = acc[d] / Z;
+            if (lse) lse[(int64_t)s * Hq + h] = m + log(Z);
+        }
+        free(Kc); free(Vc); free(z); free(acc);
+    }
+    return status;
+}
+
+/* Threads OpenMP would use for nthreads <= 0 requests (reported by the bench). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,183 @@
+"""Integer replays of the paged-KV bookkeeping, in pure Python.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg use this module.  It shares nothing with the GPU library.
+
+What is replayed, from the definitions:
+
+  * blocks a sequence of n tokens holds: ceil(n / block_size), i.e.
+    (n + block_size - 1) // block_size ("LLM+Agent 全栈推理底座" 4.2,
+    BlockManager.allocate);
+  * allocation pops the LAST element of a free list (the same section's
+    BlockManager takes `free_blocks.pop()`).  The pool's free list starts as the
+    seeded allocation order reversed, so the first block handed out is
+    alloc_order[0], the second alloc_order[1], and so on.  A fixed device pool
+    cannot grow, so where that section grows the pool this replay reports
+    exhaustion instead, with no change to any state;
+  * a token at logical position t of a sequence lives in slot
+    table[t // bs] * bs + t % bs, the block table being the logical->physical map
+    ("架构解构：推理引擎的四层抽象", PagedAttention section);
+  * blocks shared by several sequences (a common prefix, "LLM+Agent 全栈推理底座"
+    2.2 and 4.4 prefix reuse) carry a reference count.  Appending into a shared,
+    partly filled tail block first copies its used slots into a fresh block
+    (copy-on-write), so the other holders never see the write;
+  * freeing a sequence drops one reference from each of its blocks in logical
+    order; a block whose count reaches zero is pushed back onto the free list,
+    so the next allocation reuses the last block released;
+  * split-K partitions of a context of n tokens with partition size P:
+    ceil(n / P) partitions, partition p covering [p*P, min((p+1)*P, n)); work
+    items are enumerated in (sequence, kv head, partition) order.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+def ceil_div(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    return ceil_div(num_tokens, block_size)
+
+
+class PoolError(Exception):
+    def __init__(self, kind: str, msg: str = ""):
+        super().__init__(f"{kind}: {msg}")
+        self.kind = kind          # "EINVAL" | "ENOMEM"
+
+
+class AppendItem(tuple):
+    """(seq, slot, table_pos, new_block, cow_src, cow_ntok, new_len)."""
+    __slots__ = ()
+
+    def __new__(cls, seq, slot, tpos, new_block, cow_src, cow_n, new_len):
+        return tuple.__new__(cls, (seq, slot, tpos, new_block, cow_src, cow_n, new_len))
+
+
+class PoolReplay:
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int,
+                 max_blocks_per_seq: int, alloc_order: Optional[Sequence[int]] = None):
+        self.num_blocks = num_blocks
+        self.bs = block_size
+        self.max_seqs = max_seqs
+        self.max_blocks_per_seq = max_blocks_per_seq
+        order = list(range(num_blocks)) if alloc_order is None else [int(b) for b in alloc_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise PoolError("EINVAL", "alloc_order is not a permutation")
+        self.free: List[int] = list(reversed(order))       # pop() yields order[0] first
+        self.ref = [0] * num_blocks
+        self.seqs: Dict[int, Tuple[List[int], int]] = {}
+
+    # -- sequences -------------------------------------------------------
+    def _new_id(self) -> int:
+        for i in range(self.max_seqs):
+            if i not in self.seqs:
+                return i
+        raise PoolError("ENOMEM", "no free sequence slot")
+
+    def add_seq(self) -> int:
+        sid = self._new_id()
+        self.seqs[sid] = ([], 0)
+        return sid
+
+    def import_seq(self, blocks: Sequence[int], length: int) -> int:
+        blocks = [int(b) for b in blocks]
+        if length < 0 or len(blocks) != blocks_needed(length, self.bs):
+            raise PoolError("EINVAL", "block count does not match length")
+        if len(blocks) > self.max_blocks_per_seq or len(set(blocks)) != len(blocks):
+            raise PoolError("EINVAL", "bad block list")
+        for b in blocks:
+            if not 0 <= b < self.num_blocks:
+                raise PoolError("EINVAL", "block id out of range")
+        sid = self._new_id()
+        for b in blocks:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        self.seqs[sid] = (blocks, length)
+        return sid
+
+    def fork(self, src: int) -> int:
+        if src not in self.seqs:
+            raise PoolError("EINVAL", "unknown sequence")
+        sid = self._new_id()
+        blocks, length = self.seqs[src]
+        for b in blocks:
+            self.ref[b] += 1
+        self.seqs[sid] = (list(blocks), length)
+        return sid
+
+    def free_seq(self, sid: int) -> None:
+        if sid not in self.seqs:
+            raise PoolError("EINVAL", "unknown sequence")
+        blocks, _ = self.seqs.pop(sid)
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    # -- append one token to each listed sequence (all-or-nothing) --------
+    def append(self, seq_ids: Sequence[int]) -> List[AppendItem]:
+        ids = [int(s) for s in seq_ids]
+        if len(set(ids)) != len(ids):
+            raise PoolError("EINVAL", "duplicate sequence id")
+        need = 0
+        for s in ids:
+            if s not in self.seqs:
+                raise PoolError("EINVAL", "unknown sequence")
+            blocks, t = self.seqs[s]
+            if t % self.bs == 0:
+                if t // self.bs >= self.max_blocks_per_seq:
+                    raise PoolError("EINVAL", "sequence reached max_blocks_per_seq")
+                need += 1
+            elif self.ref[blocks[-1]] > 1:
+                need += 1
+        if need > len(self.free):
+            raise PoolError("ENOMEM", "pool exhausted")
+        items = []
+        for s in ids:
+            blocks, t = self.seqs[s]
+            tpos, off = divmod(t, self.bs)
+            new_block, cow_src, cow_n = -1, -1, 0
+            if off == 0:
+                new_block = self.free.pop()
+                self.ref[new_block] = 1
+                blocks.append(new_block)
+            elif self.ref[blocks[-1]] > 1:
+                new_block = self.free.pop()
+                self.ref[new_block] = 1
+                cow_src, cow_n = blocks[-1], off
+                self.ref[cow_src] -= 1
+                blocks[-1] = new_block
+            slot = blocks[tpos] * self.bs + off
+            self.seqs[s] = (blocks, t + 1)
+            items.append(AppendItem(s, slot, tpos, new_block, cow_src, cow_n, t + 1))
+        return items
+
+    # -- views ------------------------------------------------------------
+    def tables(self, width: Optional[int] = None):
+        """(block_tables [max_seqs][width] with -1 fill, context_lens [max_seqs])."""
+        w = self.max_blocks_per_seq if width is None else width
+        tab = [[-1] * w for _ in range(self.max_seqs)]
+        lens = [0] * self.max_seqs
+        for s, (blocks, length) in self.seqs.items():
+            tab[s][:len(blocks)] = blocks
+            lens[s] = length
+        return tab, lens
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+
+def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int):
+    """Split-K work items (seq, kv_head, partition, tok_lo, tok_hi) in order."""
+    if partition_size <= 0:
+        raise ValueError("partition_size must be positive")
+    items = []
+    for s, n in enumerate(context_lens):
+        n = int(n)
+        for g in range(num_kv_heads):
+            for p in range(ceil_div(n, partition_size)):
+                items.append((s, g, p, p * partition_size, min((p + 1) * partition_size, n)))
+    return items

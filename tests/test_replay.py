@@ -1,0 +1,126 @@
+"""The oracle's integer replays against the page's allocation rule and invariants."""
+import json
+import os
+import random
+
+import pytest
+
+from oracle import replay as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "blockmanager_allocate.json")
+
+
+def test_golden_blockmanager_allocate():
+    g = json.load(open(GOLDEN))
+    bs = g["block_size"]
+    # The page's free list [0..9] popped from the end == alloc_order [9, 8, ..., 0].
+    order = list(reversed(g["free_blocks"]))
+    pool = R.PoolReplay(len(order), bs, max_seqs=8, max_blocks_per_seq=8, alloc_order=order)
+    for call in g["calls"]:
+        assert R.blocks_needed(call["num_tokens"], bs) == call["needed"]
+        sid = pool.add_seq()
+        assert sid == call["seq_id"]
+        for _ in range(call["num_tokens"]):
+            pool.append([sid])
+        assert pool.seqs[sid][0] == call["blocks"]
+    assert sorted(pool.free) == g["free_blocks_after"]
+    assert list(reversed(pool.free)) == sorted(g["free_blocks_after"], reverse=True)
+
+
+@pytest.mark.parametrize("n,bs,want", [(0, 16, 0), (1, 16, 1), (16, 16, 1), (17, 16, 2),
+                                       (32, 32, 1), (33, 32, 2), (131072, 16, 8192)])
+def test_blocks_needed(n, bs, want):
+    assert R.blocks_needed(n, bs) == want
+
+
+def test_append_slots_and_tables():
+    pool = R.PoolReplay(8, 4, max_seqs=2, max_blocks_per_seq=4, alloc_order=[5, 2, 7, 0, 1, 3, 4, 6])
+    a, b = pool.add_seq(), pool.add_seq()
+    items = []
+    for _ in range(5):
+        items += pool.append([a, b])
+    # a takes 5, b takes 2 (t = 0); a takes 7, b takes 0 (t = 4).
+    assert pool.seqs[a] == ([5, 7], 5) and pool.seqs[b] == ([2, 0], 5)
+    slots_a = [it[1] for it in items if it[0] == a]
+    assert slots_a == [20, 21, 22, 23, 28]
+    tab, lens = pool.tables(width=4)
+    assert tab == [[5, 7, -1, -1], [2, 0, -1, -1]] and lens == [5, 5]
+
+
+def test_append_all_or_nothing():
+    pool = R.PoolReplay(3, 2, max_seqs=4, max_blocks_per_seq=4, alloc_order=[0, 1, 2])
+    ids = [pool.add_seq() for _ in range(4)]
+    pool.append(ids[:3])                         # three blocks taken, pool empty
+    before = (list(pool.free), {k: (list(v[0]), v[1]) for k, v in pool.seqs.items()})
+    with pytest.raises(R.PoolError) as e:
+        pool.append(ids)                         # seq 3 needs a block
+    assert e.value.kind == "ENOMEM"
+    assert (list(pool.free), {k: (list(v[0]), v[1]) for k, v in pool.seqs.items()}) == before
+    pool.append(ids[:3])                         # t = 1 fits in each tail block
+    with pytest.raises(R.PoolError):
+        pool.append([0, 0])
+
+
+def test_fork_copy_on_write():
+    pool = R.PoolReplay(6, 4, max_seqs=3, max_blocks_per_seq=3, alloc_order=[3, 1, 4, 0, 5, 2])
+    a = pool.add_seq()
+    for _ in range(6):
+        pool.append([a])                         # blocks [3, 1], len 6
+    b = pool.fork(a)
+    assert pool.ref[3] == 2 and pool.ref[1] == 2
+    (it,) = pool.append([b])                     # b's tail block 1 is shared and partly full
+    seq, slot, tpos, new_block, cow_src, cow_n, new_len = it
+    assert (tpos, new_block, cow_src, cow_n, new_len) == (1, 4, 1, 2, 7)
+    assert slot == 4 * 4 + 2
+    assert pool.seqs[b][0] == [3, 4] and pool.seqs[a][0] == [3, 1]
+    assert pool.ref[1] == 1 and pool.ref[4] == 1 and pool.ref[3] == 2
+    (it,) = pool.append([a])                     # a's tail is private again: no copy
+    assert it[3] == -1 and it[4] == -1
+    pool.free_seq(a)                             # 3 still held by b; 1 freed
+    assert pool.free[-1] == 1 and pool.ref[3] == 1
+
+
+def test_free_returns_blocks_lifo():
+    pool = R.PoolReplay(4, 2, max_seqs=2, max_blocks_per_seq=4, alloc_order=[0, 1, 2, 3])
+    a = pool.add_seq()
+    for _ in range(5):
+        pool.append([a])                         # blocks [0, 1, 2]
+    pool.free_seq(a)                             # pushed in logical order: 0, 1, 2
+    b = pool.add_seq()
+    pool.append([b])
+    assert pool.seqs[b][0] == [2]                # last released is reused first
+
+
+def test_random_ops_conserve_blocks():
+    rnd = random.Random(0)
+    pool = R.PoolReplay(64, 4, max_seqs=8, max_blocks_per_seq=16)
+    live = []
+    for _ in range(2000):
+        op = rnd.random()
+        try:
+            if op < 0.1 and len(live) < 8:
+                live.append(pool.add_seq())
+            elif op < 0.15 and live and len(live) < 8:
+                live.append(pool.fork(rnd.choice(live)))
+            elif op < 0.2 and live:
+                s = rnd.choice(live); live.remove(s); pool.free_seq(s)
+            elif live:
+                pool.append(rnd.sample(live, rnd.randint(1, len(live))))
+        except R.PoolError:
+            pass
+        held = {}
+        for blocks, n in pool.seqs.values():
+            assert len(blocks) == R.blocks_needed(n, 4)
+            for b in blocks:
+                held[b] = held.get(b, 0) + 1
+        assert all(pool.ref[b] == c for b, c in held.items())
+        assert len(held) + len(pool.free) == 64
+        assert not set(held) & set(pool.free)
+
+
+def test_plan_enumeration():
+    items = R.plan([0, 5, 1024, 1025], num_kv_heads=2, partition_size=512)
+    assert items[:2] == [(1, 0, 0, 0, 5), (1, 1, 0, 0, 5)]
+    assert (2, 1, 1, 512, 1024) in items and (3, 0, 2, 1024, 1025) in items
+    assert len(items) == 2 * (1 + 2 + 3)
+    assert items == sorted(items)
