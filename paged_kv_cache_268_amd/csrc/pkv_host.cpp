@@ -1,0 +1,633 @@
+// pkv_host.cpp -- host side of libpkv.so: the C ABI of include/pkv.h.
+//
+// Block pool bookkeeping follows the page's BlockManager ("LLM+Agent 全栈推理底座",
+// 4.2): fixed-size blocks, ceil(n / block_size) blocks per sequence, blocks
+// taken by popping the end of a free list.  The device pool is fixed, so an
+// empty free list is an error (PKV_ENOMEM), never growth.  The block table is
+// kept here on the host and published to the device between kernel launches
+// ("架构解构：推理引擎的四层抽象", PagedAttention section and runtime layer).
+// Shared blocks (prefix reuse, "LLM+Agent 全栈推理底座" 2.2 / 4.4) carry a
+// reference count and are copied before a write (copy-on-write).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+    return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kRing = 8;   // pinned staging slots for kv_append metadata
+
+}  // namespace
+
+struct pkv_pool {
+    pkv_pool_desc d{};
+    void* k_cache = nullptr;
+    void* v_cache = nullptr;
+
+    // Free list: a stack (allocation pops the back).  Removing a block from
+    // the middle (kv_seq_import) leaves a tombstone (-1) so the order of the
+    // rest is kept; pos[b] is b's index in the stack or -1.
+    std::vector<int32_t> stack;
+    std::vector<int32_t> pos;
+    int32_t num_free = 0;
+
+    std::vector<int32_t> ref;                    // holders per block
+    std::vector<std::vector<int32_t>> blocks;    // per sequence row
+    std::vector<int32_t> len;
+    std::vector<uint8_t> live;
+    int32_t num_live = 0;
+
+    struct Slot {
+        pkv::AppendItem* host = nullptr;
+        hipEvent_t ev = nullptr;
+        bool pending = false;
+    };
+    Slot ring[kRing];
+    int next = 0;
+    bool ring_ready = false;
+
+    int32_t* tab_host = nullptr;                 // staging for kv_write_tables
+    hipEvent_t tab_ev = nullptr;
+    bool tab_pending = false;
+
+    int32_t pop_free() {
+        while (!stack.empty() && stack.back() < 0) stack.pop_back();
+        const int32_t b = stack.back();
+        stack.pop_back();
+        pos[b] = -1;
+        --num_free;
+        return b;
+    }
+    void push_free(int32_t b) {
+        pos[b] = (int32_t)stack.size();
+        stack.push_back(b);
+        ++num_free;
+    }
+    void remove_free(int32_t b) {
+        stack[pos[b]] = -1;
+        pos[b] = -1;
+        --num_free;
+        if (stack.size() > 64 && (size_t)num_free * 2 < stack.size()) compact();
+    }
+    void compact() {
+        std::vector<int32_t> s;
+        s.reserve(num_free);
+        for (int32_t b : stack)
+            if (b >= 0) {
+                pos[b] = (int32_t)s.size();
+                s.push_back(b);
+            }
+        stack.swap(s);
+    }
+    int32_t new_row() const {
+        for (int32_t i = 0; i < d.max_seqs; ++i)
+            if (!live[i]) return i;
+        return -1;
+    }
+    bool valid_seq(int32_t s) const { return s >= 0 && s < d.max_seqs && live[s]; }
+};
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+// --------------------------------------------------------------------------
+// Pool
+// --------------------------------------------------------------------------
+
+int kv_block_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cache,
+                         const int32_t* alloc_order, pkv_pool** out) {
+    if (!desc || !out) return fail(PKV_EINVAL, "kv_block_pool_create: null desc or out");
+    const pkv_pool_desc& d = *desc;
+    if (d.num_blocks < 1 || d.num_kv_heads < 1 || d.max_seqs < 1 || d.max_blocks_per_seq < 1)
+        return fail(PKV_EINVAL, "kv_block_pool_create: sizes must be positive");
+    if (d.block_size != 16 && d.block_size != 32)
+        return fail(PKV_EUNSUPPORTED, "block_size %d (16 or 32)", d.block_size);
+    if (d.head_dim != 64 && d.head_dim != 128)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d (64 or 128)", d.head_dim);
+    if (d.kv_dtype != PKV_F16 && d.kv_dtype != PKV_BF16)
+        return fail(PKV_EUNSUPPORTED, "kv_dtype %d (PKV_F16 or PKV_BF16)", d.kv_dtype);
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(PKV_EINVAL, "k_cache / v_cache must be 16-byte aligned");
+    std::vector<uint8_t> seen(d.num_blocks, 0);
+    if (alloc_order) {
+        for (int32_t i = 0; i < d.num_blocks; ++i) {
+            const int32_t b = alloc_order[i];
+            if (b < 0 || b >= d.num_blocks || seen[b])
+                return fail(PKV_EINVAL, "alloc_order is not a permutation (entry %d = %d)", i, b);
+            seen[b] = 1;
+        }
+    }
+    pkv_pool* p = new pkv_pool;
+    p->d = d;
+    p->k_cache = k_cache;
+    p->v_cache = v_cache;
+    p->stack.resize(d.num_blocks);
+    p->pos.resize(d.num_blocks);
+    for (int32_t i = 0; i < d.num_blocks; ++i) {
+        const int32_t b = alloc_order ? alloc_order[d.num_blocks - 1 - i] : d.num_blocks - 1 - i;
+        p->stack[i] = b;
+        p->pos[b] = i;
+    }
+    p->num_free = d.num_blocks;
+    p->ref.assign(d.num_blocks, 0);
+    p->blocks.assign(d.max_seqs, {});
+    p->len.assign(d.max_seqs, 0);
+    p->live.assign(d.max_seqs, 0);
+    *out = p;
+    return PKV_OK;
+}
+
+void kv_block_pool_destroy(pkv_pool* p) {
+    if (!p) return;
+    for (auto& s : p->ring) {
+        if (s.pending) (void)hipEventSynchronize(s.ev);
+        if (s.ev) (void)hipEventDestroy(s.ev);
+        if (s.host) (void)hipHostFree(s.host);
+    }
+    if (p->tab_pending) (void)hipEventSynchronize(p->tab_ev);
+    if (p->tab_ev) (void)hipEventDestroy(p->tab_ev);
+    if (p->tab_host) (void)hipHostFree(p->tab_host);
+    delete p;
+}
+
+int kv_seq_add(pkv_pool* p, int32_t* seq_id_out) {
+    if (!p || !seq_id_out) return fail(PKV_EINVAL, "kv_seq_add: null argument");
+    const int32_t s = p->new_row();
+    if (s < 0) return fail(PKV_ENOMEM, "kv_seq_add: all %d sequence rows in use", p->d.max_seqs);
+    p->live[s] = 1;
+    p->blocks[s].clear();
+    p->len[s] = 0;
+    ++p->num_live;
+    *seq_id_out = s;
+    return PKV_OK;
+}
+
+int kv_seq_import(pkv_pool* p, int32_t len, const int32_t* block_ids, int32_t n_blocks,
+                  int32_t* seq_id_out) {
+    if (!p || !seq_id_out || (n_blocks > 0 && !block_ids)) return fail(PKV_EINVAL, "kv_seq_import: null argument");
+    const int32_t bs = p->d.block_size;
+    if (len < 0 || n_blocks != ceil_div(len, bs))
+        return fail(PKV_EINVAL, "kv_seq_import: %d blocks for %d tokens (need %lld)", n_blocks, len,
+                    (long long)ceil_div(len, bs));
+    if (n_blocks > p->d.max_blocks_per_seq)
+        return fail(PKV_EINVAL, "kv_seq_import: %d blocks > max_blocks_per_seq %d", n_blocks, p->d.max_blocks_per_seq);
+    std::vector<int32_t> ids(block_ids, block_ids + n_blocks);
+    std::vector<int32_t> sorted = ids;
+    std::sort(sorted.begin(), sorted.end());
+    for (size_t i = 0; i < sorted.size(); ++i) {
+        if (sorted[i] < 0 || sorted[i] >= p->d.num_blocks)
+            return fail(PKV_EINVAL, "kv_seq_import: block id %d out of range", sorted[i]);
+        if (i && sorted[i] == sorted[i - 1]) return fail(PKV_EINVAL, "kv_seq_import: block %d repeated", sorted[i]);
+    }
+    const int32_t s = p->new_row();
+    if (s < 0) return fail(PKV_ENOMEM, "kv_seq_import: all %d sequence rows in use", p->d.max_seqs);
+    for (int32_t b : ids) {
+        if (p->ref[b] == 0) p->remove_free(b);
+        ++p->ref[b];
+    }
+    p->live[s] = 1;
+    p->blocks[s] = ids;
+    p->len[s] = len;
+    ++p->num_live;
+    *seq_id_out = s;
+    return PKV_OK;
+}
+
+int kv_seq_fork(pkv_pool* p, int32_t src, int32_t* seq_id_out) {
+    if (!p || !seq_id_out) return fail(PKV_EINVAL, "kv_seq_fork: null argument");
+    if (!p->valid_seq(src)) return fail(PKV_EINVAL, "kv_seq_fork: unknown sequence %d", src);
+    const int32_t s = p->new_row();
+    if (s < 0) return fail(PKV_ENOMEM, "kv_seq_fork: all %d sequence rows in use", p->d.max_seqs);
+    for (int32_t b : p->blocks[src]) ++p->ref[b];
+    p->live[s] = 1;
+    p->blocks[s] = p->blocks[src];
+    p->len[s] = p->len[src];
+    ++p->num_live;
+    *seq_id_out = s;
+    return PKV_OK;
+}
+
+int kv_seq_free(pkv_pool* p, int32_t s) {
+    if (!p) return fail(PKV_EINVAL, "kv_seq_free: null pool");
+    if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_seq_free: unknown sequence %d", s);
+    for (int32_t b : p->blocks[s])
+        if (--p->ref[b] == 0) p->push_free(b);
+    p->blocks[s].clear();
+    p->len[s] = 0;
+    p->live[s] = 0;
+    --p->num_live;
+    return PKV_OK;
+}
+
+int kv_seq_info(const pkv_pool* p, int32_t s, int32_t* len_out, int32_t* block_ids_out, int32_t cap,
+                int32_t* n_blocks_out) {
+    if (!p) return fail(PKV_EINVAL, "kv_seq_info: null pool");
+    if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_seq_info: unknown sequence %d", s);
+    const auto& b = p->blocks[s];
+    if (len_out) *len_out = p->len[s];
+    if (n_blocks_out) *n_blocks_out = (int32_t)b.size();
+    if (block_ids_out)
+        for (int32_t i = 0; i < cap && i < (int32_t)b.size(); ++i) block_ids_out[i] = b[i];
+    return PKV_OK;
+}
+
+int kv_pool_stats(const pkv_pool* p, int32_t* num_free_out, int32_t* num_seqs_out, int32_t block,
+                  int32_t* refcount_out) {
+    if (!p) return fail(PKV_EINVAL, "kv_pool_stats: null pool");
+    if (num_free_out) *num_free_out = p->num_free;
+    if (num_seqs_out) *num_seqs_out = p->num_live;
+    if (block >= 0) {
+        if (block >= p->d.num_blocks) return fail(PKV_EINVAL, "kv_pool_stats: block %d out of range", block);
+        if (refcount_out) *refcount_out = p->ref[block];
+    }
+    return PKV_OK;
+}
+
+static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::AppendItem* items, bool* any_copy) {
+    if (n < 0 || (n > 0 && !seq_ids)) return fail(PKV_EINVAL, "kv_reserve: bad n or seq_ids");
+    const int32_t bs = p->d.block_size;
+    std::vector<uint8_t> mark(p->d.max_seqs, 0);
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_reserve: unknown sequence %d", s);
+        if (mark[s]) return fail(PKV_EINVAL, "kv_reserve: sequence %d listed twice", s);
+        mark[s] = 1;
+        const int32_t t = p->len[s];
+        if (t % bs == 0) {
+            if (t / bs >= p->d.max_blocks_per_seq)
+                return fail(PKV_EINVAL, "kv_reserve: sequence %d is full (%d blocks)", s, p->d.max_blocks_per_seq);
+            ++need;
+        } else if (p->ref[p->blocks[s].back()] > 1) {
+            ++need;
+        }
+    }
+    if (need > p->num_free)
+        return fail(PKV_ENOMEM, "kv_reserve: need %lld blocks, %d free", (long long)need, p->num_free);
+    bool copy = false;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        auto& blk = p->blocks[s];
+        const int32_t t = p->len[s];
+        const int32_t tpos = t / bs, off = t % bs;
+        pkv::AppendItem it{s, 0, tpos, -1, -1, 0, t + 1};
+        if (off == 0) {
+            it.new_block = p->pop_free();
+            p->ref[it.new_block] = 1;
+            blk.push_back(it.new_block);
+        } else if (p->ref[blk.back()] > 1) {
+            it.new_block = p->pop_free();
+            p->ref[it.new_block] = 1;
+            it.cow_src = blk.back();
+            it.cow_ntok = off;
+            --p->ref[it.cow_src];
+            blk.back() = it.new_block;
+            copy = true;
+        }
+        it.slot = blk[tpos] * bs + off;
+        p->len[s] = t + 1;
+        if (items) items[i] = it;
+    }
+    if (any_copy) *any_copy = copy;
+    return PKV_OK;
+}
+
+int kv_reserve(pkv_pool* p, int32_t n, const int32_t* seq_ids, int32_t* items_out) {
+    if (!p) return fail(PKV_EINVAL, "kv_reserve: null pool");
+    static_assert(sizeof(pkv::AppendItem) == 7 * sizeof(int32_t), "item layout");
+    return reserve_impl(p, n, seq_ids, reinterpret_cast<pkv::AppendItem*>(items_out), nullptr);
+}
+
+static int ensure_ring(pkv_pool* p) {
+    if (p->ring_ready) return PKV_OK;
+    for (auto& s : p->ring) {
+        hipError_t e = hipHostMalloc((void**)&s.host, sizeof(pkv::AppendItem) * (size_t)p->d.max_seqs,
+                                     hipHostMallocCoherent | hipHostMallocMapped);
+        if (e != hipSuccess) return fail_hip(e, "hipHostMalloc (append staging)");
+        e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+        if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    }
+    p->ring_ready = true;
+    return PKV_OK;
+}
+
+int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new, const void* v_new,
+              int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream) {
+    if (!p) return fail(PKV_EINVAL, "kv_append: null pool");
+    if (n == 0) return PKV_OK;
+    if (!k_new || !v_new || !block_tables || !context_lens || !p->k_cache || !p->v_cache)
+        return fail(PKV_EINVAL, "kv_append: null device pointer");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return fail(PKV_EINVAL, "kv_append: k_new / v_new must be 16-byte aligned");
+    if (n < 0 || n > p->d.max_seqs) return fail(PKV_EINVAL, "kv_append: n = %d", n);
+    int rc = ensure_ring(p);
+    if (rc) return rc;
+    auto& slot = p->ring[p->next];
+    if (slot.pending) {
+        hipError_t e = hipEventSynchronize(slot.ev);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (append staging)");
+        slot.pending = false;
+    }
+    bool any_copy = false;
+    rc = reserve_impl(p, n, seq_ids, slot.host, &any_copy);
+    if (rc) return rc;
+    pkv::AppendArgs a{};
+    a.items = slot.host;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = p->k_cache;
+    a.v_cache = p->v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.n = n;
+    a.num_kv_heads = p->d.num_kv_heads;
+    a.head_dim = p->d.head_dim;
+    a.block_size = p->d.block_size;
+    a.table_stride = p->d.max_blocks_per_seq;
+    hipError_t e = pkv::launch_append(a, any_copy, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "kv_append launch (pool state now ahead of the device)");
+    e = hipEventRecord(slot.ev, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+    slot.pending = true;
+    p->next = (p->next + 1) % kRing;
+    return PKV_OK;
+}
+
+int kv_write_tables(pkv_pool* p, int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream) {
+    if (!p || !block_tables || !context_lens) return fail(PKV_EINVAL, "kv_write_tables: null argument");
+    const size_t W = p->d.max_blocks_per_seq, S = p->d.max_seqs;
+    if (!p->tab_host) {
+        hipError_t e = hipHostMalloc((void**)&p->tab_host, sizeof(int32_t) * S * (W + 1), hipHostMallocDefault);
+        if (e != hipSuccess) return fail_hip(e, "hipHostMalloc (table staging)");
+        e = hipEventCreateWithFlags(&p->tab_ev, hipEventDisableTiming);
+        if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    }
+    if (p->tab_pending) {
+        hipError_t e = hipEventSynchronize(p->tab_ev);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (table staging)");
+        p->tab_pending = false;
+    }
+    int32_t* tab = p->tab_host;
+    int32_t* lens = p->tab_host + S * W;
+    for (size_t s = 0; s < S; ++s) {
+        const auto& b = p->blocks[s];
+        for (size_t j = 0; j < W; ++j) tab[s * W + j] = j < b.size() ? b[j] : -1;
+        lens[s] = p->len[s];
+    }
+    hipError_t e = hipMemcpyAsync(block_tables, tab, sizeof(int32_t) * S * W, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(context_lens, lens, sizeof(int32_t) * S, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipEventRecord(p->tab_ev, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "kv_write_tables copy");
+    p->tab_pending = true;
+    return PKV_OK;
+}
+
+int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t table_stride, int32_t table_width,
+                       const int32_t* context_lens, int32_t num_blocks, int32_t block_size) {
+    if (n_seqs < 0 || (n_seqs > 0 && (!block_tables || !context_lens)) || block_size <= 0 ||
+        table_width > table_stride)
+        return fail(PKV_EINVAL, "kv_validate_tables: bad arguments");
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        const int32_t c = context_lens[s];
+        if (c < 0) return fail(PKV_EINVAL, "kv_validate_tables: sequence %d has length %d", s, c);
+        const int64_t nb = ceil_div(c, block_size);
+        if (nb > table_width)
+            return fail(PKV_EINVAL, "kv_validate_tables: sequence %d needs %lld blocks > width %d", s,
+                        (long long)nb, table_width);
+        for (int64_t j = 0; j < nb; ++j) {
+            const int32_t b = block_tables[(int64_t)s * table_stride + j];
+            if (b < 0 || b >= num_blocks)
+                return fail(PKV_EINVAL, "kv_validate_tables: sequence %d entry %lld = %d out of [0, %d)", s,
+                            (long long)j, b, num_blocks);
+        }
+    }
+    return PKV_OK;
+}
+
+// --------------------------------------------------------------------------
+// Decode
+// --------------------------------------------------------------------------
+
+namespace {
+
+struct Plan {
+    int32_t part_size = 0;
+    int32_t max_parts = 0;
+    int32_t group_pad = 0;
+    bool bf16 = false;
+    int32_t out_kind = pkv::kOutF32;
+    size_t ws_out_bytes = 0;
+    size_t ws_bytes = 0;
+};
+
+constexpr int32_t kDefaultPartition = 512;
+
+int resolve(const pkv_attn_desc* d, Plan* pl) {
+    if (!d) return fail(PKV_EINVAL, "null descriptor");
+    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_context_len < 0)
+        return fail(PKV_EINVAL, "descriptor: bad sizes");
+    if (d->num_q_heads % d->num_kv_heads)
+        return fail(PKV_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d", d->num_q_heads, d->num_kv_heads);
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (G > 8) return fail(PKV_EUNSUPPORTED, "q heads per kv head = %d (at most 8)", G);
+    if (d->head_dim != 64 && d->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+    if (d->block_size != 16 && d->block_size != 32)
+        return fail(PKV_EUNSUPPORTED, "block_size %d (16 or 32)", d->block_size);
+    if (d->kv_dtype != PKV_F16 && d->kv_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "kv_dtype %d", d->kv_dtype);
+    if (d->q_dtype != d->kv_dtype) return fail(PKV_EUNSUPPORTED, "q_dtype must equal kv_dtype");
+    if (d->out_dtype == PKV_F32)
+        pl->out_kind = pkv::kOutF32;
+    else if (d->out_dtype == d->q_dtype)
+        pl->out_kind = d->q_dtype == PKV_BF16 ? pkv::kOutBF16 : pkv::kOutF16;
+    else
+        return fail(PKV_EUNSUPPORTED, "out_dtype must be PKV_F32 or equal q_dtype");
+    if (d->num_blocks < 0) return fail(PKV_EINVAL, "num_blocks %d", d->num_blocks);
+    const int64_t need_w = ceil_div(d->max_context_len, d->block_size);
+    if (d->table_stride < need_w)
+        return fail(PKV_EINVAL, "table_stride %d < ceil(max_context_len / block_size) = %lld", d->table_stride,
+                    (long long)need_w);
+    int32_t P = d->partition_size;
+    if (P == 0) {
+        // One partition when every context fits in the default size, else the default.
+        const int32_t m = std::max(d->max_context_len, 1);
+        P = m <= kDefaultPartition ? (int32_t)(ceil_div(m, d->block_size) * d->block_size) : kDefaultPartition;
+        P = (int32_t)(ceil_div(P, d->block_size) * d->block_size);
+    }
+    if (P < 16 || P % d->block_size)
+        return fail(PKV_EINVAL, "partition_size %d must be a positive multiple of block_size %d", P, d->block_size);
+    pl->part_size = P;
+    pl->max_parts = (int32_t)std::max<int64_t>(1, ceil_div(d->max_context_len, P));
+    pl->group_pad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+    pl->bf16 = d->kv_dtype == PKV_BF16;
+    if (pl->max_parts > 1) {
+        const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_parts;
+        pl->ws_out_bytes = (rows * d->head_dim * sizeof(float) + 255) / 256 * 256;
+        pl->ws_bytes = pl->ws_out_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+    }
+    return PKV_OK;
+}
+
+int check_ptrs(const pkv_attn_desc* d, const Plan& pl, const void* q, const void* k, const void* v,
+               const int32_t* tables, const int32_t* lens, const void* out, const void* ws, size_t ws_bytes,
+               bool need_inputs) {
+    if (need_inputs) {
+        if (!q || !k || !v || !tables || !lens) return fail(PKV_EINVAL, "null input pointer");
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(tables, 4) || !aligned(lens, 4))
+            return fail(PKV_EINVAL, "q, k_cache, v_cache must be 16-byte aligned");
+    }
+    if (!out) return fail(PKV_EINVAL, "null out");
+    if (!aligned(out, pl.out_kind == pkv::kOutF32 ? 4 : 2)) return fail(PKV_EINVAL, "out misaligned");
+    if (pl.max_parts > 1) {
+        if (!ws || ws_bytes < pl.ws_bytes)
+            return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
+        if (!aligned(ws, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+    }
+    (void)d;
+    return PKV_OK;
+}
+
+}  // namespace
+
+int32_t paged_attn_partition_size(const pkv_attn_desc* d) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    return rc ? rc : pl.part_size;
+}
+
+size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
+    Plan pl;
+    if (resolve(d, &pl)) return 0;
+    return pl.ws_bytes;
+}
+
+int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (d->num_seqs == 0) return PKV_OK;
+    rc = check_ptrs(d, pl, q, k_cache, v_cache, block_tables, context_lens, out, workspace, workspace_bytes, true);
+    if (rc) return rc;
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse = lse;
+    a.ws_out = pl.max_parts > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+    a.ws_lse = pl.max_parts > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pl.ws_out_bytes)
+                                : nullptr;
+    a.scale = scale;
+    a.num_seqs = d->num_seqs;
+    a.num_q_heads = d->num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.table_stride = d->table_stride;
+    a.part_size = pl.part_size;
+    a.max_parts = pl.max_parts;
+    a.max_context_len = d->max_context_len;
+    a.out_dtype = pl.out_kind;
+    const int64_t n = (int64_t)d->num_seqs * d->num_kv_heads * pl.max_parts;
+    if (n > 0x7FFFFFFF) return fail(PKV_EUNSUPPORTED, "grid of %lld workgroups", (long long)n);
+    hipError_t e = pkv::launch_partition(a, d->head_dim, d->block_size, pl.group_pad, pl.bf16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "partition kernel launch");
+    return PKV_OK;
+}
+
+int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* out, float* lse,
+                     const void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (d->num_seqs == 0 || pl.max_parts <= 1) return PKV_OK;
+    if (!context_lens || !aligned(context_lens, 4)) return fail(PKV_EINVAL, "null context_lens");
+    rc = check_ptrs(d, pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, workspace, workspace_bytes, false);
+    if (rc) return rc;
+    pkv::MergeArgs a{};
+    a.context_lens = context_lens;
+    a.ws_out = reinterpret_cast<const float*>(workspace);
+    a.ws_lse = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + pl.ws_out_bytes);
+    a.out = out;
+    a.lse = lse;
+    a.num_seqs = d->num_seqs;
+    a.num_q_heads = d->num_q_heads;
+    a.part_size = pl.part_size;
+    a.max_parts = pl.max_parts;
+    a.max_context_len = d->max_context_len;
+    a.out_dtype = pl.out_kind;
+    hipError_t e = pkv::launch_merge(a, d->head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "merge kernel launch");
+    return PKV_OK;
+}
+
+int paged_attn_decode(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+    int rc = paged_attn_decode_partials(d, q, k_cache, v_cache, block_tables, context_lens, scale, out, lse,
+                                        workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_plan(const pkv_attn_desc* d, const int32_t* context_lens_host, int32_t* items_out, int64_t cap,
+                    int64_t* n_out) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (!n_out || (d->num_seqs > 0 && !context_lens_host)) return fail(PKV_EINVAL, "paged_attn_plan: null argument");
+    int64_t n = 0;
+    for (int32_t s = 0; s < d->num_seqs; ++s) {
+        const int32_t c = context_lens_host[s];
+        if (c < 0 || c > d->max_context_len)
+            return fail(PKV_EINVAL, "paged_attn_plan: context_lens[%d] = %d outside [0, %d]", s, c, d->max_context_len);
+        const int64_t np = ceil_div(c, pl.part_size);
+        for (int32_t g = 0; g < d->num_kv_heads; ++g)
+            for (int64_t pp = 0; pp < np; ++pp, ++n) {
+                if (items_out && n < cap) {
+                    int32_t* r = items_out + n * 5;
+                    r[0] = s;
+                    r[1] = g;
+                    r[2] = (int32_t)pp;
+                    r[3] = (int32_t)(pp * pl.part_size);
+                    r[4] = (int32_t)std::min<int64_t>((pp + 1) * pl.part_size, c);
+                }
+            }
+    }
+    *n_out = n;
+    return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// pkv_kernels.h -- internal interface between the host library and the HIP
+// kernels of libpkv.so.  Not installed; the public ABI is include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kNumXcds = 8;      // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kOutF32 = 0, kOutF16 = 1, kOutBF16 = 2;
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    void* out;
+    float* lse;              // natural log, nullable
+    float* ws_out;           // [B][Hq][max_parts][D]
+    float* ws_lse;           // [B][Hq][max_parts], log2 domain
+    float scale;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t table_stride;
+    int32_t part_size;
+    int32_t max_parts;
+    int32_t max_context_len;
+    int32_t out_dtype;       // kOut*
+};
+
+struct MergeArgs {
+    const int32_t* context_lens;
+    const float* ws_out;
+    const float* ws_lse;
+    void* out;
+    float* lse;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t part_size;
+    int32_t max_parts;
+    int32_t max_context_len;
+    int32_t out_dtype;
+};
+
+// One append item, as staged by the host (7 int32).
+struct AppendItem {
+    int32_t seq, slot, tpos, new_block, cow_src, cow_ntok, new_len;
+};
+
+struct AppendArgs {
+    const AppendItem* items;     // device-readable (pinned host) [n]
+    const void* k_new;           // [n][Hkv][D]
+    const void* v_new;
+    void* k_cache;               // [NB][Hkv][bs][D]
+    void* v_cache;
+    int32_t* block_tables;       // [max_seqs][table_stride]
+    int32_t* context_lens;       // [max_seqs]
+    int32_t n;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t table_stride;
+};
+
+hipError_t launch_partition(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
+                            hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, bool any_copy, hipStream_t stream);
+
+}  // namespace pkv
