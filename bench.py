@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) three times, "
+                         "the known-size reference for HBM byte counters")
     return ap.parse_args()
 
 
@@ -216,6 +219,17 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.calibrate_copy:
+        n = (1 << 30) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy: 3 x (read 1 GiB + write 1 GiB)")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)

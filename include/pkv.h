@@ -180,14 +180,19 @@ int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t tabl
  * block_tables[s][t / block_size], slot t % block_size.  An empty context
  * gives out = 0.  Scores, softmax and sums are fp32.
  *
- * Split-K: a context is cut into partitions of partition_size tokens,
- * partition p covering [p * P, min((p + 1) * P, len)).  Each partition's
- * normalised partial output and its lse go to the workspace, and a merge
- * kernel combines them by their lse.  A sequence with one partition is written
- * directly.
+ * Split.  All (sequence, kv head, 16-token tile) triples form one list,
+ * sequence-major, cut into chunks of C tiles; the grid's waves take the chunks
+ * in turn.  Balanced mode (partition_size 0): C = max(8, ceil(tiles / waves)),
+ * so every wave gets the same share whatever the lengths.  Fixed mode
+ * (partition_size P > 0): C = P / 16 and each (sequence, kv head) is padded to
+ * whole chunks, so a chunk is exactly the partition [p P, min((p + 1) P, len)).
+ * A chunk's part inside one (sequence, kv head) is a segment: its normalised
+ * output and lse go to the workspace, and a merge kernel combines the segments
+ * of each (sequence, q head) by their lse.  A (sequence, kv head) covered by
+ * one segment is written directly.
  * ------------------------------------------------------------------------ */
 typedef struct pkv_attn_desc {
-    int32_t num_seqs;
+    int32_t num_seqs;            /* at most 4096 per call */
     int32_t num_q_heads;
     int32_t num_kv_heads;        /* divides num_q_heads; group size 1..8 */
     int32_t head_dim;            /* 64 or 128 */
@@ -195,34 +200,37 @@ typedef struct pkv_attn_desc {
     int32_t num_blocks;          /* for documentation and validation only */
     int32_t table_stride;        /* int32 elements between block-table rows */
     int32_t max_context_len;     /* host upper bound of context_lens[] (sizes grid and workspace) */
-    int32_t partition_size;      /* 0 = library's choice; else a multiple of block_size, >= 16 */
+    int32_t partition_size;      /* 0 = balanced split; else a multiple of block_size (fixed partitions) */
     int32_t q_dtype;             /* PKV_F16 / PKV_BF16, equal to kv_dtype */
     int32_t kv_dtype;            /* PKV_F16 / PKV_BF16 */
     int32_t out_dtype;           /* PKV_F32, or the same as q_dtype */
+    int32_t num_waves;           /* waves in the grid; 0 = every wave that fits the device at once */
 } pkv_attn_desc;
 
-/* Partition size the library uses for this descriptor (resolves 0 = auto).
- * Returns a positive token count, or a negative status. */
+/* Partition size of the descriptor's split (0 = balanced), or a negative status. */
 int32_t paged_attn_partition_size(const pkv_attn_desc* desc);
 
-/* Bytes of device workspace paged_attn_decode needs (0 when no sequence can
- * span more than one partition).  Layout, with maxP = ceil(max_context_len / P):
- *   float part_out[num_seqs][num_q_heads][maxP][head_dim]  (normalised partials)
- *   float part_lse[num_seqs][num_q_heads][maxP]            (log2-domain lse of each)
- * starting at the workspace base, part_lse right after part_out. */
+/* Waves the decode grid will have (resolves num_waves = 0 with an occupancy
+ * query on the current device), or a negative status. */
+int32_t paged_attn_grid_waves(const pkv_attn_desc* desc);
+
+/* Bytes of device workspace paged_attn_decode needs.  Layout, each part
+ * 256-byte aligned, with S = segment slots (fixed: ceil(max_context_len / P);
+ * balanced: ceil(ceil(max_context_len / 16) / 8) + 1):
+ *   int32 hdr[2 + num_seqs + 1]              (tiles, chunk size, tile prefix)
+ *   float seg_out[num_seqs][num_q_heads][S][head_dim]   (normalised outputs)
+ *   float seg_lse[num_seqs][num_q_heads][S]             (log2-domain lse) */
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* desc);
 
-/* The whole decode: partition pass, then (if any sequence may span several
- * partitions) the merge pass, both on `stream`.  workspace: device, 256-byte
- * aligned, workspace_bytes >= paged_attn_workspace_bytes(desc). */
+/* The whole decode: the split pass, then (if a (sequence, kv head) may span
+ * several segments) the merge pass, both on `stream`.  workspace: device,
+ * 256-byte aligned, workspace_bytes >= paged_attn_workspace_bytes(desc). */
 int paged_attn_decode(const pkv_attn_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, float scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
-/* The two passes on their own (paged_attn_decode == partials then merge).
- * The partials of several devices' context shards can be merged by one call
- * once gathered into one workspace. */
+/* The two passes on their own (paged_attn_decode == partials then merge). */
 int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                const int32_t* context_lens, float scale, void* out, float* lse,
@@ -231,9 +239,10 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
                      float* lse, const void* workspace, size_t workspace_bytes,
                      pkv_stream_t stream);
 
-/* Debug: the split-K work items for host context lengths, in (seq, kv head,
- * partition) order, as rows of 5 int32: seq, kv_head, partition, tok_lo, tok_hi.
- * Writes min(count, cap) rows to items_out (nullable) and the count to *n_out. */
+/* Debug: the segments of the split for host context lengths, in (seq, kv
+ * head, slot) order, as rows of 5 int32: seq, kv_head, slot, tok_lo, tok_hi.
+ * Writes min(count, cap) rows to items_out (nullable) and the count to *n_out.
+ * With num_waves = 0 in balanced mode this queries the current device. */
 int paged_attn_plan(const pkv_attn_desc* desc, const int32_t* context_lens_host,
                     int32_t* items_out, int64_t cap, int64_t* n_out);
 

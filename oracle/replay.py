@@ -24,9 +24,15 @@ What is replayed, from the definitions:
   * freeing a sequence drops one reference from each of its blocks in logical
     order; a block whose count reaches zero is pushed back onto the free list,
     so the next allocation reuses the last block released;
-  * split-K partitions of a context of n tokens with partition size P:
-    ceil(n / P) partitions, partition p covering [p*P, min((p+1)*P, n)); work
-    items are enumerated in (sequence, kv head, partition) order.
+  * the decode split: every (sequence s, kv head g, 16-token tile j) in one
+    sequence-major list -- (s, g)'s tiles start at first(s, g) =
+    Hkv * sum_{s'<s} pt_s' + g * pt_s -- cut into chunks of C tiles.  With a
+    fixed partition size P, C = P / 16 and pt_s = ceil(nt_s / C) * C (so a
+    chunk is the partition [p*P, min((p+1)*P, n)) of one (s, g)); balanced,
+    pt_s = nt_s and C = max(8, ceil(T / W)) for W waves and T tiles in all.
+    A segment is the part of one chunk inside one (s, g); its slot is the
+    chunk index minus first(s, g) // C.  Segments are listed in (s, g, slot)
+    order.
 """
 from __future__ import annotations
 
@@ -170,14 +176,38 @@ class PoolReplay:
         return len(self.free)
 
 
-def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int):
-    """Split-K work items (seq, kv_head, partition, tok_lo, tok_hi) in order."""
-    if partition_size <= 0:
-        raise ValueError("partition_size must be positive")
+TILE = 16
+MIN_CHUNK = 8
+
+
+def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, num_waves: int = 1):
+    """Segments (seq, kv_head, slot, tok_lo, tok_hi) of the decode split, in order."""
+    if partition_size < 0 or num_waves < 1:
+        raise ValueError("bad split parameters")
+    lens = [max(0, int(n)) for n in context_lens]
+    nt = [ceil_div(n, TILE) for n in lens]
+    if partition_size > 0:
+        C = partition_size // TILE
+        pt = [ceil_div(x, C) * C for x in nt]
+    else:
+        pt = list(nt)
+    firsts = []
+    acc = 0
+    for s in range(len(lens)):
+        firsts.append(acc)
+        acc += num_kv_heads * pt[s]
+    total = acc
+    if partition_size == 0:
+        C = max(MIN_CHUNK, ceil_div(total, num_waves))
     items = []
-    for s, n in enumerate(context_lens):
-        n = int(n)
+    for s, n in enumerate(lens):
         for g in range(num_kv_heads):
-            for p in range(ceil_div(n, partition_size)):
-                items.append((s, g, p, p * partition_size, min((p + 1) * partition_size, n)))
+            if nt[s] == 0:
+                continue
+            first = firsts[s] + g * pt[s]
+            c0, c1 = first // C, (first + nt[s] - 1) // C
+            for ch in range(c0, c1 + 1):
+                j0 = max(ch * C - first, 0)
+                j1 = min((ch + 1) * C - first, nt[s])
+                items.append((s, g, ch - c0, j0 * TILE, min(j1 * TILE, n)))
     return items

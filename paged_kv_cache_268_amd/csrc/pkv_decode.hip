@@ -14,29 +14,27 @@
 // (sequence s, kv head g, partition p).  A partition is P consecutive tokens
 // [p*P, min((p+1)*P, len)); it is cut into 16-token tiles (a tile never
 // crosses a block because block_size is 16 or 32 and P a multiple of it), and
-// wave w takes tiles w, w+4, w+8, ...
+// wave w takes tiles w, w+4, w+8, ...  A 16-token tile of one (block, kv head)
+// is 16*D*2 bytes contiguous.
 //
-// Lane layout inside a wave.  A K (or V) row of one token is D 16-bit values
-// = D*2 bytes.  LPR = D/8 lanes share a row, each holding one 16-byte slice
-// (8 values, d in [8c, 8c+8)); a wave load instruction therefore covers
-// RPI = 64/LPR consecutive rows = 1 KiB of contiguous memory.  A 16-token tile
-// of one (block, kv head) is 16*D*2 bytes contiguous and takes NI = 16/RPI
-// load instructions for K and NI for V.  Each lane keeps the G q heads of the
-// group for its own d-slice in registers, so a K/V row is read from HBM once
-// per kv head, not once per q head.
-//
-// QK: per lane, 4 packed dot2 (fp32 accumulate) per head per row, then a
-// butterfly over the LPR lanes of the row with DPP row operations.
-// Softmax: each row-group (the LPR lanes sharing rows) runs its own online
-// softmax in the log2 domain; the running max is only moved when a tile's max
-// exceeds it by more than TAU, so a rescale of the accumulator is rare, and
-// every weight stays <= 2^TAU.  Rows past the context are excluded (their
-// weight is 0 by selection and their V is not used), so stale or NaN data in
-// unused slots never reaches the sums.
-// End of a work item: row-group states merge by shuffles, the 4 waves merge
-// through LDS, and the result is either the final output (a one-partition
-// sequence) or a normalised partial plus its log2-domain lse in the workspace
-// for the merge kernel.
+// QK on the matrix core.  The G q heads of the kv group form the B operand of
+// v_mfma_f32_16x16x32 (32 d x 16 heads, heads >= G zero) and stay in
+// registers, so every K row is read once per kv head, not once per q head.
+// The A operand is 16 K rows x 32 d: lane l loads 16 bytes of row l%16, so
+// one wave load instruction reads 64 contiguous bytes of each of the 16 rows.
+// D/32 MFMAs give the 16x16 score tile.
+// Softmax: one running reference max per head for the whole wave; it moves
+// only when a tile's max exceeds it by more than TAU (log2 units), so the
+// accumulator rescale is a rare, scalar-branch event and every weight stays
+// <= 2^TAU.  Rows past the context get weight 0 by selection and their V is
+// zeroed before use, so stale or NaN data in unused slots never reaches a sum.
+// PV on the vector ALUs: V rows are loaded so that LPR = D/8 lanes share a
+// row (16 bytes each) and a wave load instruction reads 1 KiB contiguous; the
+// tile's weights reach these lanes through a 1 KiB per-wave LDS slot.
+// End of a work item: the row-groups' partial sums add up (shared reference),
+// the 4 waves merge through LDS, and the result is either the final output (a
+// one-partition sequence) or a normalised partial plus its log2-domain lse in
+// the workspace for the merge kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,41 +49,53 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
+constexpr int kMinChunk = 8;           // balanced split: at least 8 tiles (128 tokens) per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// DPP controls (row = 16 lanes).
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // reverse within 8 lanes
-constexpr int kDppMirror = 0x140;      // reverse within 16 lanes
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-    // After the first two steps all lanes of a quad agree, so a mirror inside
-    // 8 (then 16) lanes pairs each quad with the other quad (half) of the row.
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kDppXor1, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kDppXor2, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kDppHalfMirror, 0xF, 0xF, false));
-    if constexpr (LPR == 16)
-        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kDppMirror, 0xF, 0xF, false));
-    return x;
+template <bool BF16> struct MfmaType { using vec = f16x8; };
+template <> struct MfmaType<true> { using vec = bf16x8; };
+
+// C += A(16x32) * B(32x16), fp32 accumulate (v_mfma_f32_16x16x32_{bf16,f16}).
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma_16x16x32(typename MfmaType<BF16>::vec a, typename MfmaType<BF16>::vec b,
+                                                 floatx4 c) {
+    if constexpr (BF16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <bool BF16>
-__device__ __forceinline__ float dot8(const uint4 k, const uint4 q, float acc) {
-    if constexpr (BF16) {
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.x), __builtin_bit_cast(bf16x2, q.x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.y), __builtin_bit_cast(bf16x2, q.y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.z), __builtin_bit_cast(bf16x2, q.z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.w), __builtin_bit_cast(bf16x2, q.w), acc, false);
-    } else {
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.x), __builtin_bit_cast(f16x2, q.x), acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.y), __builtin_bit_cast(f16x2, q.y), acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.z), __builtin_bit_cast(f16x2, q.z), acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k.w), __builtin_bit_cast(f16x2, q.w), acc, false);
-    }
-    return acc;
+// Cross-row helpers (gfx950 v_permlane{16,32}_swap with both operands = x):
+// permlane16_swap yields x[l & ~16] and x[l | 16], permlane32_swap yields
+// x[l % 32] and x[32 + l % 32]; combining the pair reduces across lanes
+// l ^ 16 (resp. l ^ 32) with no LDS round trip.
+__device__ __forceinline__ float xsum16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xmax16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+// Sum over the row-groups of the V layout: lanes with equal l % LPR.
+// LPR = 16: the four DPP rows; LPR = 8: first pair the two halves of each
+// row (DPP row_ror:8 maps lane i to lane i ^ 8 inside a 16-lane row).
+template <int LPR>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+    if constexpr (LPR == 8)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    return xsum32(xsum16(x));
 }
 
 // Two packed 16-bit values -> two floats (exact widening).
@@ -119,268 +129,361 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, int o
     }
 }
 
-// Work-group id -> logical work item id.  The hardware hands workgroup i to
+// Workgroup id -> logical workgroup id.  The hardware hands workgroup i to
 // XCD i % 8; this makes consecutive logical ids land on one XCD (and so share
-// its L2) -- sequences that share prefix blocks sit next to each other.
-__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
-    const int64_t per = n / kNumXcds;
+// its L2).  Consecutive logical workgroups take consecutive chunks of the
+// flattened tile list, so sequences next to each other in the batch (a
+// shared-prefix group) are read through the same L2.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    const int per = n / kNumXcds;
     if (i < per * kNumXcds) return (i % kNumXcds) * per + i / kNumXcds;
     return i;
 }
 
+// Tiles of one kv head of sequence s (16 tokens each), and the same count
+// padded to whole chunks when the chunk size is fixed.
+__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int s) {
+    const int n = min(max(a.context_lens[s], 0), a.max_context_len);
+    return (n + kTile - 1) / kTile;
+}
+__device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
+    return fixed_chunk > 0 ? (nt + fixed_chunk - 1) / fixed_chunk * fixed_chunk : nt;
+}
+
+// The split.  All (sequence s, kv head g, tile j) are laid out in one list,
+// sequence-major: (s, g)'s tiles start at first(s, g) = pre[s] + g * pt_s,
+// pre[s] = Hkv * sum_{s' < s} pt_s'.  The list is cut into chunks of C tiles;
+// wave w of the NW waves in the grid takes chunks w, w + NW, ...  Balanced
+// mode (partition_size 0): pt_s = tiles of s, C = max(kMinChunk, ceil(T / NW))
+// so every wave gets an equal share whatever the lengths.  Fixed mode:
+// C = partition_size / 16 and pt_s is padded to a multiple of C, so a chunk
+// is exactly one partition [pC*16, min((p+1)C*16, len)) of one (s, g).
+// A chunk's part inside one (s, g) is a segment; it writes its normalised
+// output and log2-domain lse to slot k = c - first(s, g) / C, or the final
+// output directly when it covers all of (s, g).
 template <int D, int BS, int GP, bool BF16>
 __global__ void __launch_bounds__(kThreads)
-paged_decode_partition_kernel(DecodeArgs a) {
-    constexpr int LPR = D / 8;            // lanes per K/V row
-    constexpr int RPI = 64 / LPR;         // rows per wave load instruction
-    constexpr int NI = kTile / RPI;       // load instructions per tile (K or V)
-    static_assert(NI * RPI == kTile, "tile shape");
+paged_decode_split_kernel(DecodeArgs a) {
+    constexpr int KS = D / 32;            // MFMA k-steps = K load instructions per tile
+    constexpr int LPR = D / 8;            // V: lanes per row
+    constexpr int RPI = 64 / LPR;         // V: rows per wave load instruction
+    constexpr int NI = kTile / RPI;       // V: load instructions per tile
+    static_assert(NI * RPI == kTile && GP <= 16, "tile shape");
+    using MfmaIn = typename MfmaType<BF16>::vec;
 
-    const int64_t n_items = (int64_t)a.num_seqs * a.num_kv_heads * a.max_parts;
-    const int64_t item = xcd_remap(blockIdx.x, n_items);
-    const int s = (int)(item % a.num_seqs);
-    const int64_t rest = item / a.num_seqs;
-    const int g = (int)(rest % a.num_kv_heads);
-    const int p = (int)(rest / a.num_kv_heads);
-
-    // A length outside [0, max_context_len] breaks the caller's contract; it
-    // is clamped so that no access leaves the declared table and workspace.
-    const int ctx = min(max(a.context_lens[s], 0), a.max_context_len);
-    const int nparts = (ctx + a.part_size - 1) / a.part_size;
-    // Partition 0 always runs, so an empty context still gets its output.
-    if (p >= (nparts > 0 ? nparts : 1)) return;
-
-    const int t_lo = p * a.part_size;
-    const int t_hi = min(t_lo + a.part_size, ctx);
-    const int n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTile - 1) / kTile : 0;
+    __shared__ int s_pre[kMaxSeqs + 1];
+    __shared__ int s_wsum[kWaves];
+    __shared__ float s_p[kWaves][kTile][16];   // p[token][head] of the current tile, per wave
 
     const int lane = threadIdx.x & 63;
-    // Wave index as a uniform (scalar) value, so loops over tiles stay scalar.
+    // Wave index as a uniform (scalar) value, so loops stay scalar.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane % LPR;              // 16-byte slice of the row
-    const int r = lane / LPR;              // row inside a load instruction
-    const int G = a.num_q_heads / a.num_kv_heads;
-    const int h0 = g * G;
+    const int B = a.num_seqs, Hkv = a.num_kv_heads;
 
-    // q slices of the group's heads (zero for padded heads h >= G).
-    uint4 qv[GP];
+    // ---- prefix of padded tiles over sequences (every workgroup, in LDS) ----
+    int running = 0;
+    for (int base = 0; base < B; base += kThreads) {
+        const int s = base + (int)threadIdx.x;
+        const int v = s < B ? padded_tiles(seq_tiles(a, s), a.fixed_chunk) : 0;
+        int x = v;
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        if (h < G) {
-            const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)s * a.num_q_heads + h0 + h) * D + c * 8;
-            qv[h] = *reinterpret_cast<const uint4*>(qp);
-        } else {
-            qv[h] = make_uint4(0, 0, 0, 0);
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
         }
-    }
-
-    float m[GP], l[GP], acc[GP][8];
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
-
-    const float sl2 = a.scale * kLog2e;
-    const int32_t* table = a.block_tables + (int64_t)s * a.table_stride;
-    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
-    // Element offset of this lane's slice inside a tile (row r of instruction 0).
-    const int lane_off = r * D + c * 8;
-
-    // Tiles of this wave: j = wave + WAVES * it, it in [0, n_w).
-    const int n_w = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
-
-    auto tile_base = [&](int it, int32_t blk) -> int64_t {
-        const int t0 = t_lo + (wave + kWaves * it) * kTile;
-        return (((int64_t)blk * a.num_kv_heads + g) * BS + (t0 % BS)) * D + lane_off;
-    };
-
-    auto compute_tile = [&](int it, const uint4 (&kb)[NI], const uint4 (&vb)[NI]) {
-        const int t0 = t_lo + (wave + kWaves * it) * kTile;
-        const bool full = t0 + kTile <= t_hi;
-        float x[NI][GP];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-#pragma unroll
-            for (int h = 0; h < GP; ++h) x[i][h] = row_sum<LPR>(dot8<BF16>(kb[i], qv[h], 0.f)) * sl2;
-        }
-        bool valid[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) valid[i] = full || (t0 + i * RPI + r < t_hi);
-        if (!full) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int h = 0; h < GP; ++h) x[i][h] = valid[i] ? x[i][h] : -INFINITY;
-        }
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            float mt = x[0][h];
-#pragma unroll
-            for (int i = 1; i < NI; ++i) mt = fmaxf(mt, x[i][h]);
-            if (mt > m[h] + kTau) {
-                const float alpha = __builtin_amdgcn_exp2f(m[h] - mt);   // 0 when m = -inf
-                l[h] *= alpha;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-                m[h] = mt;
-            }
-        }
-        float pw[NI][GP];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                const float e = __builtin_amdgcn_exp2f(x[i][h] - m[h]);
-                pw[i][h] = valid[i] ? e : 0.f;
-                l[h] += pw[i][h];
-            }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            float vf[8];
-            widen2<BF16>(vb[i].x, vf[0], vf[1]);
-            widen2<BF16>(vb[i].y, vf[2], vf[3]);
-            widen2<BF16>(vb[i].z, vf[4], vf[5]);
-            widen2<BF16>(vb[i].w, vf[6], vf[7]);
-            if (!full) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vf[e] = valid[i] ? vf[e] : 0.f;
-            }
-#pragma unroll
-            for (int h = 0; h < GP; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[i][h], vf[e], acc[h][e]);
-        }
-    };
-
-    // Chunks of up to 64 tiles: lane i first loads the block id of the chunk's
-    // tile i.  Two register buffers then alternate (no copies between them):
-    // while one tile is computed the next tile's K/V loads are in flight.
-    auto load_tile = [&](int it, int32_t blocks, uint4 (&kb)[NI], uint4 (&vb)[NI], int c0) {
-        const int64_t base = tile_base(c0 + it, __builtin_amdgcn_readlane(blocks, it));
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            kb[i] = *reinterpret_cast<const uint4*>(kc + base + i * RPI * D);
-            vb[i] = *reinterpret_cast<const uint4*>(vc + base + i * RPI * D);
-        }
-        // Keep the scheduler from sinking these loads below the compute of the
-        // previous tile: they must be issued before that compute waits.
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int c0 = 0; c0 < n_w; c0 += 64) {
-        const int cn = min(64, n_w - c0);
-        const int32_t blocks = lane < cn ? table[(t_lo + (wave + kWaves * (c0 + lane)) * kTile) / BS] : 0;
-        uint4 ka[NI], va[NI], kb2[NI], vb2[NI];
-        load_tile(0, blocks, ka, va, c0);
-        int it = 0;
-        for (; it + 2 < cn; it += 2) {
-            load_tile(it + 1, blocks, kb2, vb2, c0);
-            compute_tile(c0 + it, ka, va);
-            load_tile(it + 2, blocks, ka, va, c0);
-            compute_tile(c0 + it + 1, kb2, vb2);
-        }
-        if (it + 1 < cn) {
-            load_tile(it + 1, blocks, kb2, vb2, c0);
-            compute_tile(c0 + it, ka, va);
-            compute_tile(c0 + it + 1, kb2, vb2);
-        } else {
-            compute_tile(c0 + it, ka, va);
-        }
-    }
-
-    // ---- merge the row-groups of this wave (lanes sharing c, different r) ----
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        float mx = m[h];
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float f = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[h] - mx);
-        float lh = l[h] * f;
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) lh += __shfl_xor(lh, off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = acc[h][e] * f;
-#pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
-            acc[h][e] = v;
-        }
-        m[h] = mx;
-        l[h] = lh;
-    }
-
-    // ---- merge the 4 waves through LDS ----
-    __shared__ float s_acc[kWaves][GP][D];
-    __shared__ float s_m[kWaves][GP];
-    __shared__ float s_l[kWaves][GP];
-    if (r == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][c * 8 + e] = acc[h][e];
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h) { s_m[wave][h] = m[h]; s_l[wave][h] = l[h]; }
-    }
-    __syncthreads();
-
-    const bool direct = nparts <= 1;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int h = idx / D, d = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        float L = 0.f, O = 0.f;
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        int woff = 0, tot = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-            L += s_l[w][h] * f;
-            O += s_acc[w][h][d] * f;
+            woff += w < wave ? s_wsum[w] : 0;
+            tot += s_wsum[w];
         }
-        O = L > 0.f ? O / L : 0.f;
-        const float lse2 = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;   // log2 domain
-        const int64_t sh = (int64_t)s * a.num_q_heads + h0 + h;
-        if (direct) {
-            store_out(a.out, sh * D + d, O, a.out_dtype);
-            if (a.lse && d == 0) a.lse[sh] = lse2 * kLn2;
-        } else {
-            a.ws_out[(sh * a.max_parts + p) * D + d] = O;
-            if (d == 0) a.ws_lse[sh * a.max_parts + p] = lse2;
+        if (s < B) s_pre[s] = (running + woff + x - v) * Hkv;
+        running += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) s_pre[B] = running * Hkv;
+    __syncthreads();
+    const int T = s_pre[B];
+    const int C = a.fixed_chunk > 0 ? a.fixed_chunk : max(kMinChunk, (T + a.num_waves - 1) / a.num_waves);
+    const int NC = (T + C - 1) / C;
+
+    const int lwg = xcd_remap(blockIdx.x, gridDim.x);
+    if (lwg == 0) {
+        // Publish the split for the merge kernel, and write the output of
+        // every empty context (no chunk covers it): zeros, lse = -inf.
+        for (int i = threadIdx.x; i <= B; i += kThreads) a.ws_hdr[2 + i] = s_pre[i];
+        if (threadIdx.x == 0) { a.ws_hdr[0] = T; a.ws_hdr[1] = C; }
+        for (int s = 0; s < B; ++s) {
+            if (s_pre[s + 1] != s_pre[s]) continue;
+            for (int i = threadIdx.x; i < a.num_q_heads * D; i += kThreads)
+                store_out(a.out, (int64_t)s * a.num_q_heads * D + i, 0.f, a.out_dtype);
+            if (a.lse)
+                for (int i = threadIdx.x; i < a.num_q_heads; i += kThreads) a.lse[(int64_t)s * a.num_q_heads + i] = -INFINITY;
+        }
+    }
+
+    const int G = a.num_q_heads / Hkv;
+    // MFMA operand roles (v_mfma_f32_16x16x32): A = 16 tokens x 32 d of K,
+    // B = 32 d x 16 heads of q (heads >= G are zero), C = scores[token][head].
+    // Lane l supplies A row l%16 and B column l%16, d-chunk 8*(l/16) of each
+    // 32-wide k-step, and receives C[4*(l/16) + i][l%16], i = 0..3.
+    const int mrow = lane & 15;           // K row (token in tile) / head of B and C
+    const int kq = lane >> 4;             // d-chunk of the k-step / token quad of C
+    // V layout: LPR lanes share a row, lane owns the 8 values [8c, 8c+8).
+    const int c = lane % LPR;
+    const int r = lane / LPR;
+    const float sl2 = a.scale * kLog2e;
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
+    const int k_off = mrow * D + kq * 8;  // lane's K element offset inside a tile (+ 32 * ks)
+    const int v_off = r * D + c * 8;      // lane's V element offset inside a tile (+ i * RPI * D)
+
+    // One segment: tiles [j0, j1) of kv head g of sequence s.
+    auto run_segment = [&](int s, int g, int j0, int j1, int slot, bool direct) {
+        const int ctx = min(max(a.context_lens[s], 0), a.max_context_len);
+        const int h0 = g * G;
+        MfmaIn qb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (mrow < G) {
+                const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                                     ((int64_t)s * a.num_q_heads + h0 + mrow) * D + ks * 32 + kq * 8;
+                w = *reinterpret_cast<const uint4*>(qp);
+            }
+            qb[ks] = __builtin_bit_cast(MfmaIn, w);
+        }
+        // Softmax state.  m[h]: one reference per head shared by the whole
+        // wave (uniform); m_lane = m[l%16] for the lanes of real heads (0
+        // elsewhere); l_lane: weight sums in the score layout; acc: V layout.
+        float m[GP], acc[GP][8];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            m[h] = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        }
+        float m_lane = mrow < G ? -INFINITY : 0.f;
+        float l_lane = 0.f;
+        const int32_t* table = a.block_tables + (int64_t)s * a.table_stride;
+
+        auto tile_base = [&](int j, int32_t blk) -> int64_t {
+            return (((int64_t)blk * Hkv + g) * BS + (j * kTile) % BS) * D;
+        };
+        // QK on the matrix core, then the online-softmax update; the tile's
+        // weights go to this wave's LDS slot.
+        auto qk_softmax = [&](int j, const uint4 (&kb)[KS]) {
+            const int t0 = j * kTile;
+            const bool full = t0 + kTile <= ctx;
+            floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
+            float x[4];
+            bool need = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = sc[i] * sl2;
+                if (!full && t0 + 4 * kq + i >= ctx) x[i] = -INFINITY;
+                need |= x[i] > m_lane + kTau;
+            }
+            // Rare path: some score exceeds its head's reference by more than TAU.
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                mx = xmax16(mx);
+                mx = xmax32(mx);                    // lane (j, n): tile max of head n
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    if (h < G) {
+                        const float mt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), h));
+                        if (mt > m[h] + kTau) {
+                            const float alpha = __builtin_amdgcn_exp2f(m[h] - mt);   // 0 when m = -inf
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                            l_lane = (mrow == h) ? l_lane * alpha : l_lane;
+                            m_lane = (mrow == h) ? mt : m_lane;
+                            m[h] = mt;
+                        }
+                    }
+                }
+            }
+            // Weights <= 2^TAU; a row past the context has x = -inf and weight 0.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = __builtin_amdgcn_exp2f(x[i] - m_lane);
+                l_lane += e;
+                s_p[wave][4 * kq + i][mrow] = e;
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+        // PV on the vector ALUs, V rows in the coalesced layout.
+        auto pv = [&](int j, const uint4 (&vb)[NI]) {
+            const int t0 = j * kTile;
+            const bool full = t0 + kTile <= ctx;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int row = i * RPI + r;
+                float ph[GP];
+                if constexpr (GP >= 4) {
+#pragma unroll
+                    for (int h4 = 0; h4 < GP; h4 += 4) {
+                        const float4 q4 = *reinterpret_cast<const float4*>(&s_p[wave][row][h4]);
+                        ph[h4] = q4.x; ph[h4 + 1] = q4.y; ph[h4 + 2] = q4.z; ph[h4 + 3] = q4.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < GP; ++h) ph[h] = s_p[wave][row][h];
+                }
+                float vf[8];
+                widen2<BF16>(vb[i].x, vf[0], vf[1]);
+                widen2<BF16>(vb[i].y, vf[2], vf[3]);
+                widen2<BF16>(vb[i].z, vf[4], vf[5]);
+                widen2<BF16>(vb[i].w, vf[6], vf[7]);
+                if (!full) {
+                    // Unused slots may hold anything (NaN included): never let them into a sum.
+                    const bool valid = t0 + row < ctx;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.f;
+                }
+#pragma unroll
+                for (int h = 0; h < GP; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[h], vf[e], acc[h][e]);
+            }
+            __builtin_amdgcn_wave_barrier();
+        };
+        auto load_k = [&](int j, int32_t blk, uint4 (&kb)[KS]) {
+            const int64_t base = tile_base(j, blk);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const uint4*>(kc + base + k_off + ks * 32);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto load_v = [&](int j, int32_t blk, uint4 (&vb)[NI]) {
+            const int64_t base = tile_base(j, blk);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const uint4*>(vc + base + v_off + i * RPI * D);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // One K and one V register buffer, refilled a phase ahead: K of the
+        // next tile is requested as soon as QK has consumed the current one,
+        // V of the next tile as soon as PV has.  Block ids come 64 tiles at a
+        // time, one per lane, and are read back with v_readlane.
+        for (int c0 = j0; c0 < j1; c0 += 64) {
+            const int cn = min(64, j1 - c0);
+            const int32_t blocks = lane < cn ? table[((c0 + lane) * kTile) / BS] : 0;
+            uint4 kb[KS], vb[NI];
+            load_k(c0, __builtin_amdgcn_readlane(blocks, 0), kb);
+            load_v(c0, __builtin_amdgcn_readlane(blocks, 0), vb);
+            for (int it = 0; it + 1 < cn; ++it) {
+                const int32_t nb = __builtin_amdgcn_readlane(blocks, it + 1);
+                qk_softmax(c0 + it, kb);
+                load_k(c0 + it + 1, nb, kb);
+                pv(c0 + it, vb);
+                load_v(c0 + it + 1, nb, vb);
+            }
+            qk_softmax(c0 + cn - 1, kb);
+            pv(c0 + cn - 1, vb);
+        }
+
+        // ---- segment totals: l per head (score layout), acc over row-groups ----
+        l_lane = xsum32(xsum16(l_lane));           // lane (j, n): total of head n
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = rowgroup_sum<LPR>(acc[h][e]);
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            if (h < G) {
+                const float L = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), h));
+                const float inv = 1.f / L;            // L >= 1: the tile that set m[h] has weight 1
+                const float lse2 = m[h] + __builtin_amdgcn_logf(L);
+                const int64_t sh = (int64_t)s * a.num_q_heads + h0 + h;
+                if (r == 0) {
+                    if (direct) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) store_out(a.out, sh * D + c * 8 + e, acc[h][e] * inv, a.out_dtype);
+                    } else {
+                        float* o = a.ws_out + (sh * a.max_seg + slot) * D + c * 8;
+                        *reinterpret_cast<float4*>(o) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+                        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+                    }
+                }
+                if (lane == 0) {
+                    if (direct) {
+                        if (a.lse) a.lse[sh] = lse2 * kLn2;
+                    } else {
+                        a.ws_lse[sh * a.max_seg + slot] = lse2;
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- this wave's chunks ----
+    const int w_global = lwg * kWaves + wave;
+    for (int ch = w_global; ch < NC; ch += a.num_waves) {
+        const int lo = ch * C, hi = min(lo + C, T);
+        // Largest s with pre[s] <= lo (empty sequences before it share its prefix).
+        int sl = 0, sh_ = B;                       // invariant: pre[sl] <= lo < pre[sh_]
+        while (sh_ - sl > 1) {
+            const int mid = (sl + sh_) >> 1;
+            if (s_pre[mid] <= lo) sl = mid; else sh_ = mid;
+        }
+        int s = sl;
+        int t = lo;
+        while (t < hi) {
+            while (s_pre[s + 1] <= t) ++s;         // skip sequences with no tiles
+            const int nt = seq_tiles(a, s);
+            const int pt = padded_tiles(nt, a.fixed_chunk);
+            const int rel = t - s_pre[s];
+            const int g = rel / pt;
+            const int j0 = rel % pt;
+            const int seg_hi = min(hi, s_pre[s] + (g + 1) * pt);
+            const int j1 = min(seg_hi - s_pre[s] - g * pt, nt);
+            if (j0 < j1) {
+                const int first = s_pre[s] + g * pt;
+                run_segment(s, g, j0, j1, ch - first / C, j0 == 0 && j1 == nt && (first + nt - 1) / C == first / C);
+            }
+            t = seg_hi;
         }
     }
 }
 
-// Merge kernel: one 256-thread workgroup per (sequence, q head) whose
-// sequence spans more than one partition.  With M = max_p lse_p and
-// w_p = 2^(lse_p - M): out = sum_p w_p o_p / sum_p w_p and
-// lse = M + log2(sum_p w_p) -- the online-softmax identity applied to the
-// partitions.  Threads own 4 consecutive d values of one partition slot; the
-// slots stride over the partitions and meet in LDS.
+// Merge kernel: one 256-thread workgroup per (sequence, q head) whose (s, g)
+// spans more than one chunk.  With M = max_k lse_k and w_k = 2^(lse_k - M):
+// out = sum_k w_k o_k / sum_k w_k and lse = M + log2(sum_k w_k) -- the
+// online-softmax identity applied to the segments.  Threads own 4
+// consecutive d values of one segment slot; the slots stride over the
+// segments and meet in LDS.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_merge_kernel(MergeArgs a) {
-    constexpr int TPP = D / 4;                 // threads per partition row
-    constexpr int SLOTS = kThreads / TPP;      // partitions handled at once
+    constexpr int TPP = D / 4;                 // threads per segment row
+    constexpr int SLOTS = kThreads / TPP;      // segments handled at once
     const int64_t sh = blockIdx.x;
     const int s = (int)(sh / a.num_q_heads);
-    const int ctx = min(max(a.context_lens[s], 0), a.max_context_len);
-    const int nparts = (ctx + a.part_size - 1) / a.part_size;
-    if (nparts <= 1) return;                  // written by the partition kernel
+    const int hq = (int)(sh % a.num_q_heads);
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int g = hq / G;
+    const int n = min(max(a.context_lens[s], 0), a.max_context_len);
+    const int nt = (n + kTile - 1) / kTile;
+    if (nt == 0) return;                       // written by the split kernel
+    const int C = a.ws_hdr[1];
+    const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
+    const int first = a.ws_hdr[2 + s] + g * pt;
+    const int nseg = (first + nt - 1) / C - first / C + 1;
+    if (nseg <= 1) return;                     // written directly
 
-    const float* lse_p = a.ws_lse + sh * a.max_parts;
-    const float* out_p = a.ws_out + sh * a.max_parts * D;
+    const float* lse_p = a.ws_lse + sh * a.max_seg;
+    const float* out_p = a.ws_out + sh * a.max_seg * D;
     __shared__ float s_red[kThreads / 64];
     __shared__ float s_acc[SLOTS][D];
     __shared__ float s_w[SLOTS];
 
-    // M = max over partitions.
     float mx = -INFINITY;
-    for (int pp = threadIdx.x; pp < nparts; pp += kThreads) mx = fmaxf(mx, lse_p[pp]);
+    for (int k = threadIdx.x; k < nseg; k += kThreads) mx = fmaxf(mx, lse_p[k]);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = mx;
     __syncthreads();
@@ -392,9 +495,9 @@ paged_decode_merge_kernel(MergeArgs a) {
     const int d4 = (threadIdx.x % TPP) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
-    for (int pp = slot; pp < nparts; pp += SLOTS) {
-        const float w = __builtin_amdgcn_exp2f(lse_p[pp] - M);
-        const float4 o = *reinterpret_cast<const float4*>(out_p + (int64_t)pp * D + d4);
+    for (int k = slot; k < nseg; k += SLOTS) {
+        const float w = __builtin_amdgcn_exp2f(lse_p[k] - M);
+        const float4 o = *reinterpret_cast<const float4*>(out_p + (int64_t)k * D + d4);
         acc.x = fmaf(w, o.x, acc.x);
         acc.y = fmaf(w, o.y, acc.y);
         acc.z = fmaf(w, o.z, acc.z);
@@ -421,42 +524,51 @@ paged_decode_merge_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int D, int BS, int GP, bool BF16>
-static hipError_t launch_partition_t(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.max_parts;
-    hipLaunchKernelGGL((paged_decode_partition_kernel<D, BS, GP, BF16>), dim3((unsigned)n), dim3(kThreads), 0,
-                       stream, a);
+static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStream_t stream) {
+    auto kern = paged_decode_split_kernel<D, BS, GP, BF16>;
+    if (waves_per_cu) {
+        int blocks = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kThreads, 0);
+        if (e != hipSuccess) return e;
+        *waves_per_cu = blocks * kWaves;
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a->num_waves / kWaves)), dim3(kThreads), 0, stream, *a);
     return hipGetLastError();
 }
 
 template <int D, int BS, bool BF16>
-static hipError_t launch_partition_g(const DecodeArgs& a, int gp, hipStream_t stream) {
+static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st) {
     switch (gp) {
-        case 1: return launch_partition_t<D, BS, 1, BF16>(a, stream);
-        case 2: return launch_partition_t<D, BS, 2, BF16>(a, stream);
-        case 4: return launch_partition_t<D, BS, 4, BF16>(a, stream);
-        case 8: return launch_partition_t<D, BS, 8, BF16>(a, stream);
+        case 1: return split_dispatch<D, BS, 1, BF16>(a, wpc, st);
+        case 2: return split_dispatch<D, BS, 2, BF16>(a, wpc, st);
+        case 4: return split_dispatch<D, BS, 4, BF16>(a, wpc, st);
+        case 8: return split_dispatch<D, BS, 8, BF16>(a, wpc, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int D, bool BF16>
-static hipError_t launch_partition_b(const DecodeArgs& a, int bs, int gp, hipStream_t stream) {
-    if (bs == 16) return launch_partition_g<D, 16, BF16>(a, gp, stream);
-    if (bs == 32) return launch_partition_g<D, 32, BF16>(a, gp, stream);
+static hipError_t split_b(const DecodeArgs* a, int bs, int gp, int* wpc, hipStream_t st) {
+    if (bs == 16) return split_g<D, 16, BF16>(a, gp, wpc, st);
+    if (bs == 32) return split_g<D, 32, BF16>(a, gp, wpc, st);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_partition(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
-                            hipStream_t stream) {
-    if (head_dim == 128) {
-        return bf16 ? launch_partition_b<128, true>(a, block_size, group_pad, stream)
-                    : launch_partition_b<128, false>(a, block_size, group_pad, stream);
-    }
-    if (head_dim == 64) {
-        return bf16 ? launch_partition_b<64, true>(a, block_size, group_pad, stream)
-                    : launch_partition_b<64, false>(a, block_size, group_pad, stream);
-    }
+static hipError_t split_any(const DecodeArgs* a, int head_dim, int bs, int gp, bool bf16, int* wpc, hipStream_t st) {
+    if (head_dim == 128) return bf16 ? split_b<128, true>(a, bs, gp, wpc, st) : split_b<128, false>(a, bs, gp, wpc, st);
+    if (head_dim == 64) return bf16 ? split_b<64, true>(a, bs, gp, wpc, st) : split_b<64, false>(a, bs, gp, wpc, st);
     return hipErrorInvalidValue;
+}
+
+hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, bool bf16, int* waves_per_cu) {
+    return split_any(nullptr, head_dim, block_size, group_pad, bf16, waves_per_cu, nullptr);
+}
+
+hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
+                        hipStream_t stream) {
+    if (a.num_waves < kWaves || a.num_waves % kWaves) return hipErrorInvalidValue;
+    return split_any(&a, head_dim, block_size, group_pad, bf16, nullptr, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

@@ -17,7 +17,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "pkv_kernels.h"
 
 namespace {
@@ -435,28 +435,35 @@ int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t tabl
     return PKV_OK;
 }
 
+}  // extern "C"
+
 // --------------------------------------------------------------------------
 // Decode
 // --------------------------------------------------------------------------
 
 namespace {
 
+constexpr int32_t kTile = pkv::kTileTokens;
+constexpr int32_t kMinChunk = 8;            // must equal the kernel's balanced-split minimum
+
 struct Plan {
-    int32_t part_size = 0;
-    int32_t max_parts = 0;
+    int32_t part_size = 0;                  // 0 = balanced split
+    int32_t fixed_chunk = 0;                // part_size / 16
+    int32_t max_seg = 0;
+    int32_t num_waves = 0;                  // resolved grid size (0 until resolved)
     int32_t group_pad = 0;
     bool bf16 = false;
     int32_t out_kind = pkv::kOutF32;
-    size_t ws_out_bytes = 0;
-    size_t ws_bytes = 0;
+    size_t hdr_bytes = 0, out_bytes = 0, ws_bytes = 0;
 };
 
-constexpr int32_t kDefaultPartition = 512;
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 int resolve(const pkv_attn_desc* d, Plan* pl) {
     if (!d) return fail(PKV_EINVAL, "null descriptor");
-    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_context_len < 0)
+    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_context_len < 0 || d->num_waves < 0)
         return fail(PKV_EINVAL, "descriptor: bad sizes");
+    if (d->num_seqs > pkv::kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d > %d", d->num_seqs, pkv::kMaxSeqs);
     if (d->num_q_heads % d->num_kv_heads)
         return fail(PKV_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d", d->num_q_heads, d->num_kv_heads);
     const int G = d->num_q_heads / d->num_kv_heads;
@@ -477,30 +484,97 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
     if (d->table_stride < need_w)
         return fail(PKV_EINVAL, "table_stride %d < ceil(max_context_len / block_size) = %lld", d->table_stride,
                     (long long)need_w);
-    int32_t P = d->partition_size;
-    if (P == 0) {
-        // One partition when every context fits in the default size, else the default.
-        const int32_t m = std::max(d->max_context_len, 1);
-        P = m <= kDefaultPartition ? (int32_t)(ceil_div(m, d->block_size) * d->block_size) : kDefaultPartition;
-        P = (int32_t)(ceil_div(P, d->block_size) * d->block_size);
-    }
-    if (P < 16 || P % d->block_size)
-        return fail(PKV_EINVAL, "partition_size %d must be a positive multiple of block_size %d", P, d->block_size);
+    const int32_t P = d->partition_size;
+    if (P < 0 || (P > 0 && P % d->block_size))
+        return fail(PKV_EINVAL, "partition_size %d must be 0 or a multiple of block_size %d", P, d->block_size);
     pl->part_size = P;
-    pl->max_parts = (int32_t)std::max<int64_t>(1, ceil_div(d->max_context_len, P));
+    pl->fixed_chunk = P / kTile;
+    const int64_t max_tiles = ceil_div(d->max_context_len, kTile);
+    if (P > 0) {
+        pl->max_seg = (int32_t)std::max<int64_t>(1, ceil_div(d->max_context_len, P));
+    } else {
+        pl->max_seg = (int32_t)(ceil_div(max_tiles, kMinChunk) + 1);
+    }
+    // Flattened tile indices are int32 on the device.
+    const int64_t per_seq = P > 0 ? (int64_t)pl->max_seg * pl->fixed_chunk : max_tiles;
+    if ((int64_t)d->num_seqs * d->num_kv_heads * per_seq >= (int64_t)1 << 30)
+        return fail(PKV_EUNSUPPORTED, "too many tiles in one call (num_seqs x kv heads x tiles >= 2^30)");
     pl->group_pad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
     pl->bf16 = d->kv_dtype == PKV_BF16;
-    if (pl->max_parts > 1) {
-        const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_parts;
-        pl->ws_out_bytes = (rows * d->head_dim * sizeof(float) + 255) / 256 * 256;
-        pl->ws_bytes = pl->ws_out_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+    const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_seg;
+    pl->hdr_bytes = up256(sizeof(int32_t) * (3 + (size_t)d->num_seqs));
+    pl->out_bytes = up256(rows * d->head_dim * sizeof(float));
+    pl->ws_bytes = pl->hdr_bytes + pl->out_bytes + up256(rows * sizeof(float));
+    return PKV_OK;
+}
+
+// Waves in the grid: the descriptor's value (rounded up to whole workgroups),
+// else every wave that fits the current device at once.  A fixed split never
+// gets more waves than it has chunks.
+int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
+    int64_t nw = d->num_waves;
+    if (nw == 0) {
+        static int cache[4][2][4][2][64];          // [D][bs][gp][bf16][device] -> waves per CU
+        static int cus[64];
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+        if (dev < 0 || dev >= 64) return fail(PKV_EUNSUPPORTED, "device index %d", dev);
+        const int di = d->head_dim == 128 ? 1 : 0, bi = d->block_size == 32 ? 1 : 0;
+        const int gi = pl->group_pad == 1 ? 0 : pl->group_pad == 2 ? 1 : pl->group_pad == 4 ? 2 : 3;
+        int& wpc = cache[di][bi][gi][pl->bf16 ? 1 : 0][dev];
+        if (wpc == 0) {
+            e = pkv::split_waves_per_cu(d->head_dim, d->block_size, pl->group_pad, pl->bf16, &wpc);
+            if (e != hipSuccess) return fail_hip(e, "occupancy query");
+        }
+        if (cus[dev] == 0) {
+            e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+        }
+        nw = (int64_t)std::max(wpc, 4) * cus[dev];
+    }
+    if (pl->fixed_chunk > 0) {
+        const int64_t chunks = (int64_t)d->num_seqs * d->num_kv_heads * pl->max_seg;
+        nw = std::min(nw, std::max<int64_t>(chunks, 1));
+    }
+    nw = std::min<int64_t>((nw + 3) / 4 * 4, (int64_t)1 << 28);
+    pl->num_waves = (int32_t)nw;
+    return PKV_OK;
+}
+
+// The split the kernel makes, replayed on the host for given lengths: calls
+// f(seq, kv_head, slot, tok_lo, tok_hi) for every segment in order.
+template <class F>
+int enumerate_segments(const pkv_attn_desc* d, const Plan& pl, const int32_t* ctx_host, F&& f) {
+    const int B = d->num_seqs, Hkv = d->num_kv_heads;
+    std::vector<int64_t> pre(B + 1, 0);
+    std::vector<int32_t> nt(B), pt(B);
+    for (int s = 0; s < B; ++s) {
+        const int32_t n = std::min(std::max(ctx_host[s], 0), d->max_context_len);
+        nt[s] = (int32_t)ceil_div(n, kTile);
+        pt[s] = pl.fixed_chunk > 0 ? (int32_t)(ceil_div(nt[s], pl.fixed_chunk) * pl.fixed_chunk) : nt[s];
+        pre[s + 1] = pre[s] + (int64_t)pt[s] * Hkv;
+    }
+    const int64_t T = pre[B];
+    const int64_t C = pl.fixed_chunk > 0 ? pl.fixed_chunk : std::max<int64_t>(kMinChunk, ceil_div(T, pl.num_waves));
+    for (int s = 0; s < B; ++s) {
+        for (int g = 0; g < Hkv && nt[s] > 0; ++g) {
+            const int64_t first = pre[s] + (int64_t)g * pt[s];
+            const int64_t c0 = first / C, c1 = (first + nt[s] - 1) / C;
+            for (int64_t ch = c0; ch <= c1; ++ch) {
+                const int64_t j0 = std::max<int64_t>(ch * C - first, 0);
+                const int64_t j1 = std::min<int64_t>((ch + 1) * C - first, nt[s]);
+                const int32_t tlo = (int32_t)(j0 * kTile);
+                const int32_t thi = (int32_t)std::min<int64_t>(j1 * kTile, std::min(ctx_host[s], d->max_context_len));
+                f(s, g, (int32_t)(ch - c0), tlo, thi);
+            }
+        }
     }
     return PKV_OK;
 }
 
-int check_ptrs(const pkv_attn_desc* d, const Plan& pl, const void* q, const void* k, const void* v,
-               const int32_t* tables, const int32_t* lens, const void* out, const void* ws, size_t ws_bytes,
-               bool need_inputs) {
+int check_ptrs(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* tables,
+               const int32_t* lens, const void* out, const void* ws, size_t ws_bytes, bool need_inputs) {
     if (need_inputs) {
         if (!q || !k || !v || !tables || !lens) return fail(PKV_EINVAL, "null input pointer");
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(tables, 4) || !aligned(lens, 4))
@@ -508,21 +582,28 @@ int check_ptrs(const pkv_attn_desc* d, const Plan& pl, const void* q, const void
     }
     if (!out) return fail(PKV_EINVAL, "null out");
     if (!aligned(out, pl.out_kind == pkv::kOutF32 ? 4 : 2)) return fail(PKV_EINVAL, "out misaligned");
-    if (pl.max_parts > 1) {
-        if (!ws || ws_bytes < pl.ws_bytes)
-            return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
-        if (!aligned(ws, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
-    }
-    (void)d;
+    if (!ws || ws_bytes < pl.ws_bytes)
+        return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
+    if (!aligned(ws, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     return PKV_OK;
 }
 
 }  // namespace
 
+extern "C" {
+
 int32_t paged_attn_partition_size(const pkv_attn_desc* d) {
     Plan pl;
     int rc = resolve(d, &pl);
     return rc ? rc : pl.part_size;
+}
+
+int32_t paged_attn_grid_waves(const pkv_attn_desc* d) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    rc = resolve_waves(d, &pl);
+    return rc ? rc : pl.num_waves;
 }
 
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
@@ -538,8 +619,11 @@ int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void
     int rc = resolve(d, &pl);
     if (rc) return rc;
     if (d->num_seqs == 0) return PKV_OK;
-    rc = check_ptrs(d, pl, q, k_cache, v_cache, block_tables, context_lens, out, workspace, workspace_bytes, true);
+    rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, workspace, workspace_bytes, true);
     if (rc) return rc;
+    rc = resolve_waves(d, &pl);
+    if (rc) return rc;
+    char* ws = reinterpret_cast<char*>(workspace);
     pkv::DecodeArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -548,22 +632,21 @@ int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void
     a.context_lens = context_lens;
     a.out = out;
     a.lse = lse;
-    a.ws_out = pl.max_parts > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
-    a.ws_lse = pl.max_parts > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pl.ws_out_bytes)
-                                : nullptr;
+    a.ws_hdr = reinterpret_cast<int32_t*>(ws);
+    a.ws_out = reinterpret_cast<float*>(ws + pl.hdr_bytes);
+    a.ws_lse = reinterpret_cast<float*>(ws + pl.hdr_bytes + pl.out_bytes);
     a.scale = scale;
     a.num_seqs = d->num_seqs;
     a.num_q_heads = d->num_q_heads;
     a.num_kv_heads = d->num_kv_heads;
     a.table_stride = d->table_stride;
-    a.part_size = pl.part_size;
-    a.max_parts = pl.max_parts;
+    a.fixed_chunk = pl.fixed_chunk;
+    a.num_waves = pl.num_waves;
+    a.max_seg = pl.max_seg;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
-    const int64_t n = (int64_t)d->num_seqs * d->num_kv_heads * pl.max_parts;
-    if (n > 0x7FFFFFFF) return fail(PKV_EUNSUPPORTED, "grid of %lld workgroups", (long long)n);
-    hipError_t e = pkv::launch_partition(a, d->head_dim, d->block_size, pl.group_pad, pl.bf16, (hipStream_t)stream);
-    if (e != hipSuccess) return fail_hip(e, "partition kernel launch");
+    hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.bf16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "split kernel launch");
     return PKV_OK;
 }
 
@@ -572,20 +655,23 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     Plan pl;
     int rc = resolve(d, &pl);
     if (rc) return rc;
-    if (d->num_seqs == 0 || pl.max_parts <= 1) return PKV_OK;
+    if (d->num_seqs == 0 || pl.max_seg <= 1) return PKV_OK;
     if (!context_lens || !aligned(context_lens, 4)) return fail(PKV_EINVAL, "null context_lens");
-    rc = check_ptrs(d, pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, workspace, workspace_bytes, false);
+    rc = check_ptrs(pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, workspace, workspace_bytes, false);
     if (rc) return rc;
+    const char* ws = reinterpret_cast<const char*>(workspace);
     pkv::MergeArgs a{};
     a.context_lens = context_lens;
-    a.ws_out = reinterpret_cast<const float*>(workspace);
-    a.ws_lse = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + pl.ws_out_bytes);
+    a.ws_hdr = reinterpret_cast<const int32_t*>(ws);
+    a.ws_out = reinterpret_cast<const float*>(ws + pl.hdr_bytes);
+    a.ws_lse = reinterpret_cast<const float*>(ws + pl.hdr_bytes + pl.out_bytes);
     a.out = out;
     a.lse = lse;
     a.num_seqs = d->num_seqs;
     a.num_q_heads = d->num_q_heads;
-    a.part_size = pl.part_size;
-    a.max_parts = pl.max_parts;
+    a.num_kv_heads = d->num_kv_heads;
+    a.fixed_chunk = pl.fixed_chunk;
+    a.max_seg = pl.max_seg;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
     hipError_t e = pkv::launch_merge(a, d->head_dim, (hipStream_t)stream);
@@ -608,24 +694,24 @@ int paged_attn_plan(const pkv_attn_desc* d, const int32_t* context_lens_host, in
     int rc = resolve(d, &pl);
     if (rc) return rc;
     if (!n_out || (d->num_seqs > 0 && !context_lens_host)) return fail(PKV_EINVAL, "paged_attn_plan: null argument");
+    for (int32_t s = 0; s < d->num_seqs; ++s)
+        if (context_lens_host[s] < 0 || context_lens_host[s] > d->max_context_len)
+            return fail(PKV_EINVAL, "paged_attn_plan: context_lens[%d] = %d outside [0, %d]", s, context_lens_host[s],
+                        d->max_context_len);
+    rc = resolve_waves(d, &pl);
+    if (rc) return rc;
     int64_t n = 0;
-    for (int32_t s = 0; s < d->num_seqs; ++s) {
-        const int32_t c = context_lens_host[s];
-        if (c < 0 || c > d->max_context_len)
-            return fail(PKV_EINVAL, "paged_attn_plan: context_lens[%d] = %d outside [0, %d]", s, c, d->max_context_len);
-        const int64_t np = ceil_div(c, pl.part_size);
-        for (int32_t g = 0; g < d->num_kv_heads; ++g)
-            for (int64_t pp = 0; pp < np; ++pp, ++n) {
-                if (items_out && n < cap) {
-                    int32_t* r = items_out + n * 5;
-                    r[0] = s;
-                    r[1] = g;
-                    r[2] = (int32_t)pp;
-                    r[3] = (int32_t)(pp * pl.part_size);
-                    r[4] = (int32_t)std::min<int64_t>((pp + 1) * pl.part_size, c);
-                }
-            }
-    }
+    enumerate_segments(d, pl, context_lens_host, [&](int32_t s, int32_t g, int32_t k, int32_t lo, int32_t hi) {
+        if (items_out && n < cap) {
+            int32_t* r = items_out + n * 5;
+            r[0] = s;
+            r[1] = g;
+            r[2] = k;
+            r[3] = lo;
+            r[4] = hi;
+        }
+        ++n;
+    });
     *n_out = n;
     return PKV_OK;
 }

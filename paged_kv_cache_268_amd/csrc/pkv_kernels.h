@@ -10,6 +10,9 @@ namespace pkv {
 constexpr int kNumXcds = 8;      // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kOutF32 = 0, kOutF16 = 1, kOutBF16 = 2;
 
+constexpr int kMaxSeqs = 4096;   // sequences per decode call (prefix of tile counts kept in LDS)
+constexpr int kTileTokens = 16;  // tokens per tile of the split
+
 struct DecodeArgs {
     const void* q;
     const void* k_cache;
@@ -18,29 +21,33 @@ struct DecodeArgs {
     const int32_t* context_lens;
     void* out;
     float* lse;              // natural log, nullable
-    float* ws_out;           // [B][Hq][max_parts][D]
-    float* ws_lse;           // [B][Hq][max_parts], log2 domain
+    int32_t* ws_hdr;         // [2 + B + 1]: T, C, prefix of padded tiles (x Hkv) over sequences
+    float* ws_out;           // [B][Hq][max_seg][D] normalised segment outputs
+    float* ws_lse;           // [B][Hq][max_seg], log2 domain
     float scale;
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t table_stride;
-    int32_t part_size;
-    int32_t max_parts;
+    int32_t fixed_chunk;     // tiles per chunk (partition_size / 16); 0 = balanced split
+    int32_t num_waves;       // waves in the grid (multiple of 4)
+    int32_t max_seg;         // segment slots per (sequence, q head) in the workspace
     int32_t max_context_len;
     int32_t out_dtype;       // kOut*
 };
 
 struct MergeArgs {
     const int32_t* context_lens;
+    const int32_t* ws_hdr;
     const float* ws_out;
     const float* ws_lse;
     void* out;
     float* lse;
     int32_t num_seqs;
     int32_t num_q_heads;
-    int32_t part_size;
-    int32_t max_parts;
+    int32_t num_kv_heads;
+    int32_t fixed_chunk;
+    int32_t max_seg;
     int32_t max_context_len;
     int32_t out_dtype;
 };
@@ -65,8 +72,10 @@ struct AppendArgs {
     int32_t table_stride;
 };
 
-hipError_t launch_partition(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
-                            hipStream_t stream);
+hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
+                        hipStream_t stream);
+// Resident waves per CU of the split kernel instance (occupancy query).
+hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, bool bf16, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, bool any_copy, hipStream_t stream);
 

@@ -23,7 +23,7 @@ EXPORTS = (
     "pkv_last_error", "pkv_version",
     "kv_block_pool_create", "kv_block_pool_destroy", "kv_seq_add", "kv_seq_import", "kv_seq_fork",
     "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_write_tables",
-    "kv_validate_tables", "paged_attn_partition_size", "paged_attn_workspace_bytes",
+    "kv_validate_tables", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
 )
 
@@ -43,7 +43,7 @@ class PoolDesc(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
-        "table_stride", "max_context_len", "partition_size", "q_dtype", "kv_dtype", "out_dtype")]
+        "table_stride", "max_context_len", "partition_size", "q_dtype", "kv_dtype", "out_dtype", "num_waves")]
 
 
 _lib = None
@@ -75,6 +75,7 @@ def load(path: str = LIB_PATH):
         "kv_write_tables": ([P, P, P, P], ctypes.c_int),
         "kv_validate_tables": ([I32, P, I32, I32, P, I32, I32], ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
+        "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], SZ),
         "paged_attn_decode": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P],
                               ctypes.c_int),
@@ -129,18 +130,18 @@ def _i32(a) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def attn_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, table_stride,
-              max_context_len, partition_size=0, dtype=PKV_BF16, out_dtype=PKV_F32) -> AttnDesc:
+              max_context_len, partition_size=0, dtype=PKV_BF16, out_dtype=PKV_F32, num_waves=0) -> AttnDesc:
     return AttnDesc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, table_stride,
-                    max_context_len, partition_size, dtype, dtype, out_dtype)
+                    max_context_len, partition_size, dtype, dtype, out_dtype, num_waves)
 
 
-def desc_for(q, k_cache, block_tables, max_context_len, partition_size=0, out_dtype=None) -> AttnDesc:
+def desc_for(q, k_cache, block_tables, max_context_len, partition_size=0, out_dtype=None, num_waves=0) -> AttnDesc:
     B, Hq, D = q.shape
     NB, Hkv, bs, D2 = k_cache.shape
     assert D == D2
     od = PKV_F32 if out_dtype is None else out_dtype
     return attn_desc(B, Hq, Hkv, D, bs, NB, block_tables.stride(0), max_context_len, partition_size,
-                     dtype_code(q), od)
+                     dtype_code(q), od, num_waves)
 
 
 def partition_size(desc: AttnDesc) -> int:
@@ -150,8 +151,30 @@ def partition_size(desc: AttnDesc) -> int:
     return r
 
 
+def grid_waves(desc: AttnDesc) -> int:
+    r = load().paged_attn_grid_waves(ctypes.byref(desc))
+    if r < 0:
+        check(r)
+    return r
+
+
 def workspace_bytes(desc: AttnDesc) -> int:
     return load().paged_attn_workspace_bytes(ctypes.byref(desc))
+
+
+def workspace_views(desc: AttnDesc, ws):
+    """(hdr int32, seg_out float [B][Hq][S][D], seg_lse float [B][Hq][S]) views of a uint8 workspace tensor,
+    following the layout include/pkv.h documents for paged_attn_workspace_bytes."""
+    import torch
+    B, Hq, D = desc.num_seqs, desc.num_q_heads, desc.head_dim
+    P, mc = desc.partition_size, desc.max_context_len
+    S = max(1, -(-mc // P)) if P > 0 else -(-(-(-mc // 16)) // 8) + 1
+    up = lambda x: (x + 255) // 256 * 256
+    hb, ob = up(4 * (3 + B)), up(B * Hq * S * D * 4)
+    hdr = ws[:4 * (3 + B)].view(torch.int32)
+    seg_out = ws[hb:hb + B * Hq * S * D * 4].view(torch.float32).view(B, Hq, S, D)
+    seg_lse = ws[hb + ob:hb + ob + B * Hq * S * 4].view(torch.float32).view(B, Hq, S)
+    return hdr, seg_out, seg_lse
 
 
 def alloc_workspace(desc: AttnDesc, device):
@@ -162,12 +185,12 @@ def alloc_workspace(desc: AttnDesc, device):
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, *,
            out=None, lse=None, partition_size: int = 0, workspace=None, stream=None, out_dtype=None,
-           desc: Optional[AttnDesc] = None):
+           num_waves: int = 0, desc: Optional[AttnDesc] = None):
     """paged_attn_decode.  Returns out (allocated as fp32 unless given)."""
     import torch
     if desc is None:
         od = out_dtype if out_dtype is not None else (dtype_code(out) if out is not None else PKV_F32)
-        desc = desc_for(q, k_cache, block_tables, max_context_len, partition_size, od)
+        desc = desc_for(q, k_cache, block_tables, max_context_len, partition_size, od, num_waves)
     if out is None:
         tdt = {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16}[desc.out_dtype]
         out = torch.empty(q.shape, dtype=tdt, device=q.device)
@@ -193,7 +216,7 @@ def merge(desc, context_lens, out, lse, workspace, stream=None):
 
 
 def plan(desc: AttnDesc, context_lens_host) -> np.ndarray:
-    """Work items (seq, kv_head, partition, tok_lo, tok_hi) as an int32 [n][5] array."""
+    """Segments (seq, kv_head, slot, tok_lo, tok_hi) of the split as an int32 [n][5] array."""
     ctx = _i32(context_lens_host)
     n = ctypes.c_int64(0)
     lib = load()

@@ -33,11 +33,11 @@ def to_dev(wl):
     return tab, ctx
 
 
-def gpu_decode(wl, q, k, v, tab, ctx, partition_size=None, out_dtype=pkv.PKV_F32, with_lse=True):
+def gpu_decode(wl, q, k, v, tab, ctx, partition_size=None, out_dtype=pkv.PKV_F32, with_lse=True, num_waves=0):
     P = wl.partition_size if partition_size is None else partition_size
     lse = torch.full((wl.num_seqs, wl.num_q_heads), float("nan"), device=DEV) if with_lse else None
     out = pkv.decode(q, k, v, tab, ctx, wl.scale, wl.max_context_len, partition_size=P, out_dtype=out_dtype,
-                     lse=lse)
+                     lse=lse, num_waves=num_waves)
     torch.cuda.synchronize()
     return out, lse
 
@@ -76,10 +76,13 @@ def test_parity_config(cid):
          f"P={wl.partition_size} blocks={wl.num_blocks}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
-    out, lse = gpu_decode(wl, q, k, v, tab, ctx)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
-    err = compare(out, lse, ref_out, ref_lse, what=f"config {cid}")
-    note(f"config {cid}: max abs err {err:.3g}")
+    # The configuration's own split (config 4: fixed 512-token partitions), the
+    # balanced split, and fixed 512-token partitions for all.
+    for P in sorted({wl.partition_size, 0, 512}):
+        out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
+        err = compare(out, lse, ref_out, ref_lse, what=f"config {cid} P={P}")
+        note(f"config {cid} P={P}: max abs err {err:.3g}")
 
 
 def _compact(wl, seqs):
@@ -102,6 +105,7 @@ def test_parity_config5_sampled():
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
     out, lse = gpu_decode(wl, q, k, v, tab, ctx)
+    out512, lse512 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=512)
     rng = np.random.default_rng(5)
     long_ids = np.nonzero(wl.context_lens > 2048)[0]
     seqs = sorted(set(range(8)) | set(rng.choice(long_ids, 6, replace=False).tolist())
@@ -113,8 +117,8 @@ def test_parity_config5_sampled():
     ref_out, ref_lse = oracle.paged_decode(qb, kb, vb, ctab, cctx, wl.scale, num_kv_heads=wl.num_kv_heads,
                                            block_size=wl.block_size, dtype=oracle.BF16)
     err = compare(out[seqs], lse[seqs], ref_out, ref_lse, what="config 5 sample")
-    o = out.cpu().numpy()
-    assert np.all(np.isfinite(o))
+    compare(out512[seqs], lse512[seqs], ref_out, ref_lse, what="config 5 sample P=512")
+    assert np.all(np.isfinite(out.cpu().numpy())) and np.all(np.isfinite(out512.cpu().numpy()))
     note(f"config 5 sample of {len(seqs)}: max abs err {err:.3g}")
 
 
@@ -156,12 +160,13 @@ def test_equal_scores_give_mean():
             assert abs(lse[s, h].item() - math.log(c)) <= TOL
 
 
-def test_permutation_bit_exact():
+@pytest.mark.parametrize("P", [256, 0])
+def test_permutation_bit_exact(P):
     wl = small(seed=3, pool_factor=2.0)
-    note("physical permutation")
+    note(f"physical permutation P={P}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
-    out0, lse0 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=256)
+    out0, lse0 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
     perm = torch.from_numpy(np.random.default_rng(7).permutation(wl.num_blocks)).to(DEV)
     k2 = torch.empty_like(k); v2 = torch.empty_like(v)
     k2[perm] = k; v2[perm] = v
@@ -170,7 +175,7 @@ def test_permutation_bit_exact():
     t2[t2 >= 0] = pm[t2[t2 >= 0]]
     wl.block_tables = t2
     tab2, _ = to_dev(wl)
-    out1, lse1 = gpu_decode(wl, q, k2, v2, tab2, ctx, partition_size=256)
+    out1, lse1 = gpu_decode(wl, q, k2, v2, tab2, ctx, partition_size=P)
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
 
 
@@ -195,72 +200,73 @@ def test_shared_prefix_equals_duplicated():
     compare(out0, lse0, ref_out, ref_lse, what="shared prefix")
 
 
-def test_deterministic_and_tail_poison_bit_exact():
+@pytest.mark.parametrize("P", [256, 0])
+def test_deterministic_and_tail_poison_bit_exact(P):
     wl = small(seed=5, extra_table_entries=3)
-    note("run twice; clean vs NaN-poisoned unused slots")
+    note(f"run twice; clean vs NaN-poisoned unused slots, P={P}")
     q, k, v = W.make_values(wl, DEV)
     tab, ctx = to_dev(wl)
-    out0, lse0 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=256)
-    out1, lse1 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=256)
+    out0, lse0 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
+    out1, lse1 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
     W.poison_unused_(wl, k, v)
-    out2, lse2 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=256)
+    out2, lse2 = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
     assert torch.equal(out0, out2) and torch.equal(lse0, lse2)
 
 
-@pytest.mark.parametrize("P", [16, 32, 48, 256, 512, 2048])
-def test_split_sizes_match_oracle(P):
+@pytest.mark.parametrize("P,nw", [(16, 0), (32, 0), (48, 0), (256, 0), (512, 0), (2048, 0), (0, 0), (0, 4),
+                                  (0, 8), (0, 12), (0, 64), (512, 4), (16, 4)])
+def test_split_sizes_match_oracle(P, nw):
     wl = small(seed=6, ctx=(1, 15, 16, 17, 511, 512, 513, 2000), B=8)
-    note(f"partition size {P}")
+    note(f"partition size {P}, {nw} waves")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
-    out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
+    out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P, num_waves=nw)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
-    compare(out, lse, ref_out, ref_lse, what=f"P={P}")
+    compare(out, lse, ref_out, ref_lse, what=f"P={P} nw={nw}")
 
 
-def test_partials_are_the_partitions():
-    """Each partition's partial (workspace) equals the oracle on [pP, min((p+1)P, len))."""
-    wl = small(seed=7, ctx=(5, 700, 1024, 1500), B=4)
-    P = 256
-    note("workspace partials vs oracle sub-ranges")
+@pytest.mark.parametrize("P,nw", [(256, 0), (0, 8), (0, 16), (512, 4)])
+def test_segments_are_the_plan(P, nw):
+    """Each segment's output in the workspace equals the oracle on its token range."""
+    wl = small(seed=7, ctx=(5, 700, 1024, 1500, 0, 33), B=6)
+    note(f"workspace segments vs oracle sub-ranges, P={P} nw={nw}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
-    desc = pkv.desc_for(q, k, tab, wl.max_context_len, P)
+    desc = pkv.desc_for(q, k, tab, wl.max_context_len, P, num_waves=nw)
     ws = pkv.alloc_workspace(desc, DEV)
     ws.fill_(255)                                              # NaN pattern in every float
     out = torch.zeros(q.shape, device=DEV)
     lse = torch.zeros(q.shape[:2], device=DEV)
     pkv.decode_partials(desc, q, k, v, tab, ctx, wl.scale, out, lse, ws)
     torch.cuda.synchronize()
-    maxP = -(-wl.max_context_len // P)
-    B, Hq, D = q.shape
-    wsf = ws.view(torch.float32)
-    nout = B * Hq * maxP * D
-    part_out = wsf[:nout].view(B, Hq, maxP, D).cpu().numpy()
-    off = (nout * 4 + 255) // 256 * 256 // 4
-    part_lse = wsf[off:off + B * Hq * maxP].view(B, Hq, maxP).cpu().numpy()
+    _, seg_out, seg_lse = pkv.workspace_views(desc, ws)
+    seg_out, seg_lse = seg_out.cpu().numpy(), seg_lse.cpu().numpy()
     items = pkv.plan(desc, wl.context_lens)
-    want_items = np.array(R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P), dtype=np.int32)
-    assert np.array_equal(items, want_items)
-    for p in range(maxP):
-        lo = np.full(B, p * P, np.int32); hi = np.full(B, (p + 1) * P, np.int32)
-        ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v, tok_lo=lo, tok_hi=hi)
-        for s in range(B):
-            n = -(-int(wl.context_lens[s]) // P)
-            if n <= 1:
-                continue                                       # written directly to out
-            if p < n:
-                assert np.abs(part_out[s, :, p] - ref_out[s]).max() <= TOL
-                assert np.abs(part_lse[s, :, p] / math.log2(math.e) - ref_lse[s]).max() <= TOL
-            else:
-                assert np.all(np.isnan(part_out[s, :, p])) and np.all(np.isnan(part_lse[s, :, p]))
-    # a one-partition sequence was written straight to out
-    ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
-    compare(out[0:1], lse[0:1], ref_out[0:1], ref_lse[0:1], what="direct")
+    want = np.array(R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc)), dtype=np.int32)
+    assert np.array_equal(items, want.reshape(-1, 5))
+    G = wl.num_q_heads // wl.num_kv_heads
+    nseg = {}
+    for s_, g, kslot, lo, hi in items.tolist():
+        nseg[(s_, g)] = nseg.get((s_, g), 0) + 1
+    ref_full, ref_full_lse = oracle.paged_decode_workload(wl, q, k, v)
+    used = np.zeros(seg_lse.shape, dtype=bool)
+    for s_, g, kslot, lo, hi in items.tolist():
+        heads = slice(g * G, (g + 1) * G)
+        if nseg[(s_, g)] == 1:                                 # written straight to out
+            compare(out[s_, heads][None], lse[s_, heads][None], ref_full[s_, heads][None],
+                    ref_full_lse[s_, heads][None], what="direct")
+            continue
+        los = np.zeros(wl.num_seqs, np.int32); his = np.zeros(wl.num_seqs, np.int32)
+        los[s_], his[s_] = lo, hi
+        ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v, tok_lo=los, tok_hi=his)
+        assert np.abs(seg_out[s_, heads, kslot] - ref_out[s_, heads]).max() <= TOL
+        assert np.abs(seg_lse[s_, heads, kslot] / math.log2(math.e) - ref_lse[s_, heads]).max() <= TOL
+        used[s_, heads, kslot] = True
+    assert np.all(np.isnan(seg_lse[~used]))                    # nothing else was written
     pkv.merge(desc, ctx, out, lse, ws)
     torch.cuda.synchronize()
-    compare(out, lse, ref_out, ref_lse, what="merged")
+    compare(out, lse, ref_full, ref_full_lse, what="merged")
 
 
 def test_empty_context():
@@ -268,7 +274,7 @@ def test_empty_context():
     note("empty contexts")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
-    for P in (256, 1024):
+    for P in (256, 1024, 0):
         out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
         ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
         compare(out, lse, ref_out, ref_lse, what=f"empty P={P}")
@@ -313,12 +319,13 @@ def test_random_small_shapes(seed):
     Hkv = int(rng.integers(1, 5)); G = int(rng.choice([1, 2, 3, 4, 5, 8])); B = int(rng.integers(1, 9))
     ctx = rng.integers(0, 3000, B)
     P = int(rng.choice([0, bs, 2 * bs, 512, 4096]))
+    nw = int(rng.choice([0, 4, 8, 40]))
     wl = W.make_workload(B, Hkv * G, Hkv, D, bs, dtype, ctx, seed, pool_factor=float(rng.uniform(1, 2)),
                          extra_table_entries=int(rng.integers(0, 3)), partition_size=P)
-    note(f"random seed={seed} D={D} bs={bs} {dtype} Hkv={Hkv} G={G} B={B} P={P} ctx={ctx.tolist()}")
+    note(f"random seed={seed} D={D} bs={bs} {dtype} Hkv={Hkv} G={G} B={B} P={P} nw={nw} ctx={ctx.tolist()}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, dctx = to_dev(wl)
-    out, lse = gpu_decode(wl, q, k, v, tab, dctx)
+    out, lse = gpu_decode(wl, q, k, v, tab, dctx, num_waves=nw)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
     compare(out, lse, ref_out, ref_lse, what=f"random {seed}")
 

@@ -176,32 +176,51 @@ def test_bad_pool_arguments():
 # Decode descriptor, plan, workspace, errors (host only)
 # ---------------------------------------------------------------------------
 
-def test_plan_matches_replay_bit_exact():
+@pytest.mark.parametrize("P,bs,nw", [(512, 16, 64), (256, 32, 4), (48, 16, 1000), (0, 16, 64), (0, 32, 3072),
+                                       (0, 16, 4), (0, 16, 100000)])
+def test_plan_matches_replay_bit_exact(P, bs, nw):
     rng = np.random.default_rng(0)
     ctx = rng.integers(0, 5000, 37).astype(np.int32)
     ctx[3] = 0
     ctx[5] = 512
-    for P, bs in ((512, 16), (256, 32), (48, 16), (0, 16)):
-        d = pkv.attn_desc(37, 32, 8, 128, bs, 10000, 400, int(ctx.max()), P)
-        used = pkv.partition_size(d)
-        got = pkv.plan(d, ctx)
-        want = np.array(R.plan(ctx.tolist(), 8, used), dtype=np.int32).reshape(-1, 5)
-        assert np.array_equal(got, want)
+    ctx[6] = 1
+    d = pkv.attn_desc(37, 32, 8, 128, bs, 10000, 400, int(ctx.max()), P, num_waves=nw)
+    got = pkv.plan(d, ctx)
+    want = np.array(R.plan(ctx.tolist(), 8, P, pkv.grid_waves(d)), dtype=np.int32).reshape(-1, 5)
+    assert np.array_equal(got, want)
+    # Every token of every (seq, kv head) is covered exactly once, in order.
+    for s in range(37):
+        for g in range(8):
+            rows = got[(got[:, 0] == s) & (got[:, 1] == g)]
+            if ctx[s] == 0:
+                assert len(rows) == 0
+                continue
+            assert rows[0, 3] == 0 and rows[-1, 4] == ctx[s]
+            assert np.array_equal(rows[1:, 3], rows[:-1, 4]) and np.array_equal(rows[:, 2], np.arange(len(rows)))
+    if P > 0:                                             # fixed mode: segments are the partitions
+        part = got[:, 3] // P
+        assert np.array_equal(part, got[:, 2]) and np.all(got[:, 4] - got[:, 3] <= P)
 
 
-def test_auto_partition_and_workspace():
-    d = pkv.attn_desc(4, 4, 4, 64, 16, 64, 16, 256, 0, pkv.PKV_F16)
-    assert pkv.partition_size(d) == 256 and pkv.workspace_bytes(d) == 0
-    d = pkv.attn_desc(64, 32, 8, 128, 16, 30000, 512, 8192, 0)
-    P = pkv.partition_size(d)
-    assert P == 512
-    rows = 64 * 32 * (8192 // 512)
-    def up(x):
-        return (x + 255) // 256 * 256
-    assert pkv.workspace_bytes(d) == up(rows * 128 * 4) + up(rows * 4)
+def test_split_sizes_and_workspace():
+    d = pkv.attn_desc(4, 4, 4, 64, 16, 64, 16, 256, 0, pkv.PKV_F16, num_waves=8)
+    assert pkv.partition_size(d) == 0 and pkv.grid_waves(d) == 8
+    up = lambda x: (x + 255) // 256 * 256
+    S = -(-(256 // 16) // 8) + 1
+    assert pkv.workspace_bytes(d) == up(4 * 7) + up(4 * 4 * S * 64 * 4) + up(4 * 4 * S * 4)
+    d = pkv.attn_desc(64, 32, 8, 128, 16, 30000, 512, 8192, 512, num_waves=0)
+    S = 8192 // 512
+    assert pkv.workspace_bytes(d) == up(4 * 67) + up(64 * 32 * S * 128 * 4) + up(64 * 32 * S * 4)
+    # a fixed split never gets more waves than chunks
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 512, num_waves=4000)
+    assert pkv.grid_waves(d) == 2 * 4 * 2
     d = pkv.attn_desc(2, 2, 2, 64, 32, 8, 4, 100, 48)
     with pytest.raises(pkv.PkvError):
         pkv.partition_size(d)                             # 48 is not a multiple of 32
+    d = pkv.attn_desc(5000, 8, 8, 128, 16, 100, 64, 1000, 0)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.partition_size(d)                             # more sequences than one call takes
+    assert e.value.code == pkv.PKV_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -214,7 +233,7 @@ def test_auto_partition_and_workspace():
     ("table_stride", 3, pkv.PKV_EINVAL),                  # < ceil(1000 / 16)
 ])
 def test_descriptor_errors(field, value, code):
-    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 0)
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 0, num_waves=64)
     setattr(d, field, value)
     if field == "kv_dtype":
         d.q_dtype = value
@@ -227,7 +246,7 @@ def test_descriptor_errors(field, value, code):
 
 
 def test_workspace_too_small_is_refused():
-    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 0)
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 0, num_waves=64)
     need = pkv.workspace_bytes(d)
     assert need > 0
     lib = pkv.load()
@@ -241,7 +260,7 @@ def test_workspace_too_small_is_refused():
 
 
 def test_misaligned_inputs_are_refused():
-    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0)
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0, num_waves=64)
     lib = pkv.load()
     ok = ctypes.c_void_p(1 << 20)
     bad = ctypes.c_void_p((1 << 20) + 8)

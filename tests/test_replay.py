@@ -118,9 +118,25 @@ def test_random_ops_conserve_blocks():
         assert not set(held) & set(pool.free)
 
 
-def test_plan_enumeration():
+def test_plan_fixed_partitions():
     items = R.plan([0, 5, 1024, 1025], num_kv_heads=2, partition_size=512)
     assert items[:2] == [(1, 0, 0, 0, 5), (1, 1, 0, 0, 5)]
     assert (2, 1, 1, 512, 1024) in items and (3, 0, 2, 1024, 1025) in items
     assert len(items) == 2 * (1 + 2 + 3)
     assert items == sorted(items)
+
+
+def test_plan_balanced_worked_example():
+    # Two sequences of 40 and 200 tokens, one kv head: 3 + 13 = 16 tiles.
+    # 2 waves -> C = max(8, 8) = 8 tiles: chunk 0 = tiles 0..7, chunk 1 = 8..15.
+    # Sequence 0 (tiles 0..2) is whole in chunk 0; sequence 1 starts at tile 3:
+    # its tiles 0..4 are in chunk 0 (slot 0), tiles 5..12 in chunk 1 (slot 1).
+    items = R.plan([40, 200], num_kv_heads=1, partition_size=0, num_waves=2)
+    assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200)]
+    # Many waves: the chunk never drops below 8 tiles (128 tokens).
+    items = R.plan([40, 200], num_kv_heads=1, partition_size=0, num_waves=1000)
+    assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200)]
+    # One wave: everything in one chunk, every (seq, head) whole.
+    items = R.plan([40, 200, 0, 7], num_kv_heads=2, partition_size=0, num_waves=1)
+    assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 200), (1, 1, 0, 0, 200),
+                     (3, 0, 0, 0, 7), (3, 1, 0, 0, 7)]
