@@ -217,14 +217,16 @@ int32_t paged_attn_grid_waves(const pkv_attn_desc* desc);
 /* Bytes of device workspace paged_attn_decode needs.  Layout, each part
  * 256-byte aligned, with S = segment slots (fixed: ceil(max_context_len / P);
  * balanced: ceil(ceil(max_context_len / 16) / 8) + 1):
- *   int32 hdr[2 + num_seqs + 1]              (tiles, chunk size, tile prefix)
+ *   int32 hdr[3 + num_seqs]   (tiles, chunk size, tile prefix [num_seqs + 1])
  *   float seg_out[num_seqs][num_q_heads][S][head_dim]   (normalised outputs)
  *   float seg_lse[num_seqs][num_q_heads][S]             (log2-domain lse) */
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* desc);
 
 /* The whole decode: the split pass, then (if a (sequence, kv head) may span
  * several segments) the merge pass, both on `stream`.  workspace: device,
- * 256-byte aligned, workspace_bytes >= paged_attn_workspace_bytes(desc). */
+ * 256-byte aligned, workspace_bytes >= paged_attn_workspace_bytes(desc); its
+ * contents on entry do not matter.  Calls sharing one workspace must be
+ * ordered (same stream or synchronised). */
 int paged_attn_decode(const pkv_attn_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, float scale, void* out, float* lse,

@@ -1,12 +1,16 @@
 // pkv_append.hip -- write one new token's K/V per sequence into its slot.
 //
 // The host has already reserved the slots (free-list pops, copy-on-write
-// decisions); each work item arrives as (seq, slot, table_pos, new_block,
-// cow_src, cow_ntok, new_len).  One 64-thread workgroup per (item, kv head):
-//   1. copy-on-write: rows [0, cow_ntok) of (cow_src, g) -> (new_block, g), K and V;
-//   2. the new row k_new[i][g][:] / v_new[i][g][:] -> slot's row of kv head g;
-//   3. (kv head 0 only) block_tables[seq][table_pos] = new_block if one was
-//      taken, context_lens[seq] = new_len.
+// decisions); each work item is (seq, slot, table_pos, new_block, cow_src,
+// cow_ntok, new_len).  Up to 160 items travel in the kernel arguments;
+// larger batches, and the copy-on-write phase, read them from pinned host
+// memory.  One 256-thread workgroup per item:
+//   1. copy-on-write: rows [0, cow_ntok) of (cow_src, g) -> (new_block, g) for
+//      every kv head g, K and V;
+//   2. the new rows k_new[i][g][:] / v_new[i][g][:] -> the slot's row of every
+//      kv head g;
+//   3. block_tables[seq][table_pos] = new_block if one was taken,
+//      context_lens[seq] = new_len.
 // Rows are moved with 16-byte loads and stores; the copy is bit-exact.
 // The slot of token t is table[t / block_size] * block_size + t % block_size
 // ("架构解构：推理引擎的四层抽象", PagedAttention section: logical->physical block
@@ -22,51 +26,74 @@
 
 namespace pkv {
 
-template <bool COPY_PHASE>
-__global__ void __launch_bounds__(64) kv_append_kernel(AppendArgs a) {
-    const int i = blockIdx.x / a.num_kv_heads;
-    const int g = blockIdx.x % a.num_kv_heads;
-    const AppendItem it = a.items[i];
-    const int D = a.head_dim, bs = a.block_size, Hkv = a.num_kv_heads;
-    const int vec_per_row = D / 8;                 // uint4 per row
+// Copy-on-write phase: rows [0, cow_ntok) of every kv head, (cow_src, g) ->
+// (new_block, g), K and V, for the items that need it.
+__global__ void __launch_bounds__(256) kv_append_cow_kernel(AppendArgs a) {
+    __shared__ AppendItem s_it;
+    if (threadIdx.x == 0) s_it = a.items[blockIdx.x];
+    __syncthreads();
+    const AppendItem it = s_it;
+    if (it.cow_src < 0) return;
+    const int bs = a.block_size, Hkv = a.num_kv_heads, vec_per_row = a.head_dim / 8;   // uint4 per row
     uint4* kc = reinterpret_cast<uint4*>(a.k_cache);
     uint4* vc = reinterpret_cast<uint4*>(a.v_cache);
-
-    if constexpr (COPY_PHASE) {
-        if (it.cow_src >= 0) {
-            const int64_t src = ((int64_t)it.cow_src * Hkv + g) * bs * vec_per_row;
-            const int64_t dst = ((int64_t)it.new_block * Hkv + g) * bs * vec_per_row;
-            for (int x = threadIdx.x; x < it.cow_ntok * vec_per_row; x += 64) {
-                kc[dst + x] = kc[src + x];
-                vc[dst + x] = vc[src + x];
-            }
-        }
-        return;
-    }
-    const int blk = it.slot / bs, off = it.slot % bs;
-    const int64_t row = (((int64_t)blk * Hkv + g) * bs + off) * vec_per_row;
-    const int64_t srow = ((int64_t)i * Hkv + g) * vec_per_row;
-    const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
-    const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
-    for (int x = threadIdx.x; x < vec_per_row; x += 64) {
-        kc[row + x] = kn[srow + x];
-        vc[row + x] = vn[srow + x];
-    }
-    if (g == 0 && threadIdx.x == 0) {
-        if (it.new_block >= 0) a.block_tables[(int64_t)it.seq * a.table_stride + it.tpos] = it.new_block;
-        a.context_lens[it.seq] = it.new_len;
+    const int per_head = it.cow_ntok * vec_per_row;
+    for (int x = threadIdx.x; x < Hkv * per_head; x += blockDim.x) {
+        const int g = x / per_head, r = x % per_head;
+        const int64_t src = ((int64_t)it.cow_src * Hkv + g) * bs * vec_per_row + r;
+        const int64_t dst = ((int64_t)it.new_block * Hkv + g) * bs * vec_per_row + r;
+        kc[dst] = kc[src];
+        vc[dst] = vc[src];
     }
 }
 
-hipError_t launch_append(const AppendArgs& a, bool any_copy, hipStream_t stream) {
+// Write phase: one 256-thread workgroup per item moves 16-byte pieces of the
+// new K/V row of every kv head into the slot, then updates the tables.
+__device__ __forceinline__ void append_item(const AppendArgs& a, int i, int seq, int slot, int new_block,
+                                            int new_len) {
+    const int bs = a.block_size, Hkv = a.num_kv_heads, vec_per_row = a.head_dim / 8;
+    uint4* kc = reinterpret_cast<uint4*>(a.k_cache);
+    uint4* vc = reinterpret_cast<uint4*>(a.v_cache);
+    const int blk = slot / bs, off = slot % bs;
+    const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
+    const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
+    for (int x = threadIdx.x; x < Hkv * vec_per_row; x += blockDim.x) {
+        const int g = x / vec_per_row, r = x % vec_per_row;
+        const int64_t row = (((int64_t)blk * Hkv + g) * bs + off) * vec_per_row + r;
+        const int64_t src = ((int64_t)i * Hkv + g) * vec_per_row + r;
+        kc[row] = kn[src];
+        vc[row] = vn[src];
+    }
+    if (threadIdx.x == 0) {
+        if (new_block >= 0) a.block_tables[(int64_t)seq * a.table_stride + (new_len - 1) / bs] = new_block;
+        a.context_lens[seq] = new_len;
+    }
+}
+
+__global__ void __launch_bounds__(256) kv_append_kernel_args(AppendArgs a, ArgItems items) {
+    const ArgItem it = items.it[blockIdx.x];
+    append_item(a, blockIdx.x, it.seq, it.slot, it.new_block, it.new_len);
+}
+
+__global__ void __launch_bounds__(256) kv_append_kernel_host(AppendArgs a) {
+    __shared__ AppendItem s_it;
+    if (threadIdx.x == 0) s_it = a.items[blockIdx.x];   // host memory: read once
+    __syncthreads();
+    append_item(a, blockIdx.x, s_it.seq, s_it.slot, s_it.new_block, s_it.new_len);
+}
+
+hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream) {
     if (a.n == 0) return hipSuccess;
-    const dim3 grid((unsigned)(a.n * a.num_kv_heads));
+    const dim3 grid((unsigned)a.n);
     if (any_copy) {
-        hipLaunchKernelGGL(kv_append_kernel<true>, grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(kv_append_cow_kernel, grid, dim3(256), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kv_append_kernel<false>, grid, dim3(64), 0, stream, a);
+    if (inl && a.n <= kArgItems)
+        hipLaunchKernelGGL(kv_append_kernel_args, grid, dim3(256), 0, stream, a, *inl);
+    else
+        hipLaunchKernelGGL(kv_append_kernel_host, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

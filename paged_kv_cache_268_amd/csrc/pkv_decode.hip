@@ -40,6 +40,8 @@
 
 #include "pkv_kernels.h"
 
+
+
 namespace pkv {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -242,7 +244,9 @@ paged_decode_split_kernel(DecodeArgs a) {
 
     // One segment: tiles [j0, j1) of kv head g of sequence s.
     auto run_segment = [&](int s, int g, int j0, int j1, int slot, bool direct) {
-        const int ctx = min(max(a.context_lens[s], 0), a.max_context_len);
+        // Tokens this segment owns end here: at the context end or at the
+        // segment's last tile, whichever is first.
+        const int ctx = min(min(max(a.context_lens[s], 0), a.max_context_len), j1 * kTile);
         const int h0 = g * G;
         MfmaIn qb[KS];
 #pragma unroll
@@ -366,25 +370,37 @@ paged_decode_split_kernel(DecodeArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         };
 
-        // One K and one V register buffer, refilled a phase ahead: K of the
-        // next tile is requested as soon as QK has consumed the current one,
-        // V of the next tile as soon as PV has.  Block ids come 64 tiles at a
-        // time, one per lane, and are read back with v_readlane.
-        for (int c0 = j0; c0 < j1; c0 += 64) {
-            const int cn = min(64, j1 - c0);
-            const int32_t blocks = lane < cn ? table[((c0 + lane) * kTile) / BS] : 0;
-            uint4 kb[KS], vb[NI];
-            load_k(c0, __builtin_amdgcn_readlane(blocks, 0), kb);
-            load_v(c0, __builtin_amdgcn_readlane(blocks, 0), vb);
-            for (int it = 0; it + 1 < cn; ++it) {
-                const int32_t nb = __builtin_amdgcn_readlane(blocks, it + 1);
-                qk_softmax(c0 + it, kb);
-                load_k(c0 + it + 1, nb, kb);
-                pv(c0 + it, vb);
-                load_v(c0 + it + 1, nb, vb);
+        // Two K and two V register buffers: the loads of tile j + 2 are issued
+        // as soon as tile j's K (after QK) or V (after PV) is consumed, so two
+        // tiles stay in flight per wave.  Loads past the window's last tile
+        // re-read that tile (in bounds, served by the cache); a window with an
+        // odd tile count ends with one tile past the segment, which every row
+        // treats as outside the context (weight 0, V never used).  Block ids
+        // come 128 tiles at a time, two per lane, read back with v_readlane.
+        for (int c0 = j0; c0 < j1; c0 += 128) {
+            const int cn = min(128, j1 - c0);
+            const int32_t blo = lane < cn ? table[((c0 + lane) * kTile) / BS] : 0;
+            const int32_t bhi = lane + 64 < cn ? table[((c0 + 64 + lane) * kTile) / BS] : 0;
+            auto blk = [&](int it) {
+                const int i = min(it, cn - 1);
+                return i < 64 ? __builtin_amdgcn_readlane(blo, i) : __builtin_amdgcn_readlane(bhi, i - 64);
+            };
+            auto tile = [&](int it) { return c0 + min(it, cn - 1); };
+            uint4 ka[KS], va[NI], kb2[KS], vb2[NI];
+            load_k(tile(0), blk(0), ka);
+            load_v(tile(0), blk(0), va);
+            load_k(tile(1), blk(1), kb2);
+            load_v(tile(1), blk(1), vb2);
+            for (int it = 0; it < cn; it += 2) {
+                qk_softmax(c0 + it, ka);
+                load_k(tile(it + 2), blk(it + 2), ka);
+                pv(c0 + it, va);
+                load_v(tile(it + 2), blk(it + 2), va);
+                qk_softmax(c0 + it + 1, kb2);
+                load_k(tile(it + 3), blk(it + 3), kb2);
+                pv(c0 + it + 1, vb2);
+                load_v(tile(it + 3), blk(it + 3), vb2);
             }
-            qk_softmax(c0 + cn - 1, kb);
-            pv(c0 + cn - 1, vb);
         }
 
         // ---- segment totals: l per head (score layout), acc over row-groups ----
@@ -421,7 +437,7 @@ paged_decode_split_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- this wave's chunks ----
+    // ---- this wave's chunks: w, w + NW, w + 2 NW, ... ----
     const int w_global = lwg * kWaves + wave;
     for (int ch = w_global; ch < NC; ch += a.num_waves) {
         const int lo = ch * C, hi = min(lo + C, T);
@@ -444,7 +460,7 @@ paged_decode_split_kernel(DecodeArgs a) {
             const int j1 = min(seg_hi - s_pre[s] - g * pt, nt);
             if (j0 < j1) {
                 const int first = s_pre[s] + g * pt;
-                run_segment(s, g, j0, j1, ch - first / C, j0 == 0 && j1 == nt && (first + nt - 1) / C == first / C);
+                run_segment(s, g, j0, j1, ch - first / C, (first + nt - 1) / C == first / C);
             }
             t = seg_hi;
         }

@@ -374,7 +374,12 @@ int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new,
     a.head_dim = p->d.head_dim;
     a.block_size = p->d.block_size;
     a.table_stride = p->d.max_blocks_per_seq;
-    hipError_t e = pkv::launch_append(a, any_copy, (hipStream_t)stream);
+    pkv::ArgItems inl;
+    const bool small = n <= pkv::kArgItems;
+    if (small)
+        for (int32_t i = 0; i < n; ++i)
+            inl.it[i] = {slot.host[i].seq, slot.host[i].slot, slot.host[i].new_block, slot.host[i].new_len};
+    hipError_t e = pkv::launch_append(a, any_copy, small ? &inl : nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "kv_append launch (pool state now ahead of the device)");
     e = hipEventRecord(slot.ev, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord");

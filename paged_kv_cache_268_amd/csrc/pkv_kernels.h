@@ -57,6 +57,16 @@ struct AppendItem {
     int32_t seq, slot, tpos, new_block, cow_src, cow_ntok, new_len;
 };
 
+// Items small enough to travel in the kernel arguments (no host-memory read
+// on the device): 16 bytes each, up to kArgItems of them.
+struct ArgItem {
+    int32_t seq, slot, new_block, new_len;     // table_pos = (new_len - 1) / block_size
+};
+constexpr int kArgItems = 160;
+struct ArgItems {
+    ArgItem it[kArgItems];
+};
+
 struct AppendArgs {
     const AppendItem* items;     // device-readable (pinned host) [n]
     const void* k_new;           // [n][Hkv][D]
@@ -77,6 +87,8 @@ hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int g
 // Resident waves per CU of the split kernel instance (occupancy query).
 hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, bool bf16, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_append(const AppendArgs& a, bool any_copy, hipStream_t stream);
+// items_in_args: a.n <= kArgItems and `inl` holds the items (copy-on-write
+// still reads a.items, in the separate copy launch).
+hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream);
 
 }  // namespace pkv

@@ -178,9 +178,10 @@ def workspace_views(desc: AttnDesc, ws):
 
 
 def alloc_workspace(desc: AttnDesc, device):
+    """A workspace for `desc` (zero-filled; the library needs no particular contents)."""
     import torch
     n = workspace_bytes(desc)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, *,

@@ -161,3 +161,32 @@ def test_append_same_call_cow_and_tail_write():
     torch.cuda.synchronize()
     assert np.array_equal(W.bits16(k), mirror.k) and np.array_equal(W.bits16(v), mirror.v)
     pool.close()
+
+
+def test_append_large_batch():
+    """More sequences than fit in the kernel arguments: items read from pinned host memory."""
+    NB, Hkv, D, bs, S = 900, 2, 64, 16, 200
+    note("append, 200 sequences in one call")
+    order = np.random.default_rng(3).permutation(NB).astype(np.int32)
+    k = torch.empty((NB, Hkv, bs, D), dtype=torch.bfloat16, device=DEV); W.fill_normal_(k, 5)
+    v = torch.empty_like(k); W.fill_normal_(v, 6)
+    tab = torch.full((S, 4), -1, dtype=torch.int32, device=DEV)
+    lens = torch.zeros(S, dtype=torch.int32, device=DEV)
+    pool = pkv.BlockPool(NB, bs, Hkv, D, pkv.PKV_BF16, S, 4, k_cache=k, v_cache=v, alloc_order=order)
+    ref = R.PoolReplay(NB, bs, S, 4, alloc_order=order)
+    mirror = Mirror(k, v)
+    ids = [pool.add() for _ in range(S)]
+    assert ids == [ref.add_seq() for _ in range(S)]
+    pool.write_tables(tab, lens)
+    for r in range(20):
+        kn = torch.empty((S, Hkv, D), dtype=torch.bfloat16, device=DEV); W.fill_normal_(kn, 100 + r)
+        vn = torch.empty_like(kn); W.fill_normal_(vn, 200 + r)
+        items = ref.append(ids)
+        pool.append(ids, kn, vn, tab, lens)
+        mirror.apply(items, kn, vn, bs)
+    torch.cuda.synchronize()
+    want_tab, want_len = ref.tables(4)
+    assert lens.cpu().tolist() == want_len
+    assert tab.cpu().numpy().tolist() == want_tab
+    assert np.array_equal(W.bits16(k), mirror.k) and np.array_equal(W.bits16(v), mirror.v)
+    pool.close()

@@ -235,12 +235,13 @@ def test_segments_are_the_plan(P, nw):
     tab, ctx = to_dev(wl)
     desc = pkv.desc_for(q, k, tab, wl.max_context_len, P, num_waves=nw)
     ws = pkv.alloc_workspace(desc, DEV)
-    ws.fill_(255)                                              # NaN pattern in every float
+    hdr, seg_out, seg_lse = pkv.workspace_views(desc, ws)
+    seg_out.fill_(float("nan"))                                # unwritten segment slots stay NaN
+    seg_lse.fill_(float("nan"))
     out = torch.zeros(q.shape, device=DEV)
     lse = torch.zeros(q.shape[:2], device=DEV)
     pkv.decode_partials(desc, q, k, v, tab, ctx, wl.scale, out, lse, ws)
     torch.cuda.synchronize()
-    _, seg_out, seg_lse = pkv.workspace_views(desc, ws)
     seg_out, seg_lse = seg_out.cpu().numpy(), seg_lse.cpu().numpy()
     items = pkv.plan(desc, wl.context_lens)
     want = np.array(R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc)), dtype=np.int32)

@@ -136,7 +136,7 @@ def test_plan_balanced_worked_example():
     # Many waves: the chunk never drops below 8 tiles (128 tokens).
     items = R.plan([40, 200], num_kv_heads=1, partition_size=0, num_waves=1000)
     assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200)]
-    # One wave: everything in one chunk, every (seq, head) whole.
+    # One wave: C = max(8, 34) = 34 tiles, everything in one chunk, every (seq, head) whole.
     items = R.plan([40, 200, 0, 7], num_kv_heads=2, partition_size=0, num_waves=1)
     assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 200), (1, 1, 0, 0, 200),
                      (3, 0, 0, 0, 7), (3, 1, 0, 0, 7)]
