@@ -10,12 +10,15 @@
 // score ever reaches HBM ("架构解构：推理引擎的四层抽象", FlashAttention
 // integration section).
 //
-// Work decomposition.  One 256-thread workgroup (4 wave64) per work item
-// (sequence s, kv head g, partition p).  A partition is P consecutive tokens
-// [p*P, min((p+1)*P, len)); it is cut into 16-token tiles (a tile never
-// crosses a block because block_size is 16 or 32 and P a multiple of it), and
-// wave w takes tiles w, w+4, w+8, ...  A 16-token tile of one (block, kv head)
-// is 16*D*2 bytes contiguous.
+// Work decomposition.  A persistent grid of 256-thread workgroups (4 wave64),
+// as many as fit the device at once.  Every (sequence s, kv head g, 16-token
+// tile j) is one entry of a flattened, sequence-major list; the list is cut
+// into chunks of C tiles and wave w of the NW waves takes chunks w, w + NW,
+// ...  With C = ceil(T / NW) (balanced mode) every wave gets the same number
+// of tiles whatever the context lengths; with C = P / 16 and each (s, g)
+// padded to whole chunks (fixed mode) a chunk is one partition of P tokens.
+// A 16-token tile of one (block, kv head) is 16*D*2 bytes contiguous and
+// never crosses a block (block_size is 16 or 32).
 //
 // QK on the matrix core.  The G q heads of the kv group form the B operand of
 // v_mfma_f32_16x16x32 (32 d x 16 heads, heads >= G zero) and stay in
@@ -31,10 +34,10 @@
 // PV on the vector ALUs: V rows are loaded so that LPR = D/8 lanes share a
 // row (16 bytes each) and a wave load instruction reads 1 KiB contiguous; the
 // tile's weights reach these lanes through a 1 KiB per-wave LDS slot.
-// End of a work item: the row-groups' partial sums add up (shared reference),
-// the 4 waves merge through LDS, and the result is either the final output (a
-// one-partition sequence) or a normalised partial plus its log2-domain lse in
-// the workspace for the merge kernel.
+// End of a segment (the part of a chunk inside one (s, g)): the row-groups'
+// partial sums add up (shared reference) and the result is either the final
+// output (the segment covers all of (s, g)) or a normalised partial plus its
+// log2-domain lse in the workspace for the merge kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
