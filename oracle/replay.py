@@ -24,6 +24,17 @@ What is replayed, from the definitions:
   * freeing a sequence drops one reference from each of its blocks in logical
     order; a block whose count reaches zero is pushed back onto the free list,
     so the next allocation reuses the last block released;
+  * the host tier ("LLM+Agent 全栈推理底座" 4.2, TieredBlockManager): a sequence
+    keeps its last gpu_window blocks on the GPU; the blocks before them (the
+    listing's blocks[:-gpu_window], taken only when the sequence holds more than
+    gpu_window blocks) are cold and move to a pool of pinned host blocks; when
+    the sequence is needed again they are copied back ("DMA back").  Host blocks
+    come from their own LIFO free list (first handed out: 0, 1, 2, ...).  Moving
+    a block gives the moving sequence a private copy in the other tier; the old
+    block loses one reference and is freed at zero, so a block still shared by
+    another holder stays where it is.  In a block list a host block c is written
+    -2 - c.  A sequence holding host blocks is parked: it cannot be appended to
+    and it publishes length 0 (table row all -1) until it is restored;
   * the decode split: every (sequence s, kv head g, 16-token tile j) in one
     sequence-major list -- (s, g)'s tiles start at first(s, g) =
     Hkv * sum_{s'<s} pt_s' + g * pt_s -- cut into chunks of C tiles.  With a
@@ -74,6 +85,92 @@ class PoolReplay:
         self.free: List[int] = list(reversed(order))       # pop() yields order[0] first
         self.ref = [0] * num_blocks
         self.seqs: Dict[int, Tuple[List[int], int]] = {}
+        self.num_host_blocks = 0
+        self.host_free: List[int] = []
+        self.host_ref: List[int] = []
+
+    # -- host tier ---------------------------------------------------------
+    def attach_host_tier(self, num_host_blocks: int) -> None:
+        if num_host_blocks < 1 or self.num_host_blocks:
+            raise PoolError("EINVAL", "bad or repeated host tier")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = list(reversed(range(num_host_blocks)))
+        self.host_ref = [0] * num_host_blocks
+
+    @staticmethod
+    def is_host(entry: int) -> bool:
+        return entry <= -2
+
+    @staticmethod
+    def host_id(entry: int) -> int:
+        return -2 - entry
+
+    def parked(self, sid: int) -> bool:
+        return any(e <= -2 for e in self.seqs[sid][0])
+
+    def _unref(self, entry: int) -> None:
+        if entry <= -2:
+            c = -2 - entry
+            self.host_ref[c] -= 1
+            if self.host_ref[c] == 0:
+                self.host_free.append(c)
+        else:
+            self.ref[entry] -= 1
+            if self.ref[entry] == 0:
+                self.free.append(entry)
+
+    def _check_ids(self, ids: Sequence[int]) -> List[int]:
+        ids = [int(s) for s in ids]
+        if len(set(ids)) != len(ids):
+            raise PoolError("EINVAL", "duplicate sequence id")
+        for s in ids:
+            if s not in self.seqs:
+                raise PoolError("EINVAL", "unknown sequence")
+        return ids
+
+    def offload(self, seq_ids: Sequence[int], gpu_window: int) -> List[Tuple[int, int]]:
+        """Move each sequence's cold GPU blocks to the host tier; the (gpu, host) copies in order."""
+        if not self.num_host_blocks:
+            raise PoolError("EINVAL", "no host tier")
+        if gpu_window < 1:
+            raise PoolError("EINVAL", "gpu_window must be >= 1")
+        ids = self._check_ids(seq_ids)
+        cold = {s: self.seqs[s][0][:-gpu_window] if len(self.seqs[s][0]) > gpu_window else [] for s in ids}
+        need = sum(1 for s in ids for e in cold[s] if e >= 0)
+        if need > len(self.host_free):
+            raise PoolError("ENOMEM", "host tier exhausted")
+        copies = []
+        for s in ids:
+            blocks, _ = self.seqs[s]
+            for i in range(len(cold[s])):
+                b = blocks[i]
+                if b < 0:
+                    continue
+                c = self.host_free.pop()
+                self.host_ref[c] = 1
+                copies.append((b, c))
+                blocks[i] = -2 - c
+                self._unref(b)
+        return copies
+
+    def restore(self, seq_ids: Sequence[int]) -> List[Tuple[int, int]]:
+        """Copy each sequence's host blocks back into fresh GPU blocks; the (host, gpu) copies in order."""
+        ids = self._check_ids(seq_ids)
+        need = sum(1 for s in ids for e in self.seqs[s][0] if e <= -2)
+        if need > len(self.free):
+            raise PoolError("ENOMEM", "pool exhausted")
+        copies = []
+        for s in ids:
+            blocks, _ = self.seqs[s]
+            for i, e in enumerate(blocks):
+                if e > -2:
+                    continue
+                b = self.free.pop()
+                self.ref[b] = 1
+                copies.append((-2 - e, b))
+                blocks[i] = b
+                self._unref(e)
+        return copies
 
     # -- sequences -------------------------------------------------------
     def _new_id(self) -> int:
@@ -110,7 +207,10 @@ class PoolReplay:
         sid = self._new_id()
         blocks, length = self.seqs[src]
         for b in blocks:
-            self.ref[b] += 1
+            if b <= -2:
+                self.host_ref[-2 - b] += 1
+            else:
+                self.ref[b] += 1
         self.seqs[sid] = (list(blocks), length)
         return sid
 
@@ -119,9 +219,7 @@ class PoolReplay:
             raise PoolError("EINVAL", "unknown sequence")
         blocks, _ = self.seqs.pop(sid)
         for b in blocks:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+            self._unref(b)
 
     # -- append one token to each listed sequence (all-or-nothing) --------
     def append(self, seq_ids: Sequence[int]) -> List[AppendItem]:
@@ -132,6 +230,8 @@ class PoolReplay:
         for s in ids:
             if s not in self.seqs:
                 raise PoolError("EINVAL", "unknown sequence")
+            if self.parked(s):
+                raise PoolError("EINVAL", "sequence has blocks in the host tier")
             blocks, t = self.seqs[s]
             if t % self.bs == 0:
                 if t // self.bs >= self.max_blocks_per_seq:
@@ -168,12 +268,17 @@ class PoolReplay:
         tab = [[-1] * w for _ in range(self.max_seqs)]
         lens = [0] * self.max_seqs
         for s, (blocks, length) in self.seqs.items():
+            if self.parked(s):
+                continue
             tab[s][:len(blocks)] = blocks
             lens[s] = length
         return tab, lens
 
     def num_free(self) -> int:
         return len(self.free)
+
+    def num_host_free(self) -> int:
+        return len(self.host_free)
 
 
 TILE = 16

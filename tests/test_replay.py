@@ -140,3 +140,137 @@ def test_plan_balanced_worked_example():
     items = R.plan([40, 200, 0, 7], num_kv_heads=2, partition_size=0, num_waves=1)
     assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 200), (1, 1, 0, 0, 200),
                      (3, 0, 0, 0, 7), (3, 1, 0, 0, 7)]
+
+
+# ---------------------------------------------------------------- host tier
+
+GOLDEN_TIER = os.path.join(os.path.dirname(__file__), "golden", "tiered_evict_to_cpu.json")
+
+
+def _seq_with_blocks(pool, blocks, bs):
+    return pool.import_seq(blocks, len(blocks) * bs)
+
+
+def test_golden_tiered_evict_to_cpu():
+    g = json.load(open(GOLDEN_TIER))
+    for case in g["cases"]:
+        pool = R.PoolReplay(16, 4, max_seqs=2, max_blocks_per_seq=8)
+        pool.attach_host_tier(8)
+        sid = _seq_with_blocks(pool, g["blocks"], 4)
+        copies = pool.offload([sid], case["gpu_window"])
+        assert [b for b, _ in copies] == case["cold"]
+        # host blocks come out 0, 1, 2, ... and replace the cold entries in place
+        assert [c for _, c in copies] == list(range(len(case["cold"])))
+        blocks = pool.seqs[sid][0]
+        assert blocks[len(case["cold"]):] == case["kept"]
+        assert [R.PoolReplay.host_id(e) for e in blocks[:len(case["cold"])]] == list(range(len(case["cold"])))
+        # cold GPU blocks went back to the free list in logical order (last one on top)
+        if case["cold"]:
+            assert pool.free[-len(case["cold"]):] == case["cold"]
+    # the listing's gpu_window = 0 slice moves nothing; the replay refuses the case instead
+    assert g["blocks"][:-0] == g["listing_quirk"]["listing_cold"]
+    pool = R.PoolReplay(16, 4, max_seqs=2, max_blocks_per_seq=8)
+    pool.attach_host_tier(8)
+    sid = _seq_with_blocks(pool, g["blocks"], 4)
+    with pytest.raises(R.PoolError):
+        pool.offload([sid], 0)
+
+
+def test_offload_restore_round_trip_and_parking():
+    pool = R.PoolReplay(12, 4, max_seqs=4, max_blocks_per_seq=8, alloc_order=list(range(11, -1, -1)))
+    pool.attach_host_tier(6)
+    a = pool.add_seq()
+    for _ in range(18):                      # 5 blocks: 11, 10, 9, 8, 7
+        pool.append([a])
+    b = pool.add_seq()
+    for _ in range(5):                       # 2 blocks: 6, 5
+        pool.append([b])
+    assert pool.seqs[a][0] == [11, 10, 9, 8, 7]
+    copies = pool.offload([a, b], 2)
+    assert copies == [(11, 0), (10, 1), (9, 2)]
+    assert pool.seqs[a][0] == [-2, -3, -4, 8, 7] and pool.parked(a) and not pool.parked(b)
+    tab, lens = pool.tables()
+    assert lens[a] == 0 and tab[a] == [-1] * 8 and lens[b] == 5
+    with pytest.raises(R.PoolError):
+        pool.append([a])
+    assert pool.num_host_free() == 3
+    back = pool.restore([a, b])
+    # free list top was 9 (freed last), then 10, 11
+    assert back == [(0, 9), (1, 10), (2, 11)]
+    assert pool.seqs[a][0] == [9, 10, 11, 8, 7] and not pool.parked(a)
+    assert pool.num_host_free() == 6 and pool.host_free[-3:] == [0, 1, 2]
+    assert pool.append([a])[0][1] == 7 * 4 + 2      # slot in the tail block, offset 2
+
+
+def test_offload_all_or_nothing():
+    pool = R.PoolReplay(16, 4, max_seqs=4, max_blocks_per_seq=8)
+    pool.attach_host_tier(3)
+    a = _seq_with_blocks(pool, [0, 1, 2, 3], 4)
+    b = _seq_with_blocks(pool, [4, 5, 6], 4)
+    snap = (list(pool.free), list(pool.host_free), [list(x[0]) for x in pool.seqs.values()])
+    with pytest.raises(R.PoolError):
+        pool.offload([a, b], 1)              # needs 3 + 2 host blocks, 3 free
+    assert snap == (list(pool.free), list(pool.host_free), [list(x[0]) for x in pool.seqs.values()])
+    with pytest.raises(R.PoolError):
+        pool.offload([a, a], 1)
+    pool.offload([a], 1)
+    full = R.PoolReplay(4, 4, max_seqs=2, max_blocks_per_seq=4)
+    full.attach_host_tier(4)
+    s = _seq_with_blocks(full, [0, 1, 2], 4)
+    full.offload([s], 1)
+    t = _seq_with_blocks(full, [0, 1, 3], 4)
+    with pytest.raises(R.PoolError):
+        full.restore([s])                    # 2 host blocks back, 0 GPU blocks free
+    assert full.seqs[s][0] == [-2, -3, 2]
+
+
+def test_offload_shared_block_copies_for_the_mover_only():
+    pool = R.PoolReplay(16, 4, max_seqs=4, max_blocks_per_seq=8)
+    pool.attach_host_tier(8)
+    a = _seq_with_blocks(pool, [3, 4, 5], 4)
+    b = pool.fork(a)
+    copies = pool.offload([a], 1)
+    assert copies == [(3, 0), (4, 1)]
+    assert pool.ref[3] == 1 and pool.ref[4] == 1 and pool.seqs[b][0] == [3, 4, 5]
+    assert 3 not in pool.free
+    c = pool.fork(a)                          # a parked sequence forks with its host blocks
+    assert pool.host_ref[0] == 2
+    pool.free_seq(a)
+    assert pool.host_ref[0] == 1 and 0 not in pool.host_free
+    pool.free_seq(c)
+    assert pool.host_free[-2:] == [0, 1]
+
+
+def test_random_tier_ops_conserve_blocks():
+    rnd = random.Random(1)
+    pool = R.PoolReplay(48, 4, max_seqs=8, max_blocks_per_seq=12)
+    pool.attach_host_tier(24)
+    live = []
+    for _ in range(3000):
+        op = rnd.random()
+        try:
+            if op < 0.08 and len(live) < 8:
+                live.append(pool.add_seq())
+            elif op < 0.12 and live and len(live) < 8:
+                live.append(pool.fork(rnd.choice(live)))
+            elif op < 0.17 and live:
+                s = rnd.choice(live); live.remove(s); pool.free_seq(s)
+            elif op < 0.27 and live:
+                pool.offload(rnd.sample(live, rnd.randint(1, len(live))), rnd.randint(1, 4))
+            elif op < 0.37 and live:
+                pool.restore(rnd.sample(live, rnd.randint(1, len(live))))
+            elif live:
+                pool.append(rnd.sample(live, rnd.randint(1, len(live))))
+        except R.PoolError:
+            pass
+        held, hheld = {}, {}
+        for blocks, n in pool.seqs.values():
+            assert len(blocks) == R.blocks_needed(n, 4)
+            for e in blocks:
+                d = hheld if e <= -2 else held
+                k = -2 - e if e <= -2 else e
+                d[k] = d.get(k, 0) + 1
+        assert all(pool.ref[b] == c for b, c in held.items())
+        assert all(pool.host_ref[b] == c for b, c in hheld.items())
+        assert len(held) + len(pool.free) == 48 and not set(held) & set(pool.free)
+        assert len(hheld) + len(pool.host_free) == 24 and not set(hheld) & set(pool.host_free)
