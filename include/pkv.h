@@ -114,7 +114,8 @@ int kv_seq_fork(pkv_pool* pool, int32_t src_seq, int32_t* seq_id_out);
  * reuses the last one released).  Host only. */
 int kv_seq_free(pkv_pool* pool, int32_t seq_id);
 
-/* Host view of one sequence: its length and up to `cap` block ids. */
+/* Host view of one sequence: its length and up to `cap` block-list entries
+ * (a GPU block id b >= 0, or -2 - c for host-tier block c). */
 int kv_seq_info(const pkv_pool* pool, int32_t seq_id, int32_t* len_out,
                 int32_t* block_ids_out, int32_t cap, int32_t* n_blocks_out);
 
@@ -150,9 +151,56 @@ int kv_append(pkv_pool* pool, int32_t n, const int32_t* seq_ids,
               int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream);
 
 /* Publish the whole host view to the device tables (-1 past each length,
- * length 0 for free rows), ordered on `stream`. */
+ * length 0 for free rows and for sequences parked in the host tier), ordered
+ * on `stream`. */
 int kv_write_tables(pkv_pool* pool, int32_t* block_tables, int32_t* context_lens,
                     pkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Host tier ("LLM+Agent 全栈推理底座" 4.2, TieredBlockManager: a sequence keeps
+ * its most recent gpu_window blocks in GPU memory; the colder blocks before
+ * them move to pinned host memory and are copied back when the sequence is
+ * needed again).
+ *
+ * Host layout (caller-allocated pinned memory, e.g. hipHostMalloc; the pool
+ * borrows it until destroyed):
+ *   k_host, v_host : [num_host_blocks][num_kv_heads][block_size][head_dim] of kv_dtype
+ * Host blocks come from their own free list, handed out 0, 1, 2, ... and
+ * reused last-released-first.  Moving a block gives the moving sequence a
+ * private copy in the other tier; the old block loses one reference and is
+ * freed when none are left, so a block another sequence still holds stays
+ * where it is.  A sequence holding any host block is parked: kv_append and
+ * kv_reserve reject it (PKV_EINVAL) and kv_write_tables publishes it with
+ * length 0 until kv_seq_restore brings it back.  Block moves are one batched
+ * copy kernel per call on `stream` (GPU loads / stores across the host link);
+ * later work that reuses a freed block, or reads the host buffers from the
+ * CPU, must be ordered after it (same stream or synchronised).
+ * ------------------------------------------------------------------------ */
+
+/* Give the pool a host tier of num_host_blocks blocks.  k_host / v_host must
+ * be pinned, device-mapped host memory (PKV_EINVAL otherwise), 16-byte
+ * aligned, of the layout above.  Once per pool. */
+int kv_block_pool_attach_host_tier(pkv_pool* pool, int32_t num_host_blocks, void* k_host,
+                                   void* v_host);
+
+/* For each of the n listed sequences (host array, no repeats) holding more
+ * than gpu_window blocks (gpu_window >= 1), move every GPU block before its
+ * last gpu_window blocks to a new host block, in sequence order then logical
+ * order.  All or nothing: PKV_ENOMEM if the host tier has too few free
+ * blocks, PKV_EINVAL for a bad id or window; nothing changes then. */
+int kv_seq_offload(pkv_pool* pool, int32_t n, const int32_t* seq_ids, int32_t gpu_window,
+                   pkv_stream_t stream);
+
+/* Copy every host block of the n listed sequences back into new GPU blocks
+ * (taken from the GPU free list in sequence order, then logical order) and
+ * un-park them.  All or nothing: PKV_ENOMEM if the GPU pool has too few free
+ * blocks.  Host bookkeeping only changes the device tables through a later
+ * kv_write_tables(). */
+int kv_seq_restore(pkv_pool* pool, int32_t n, const int32_t* seq_ids, pkv_stream_t stream);
+
+/* Free host blocks, and the reference count of host block `block` (< 0: skip). */
+int kv_host_tier_stats(const pkv_pool* pool, int32_t* num_free_out, int32_t block,
+                       int32_t* refcount_out);
 
 /* Debug: check host copies of device tables (block_tables [n_seqs][table_stride],
  * context_lens [n_seqs]): every entry a context reaches is in [0, num_blocks)

@@ -8,6 +8,9 @@
 // ("架构解构：推理引擎的四层抽象", PagedAttention section and runtime layer).
 // Shared blocks (prefix reuse, "LLM+Agent 全栈推理底座" 2.2 / 4.4) carry a
 // reference count and are copied before a write (copy-on-write).
+// The host tier ("LLM+Agent 全栈推理底座" 4.2, TieredBlockManager) keeps a
+// sequence's last gpu_window blocks on the GPU and moves the ones before them
+// to caller-owned pinned host memory, copied back when the sequence is needed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -19,6 +22,7 @@
 
 #include "pkv.h"
 #include "pkv_kernels.h"
+#include "pkv_tier.h"
 
 namespace {
 
@@ -43,6 +47,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kRing = 8;   // pinned staging slots for kv_append metadata
+constexpr int kCopyRing = 4;   // pinned staging slots for host-tier block moves
+
+// A block list entry: a GPU block id b >= 0, or host block c written -2 - c.
+inline bool is_host(int32_t e) { return e <= -2; }
+inline int32_t host_id(int32_t e) { return -2 - e; }
+inline int32_t host_entry(int32_t c) { return -2 - c; }
 
 }  // namespace
 
@@ -76,6 +86,23 @@ struct pkv_pool {
     int32_t* tab_host = nullptr;                 // staging for kv_write_tables
     hipEvent_t tab_ev = nullptr;
     bool tab_pending = false;
+
+    // Host tier: caller-owned pinned buffers, their device-mapped addresses,
+    // a LIFO free list of host blocks and a reference count per host block.
+    int32_t num_host = 0;
+    void* k_host_dev = nullptr;
+    void* v_host_dev = nullptr;
+    std::vector<int32_t> host_stack;
+    std::vector<int32_t> host_ref;
+    std::vector<int32_t> nhost;                  // host blocks held, per sequence row (> 0: parked)
+    struct CopySlot {
+        int32_t* pairs = nullptr;                // pinned, device-readable [cap][2]
+        int64_t cap = 0;
+        hipEvent_t ev = nullptr;
+        bool pending = false;
+    };
+    CopySlot copy_ring[kCopyRing];
+    int copy_next = 0;
 
     int32_t pop_free() {
         while (!stack.empty() && stack.back() < 0) stack.pop_back();
@@ -112,6 +139,20 @@ struct pkv_pool {
         return -1;
     }
     bool valid_seq(int32_t s) const { return s >= 0 && s < d.max_seqs && live[s]; }
+
+    // Drop one holder of a block-list entry; a block with none left is freed in its tier.
+    void unref(int32_t e) {
+        if (is_host(e)) {
+            const int32_t c = host_id(e);
+            if (--host_ref[c] == 0) host_stack.push_back(c);
+        } else if (--ref[e] == 0) {
+            push_free(e);
+        }
+    }
+    void addref(int32_t e) {
+        if (is_host(e)) ++host_ref[host_id(e)];
+        else ++ref[e];
+    }
 };
 
 extern "C" {
@@ -163,6 +204,7 @@ int kv_block_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cache
     p->blocks.assign(d.max_seqs, {});
     p->len.assign(d.max_seqs, 0);
     p->live.assign(d.max_seqs, 0);
+    p->nhost.assign(d.max_seqs, 0);
     *out = p;
     return PKV_OK;
 }
@@ -173,6 +215,11 @@ void kv_block_pool_destroy(pkv_pool* p) {
         if (s.pending) (void)hipEventSynchronize(s.ev);
         if (s.ev) (void)hipEventDestroy(s.ev);
         if (s.host) (void)hipHostFree(s.host);
+    }
+    for (auto& c : p->copy_ring) {
+        if (c.pending) (void)hipEventSynchronize(c.ev);
+        if (c.ev) (void)hipEventDestroy(c.ev);
+        if (c.pairs) (void)hipHostFree(c.pairs);
     }
     if (p->tab_pending) (void)hipEventSynchronize(p->tab_ev);
     if (p->tab_ev) (void)hipEventDestroy(p->tab_ev);
@@ -187,6 +234,7 @@ int kv_seq_add(pkv_pool* p, int32_t* seq_id_out) {
     p->live[s] = 1;
     p->blocks[s].clear();
     p->len[s] = 0;
+    p->nhost[s] = 0;
     ++p->num_live;
     *seq_id_out = s;
     return PKV_OK;
@@ -218,6 +266,7 @@ int kv_seq_import(pkv_pool* p, int32_t len, const int32_t* block_ids, int32_t n_
     p->live[s] = 1;
     p->blocks[s] = ids;
     p->len[s] = len;
+    p->nhost[s] = 0;
     ++p->num_live;
     *seq_id_out = s;
     return PKV_OK;
@@ -228,10 +277,11 @@ int kv_seq_fork(pkv_pool* p, int32_t src, int32_t* seq_id_out) {
     if (!p->valid_seq(src)) return fail(PKV_EINVAL, "kv_seq_fork: unknown sequence %d", src);
     const int32_t s = p->new_row();
     if (s < 0) return fail(PKV_ENOMEM, "kv_seq_fork: all %d sequence rows in use", p->d.max_seqs);
-    for (int32_t b : p->blocks[src]) ++p->ref[b];
+    for (int32_t b : p->blocks[src]) p->addref(b);
     p->live[s] = 1;
     p->blocks[s] = p->blocks[src];
     p->len[s] = p->len[src];
+    p->nhost[s] = p->nhost[src];
     ++p->num_live;
     *seq_id_out = s;
     return PKV_OK;
@@ -240,10 +290,10 @@ int kv_seq_fork(pkv_pool* p, int32_t src, int32_t* seq_id_out) {
 int kv_seq_free(pkv_pool* p, int32_t s) {
     if (!p) return fail(PKV_EINVAL, "kv_seq_free: null pool");
     if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_seq_free: unknown sequence %d", s);
-    for (int32_t b : p->blocks[s])
-        if (--p->ref[b] == 0) p->push_free(b);
+    for (int32_t b : p->blocks[s]) p->unref(b);
     p->blocks[s].clear();
     p->len[s] = 0;
+    p->nhost[s] = 0;
     p->live[s] = 0;
     --p->num_live;
     return PKV_OK;
@@ -282,6 +332,7 @@ static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::App
         const int32_t s = seq_ids[i];
         if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_reserve: unknown sequence %d", s);
         if (mark[s]) return fail(PKV_EINVAL, "kv_reserve: sequence %d listed twice", s);
+        if (p->nhost[s]) return fail(PKV_EINVAL, "kv_reserve: sequence %d has blocks in the host tier (restore it first)", s);
         mark[s] = 1;
         const int32_t t = p->len[s];
         if (t % bs == 0) {
@@ -406,8 +457,9 @@ int kv_write_tables(pkv_pool* p, int32_t* block_tables, int32_t* context_lens, p
     int32_t* lens = p->tab_host + S * W;
     for (size_t s = 0; s < S; ++s) {
         const auto& b = p->blocks[s];
-        for (size_t j = 0; j < W; ++j) tab[s * W + j] = j < b.size() ? b[j] : -1;
-        lens[s] = p->len[s];
+        const bool parked = p->nhost[s] > 0;     // not attendable until restored
+        for (size_t j = 0; j < W; ++j) tab[s * W + j] = !parked && j < b.size() ? b[j] : -1;
+        lens[s] = parked ? 0 : p->len[s];
     }
     hipError_t e = hipMemcpyAsync(block_tables, tab, sizeof(int32_t) * S * W, hipMemcpyHostToDevice, (hipStream_t)stream);
     if (e == hipSuccess)
@@ -416,6 +468,192 @@ int kv_write_tables(pkv_pool* p, int32_t* block_tables, int32_t* context_lens, p
     if (e != hipSuccess) return fail_hip(e, "kv_write_tables copy");
     p->tab_pending = true;
     return PKV_OK;
+}
+
+// --------------------------------------------------------------------------
+// Host tier
+// --------------------------------------------------------------------------
+
+int kv_block_pool_attach_host_tier(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host) {
+    if (!p || !k_host || !v_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: null argument");
+    if (p->num_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: the pool already has a host tier");
+    if (num_host_blocks < 1) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: %d host blocks", num_host_blocks);
+    if (!aligned(k_host, 16) || !aligned(v_host, 16))
+        return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers must be 16-byte aligned");
+    // Only pinned host memory (hipHostMalloc) is reachable from a kernel; a
+    // pageable buffer is refused here, before any copy could touch it.
+    for (void* h : {k_host, v_host}) {
+        hipPointerAttribute_t at{};
+        const hipError_t pe = hipPointerGetAttributes(&at, h);
+        if (pe != hipSuccess || at.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers are not pinned host memory "
+                                    "(allocate them with hipHostMalloc)");
+        }
+    }
+    void* kd = nullptr;
+    void* vd = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&kd, k_host, 0);
+    if (e == hipSuccess) e = hipHostGetDevicePointer(&vd, v_host, 0);
+    if (e != hipSuccess || !kd || !vd) {
+        (void)hipGetLastError();
+        return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers are not pinned, device-mapped "
+                                "memory (allocate them with hipHostMalloc)");
+    }
+    p->num_host = num_host_blocks;
+    p->k_host_dev = kd;
+    p->v_host_dev = vd;
+    p->host_stack.resize(num_host_blocks);
+    for (int32_t i = 0; i < num_host_blocks; ++i) p->host_stack[i] = num_host_blocks - 1 - i;   // pops 0, 1, ...
+    p->host_ref.assign(num_host_blocks, 0);
+    return PKV_OK;
+}
+
+int kv_host_tier_stats(const pkv_pool* p, int32_t* num_free_out, int32_t block, int32_t* refcount_out) {
+    if (!p) return fail(PKV_EINVAL, "kv_host_tier_stats: null pool");
+    if (!p->num_host) return fail(PKV_EINVAL, "kv_host_tier_stats: the pool has no host tier");
+    if (num_free_out) *num_free_out = (int32_t)p->host_stack.size();
+    if (block >= 0) {
+        if (block >= p->num_host) return fail(PKV_EINVAL, "kv_host_tier_stats: host block %d out of range", block);
+        if (refcount_out) *refcount_out = p->host_ref[block];
+    }
+    return PKV_OK;
+}
+
+// A staging slot for n (source, destination) pairs, waiting for the slot's
+// previous launch if it is still in flight and growing it if it is too small.
+static int copy_slot(pkv_pool* p, int64_t n, pkv_pool::CopySlot** out) {
+    auto& c = p->copy_ring[p->copy_next];
+    if (!c.ev) {
+        hipError_t e = hipEventCreateWithFlags(&c.ev, hipEventDisableTiming);
+        if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags (block-move staging)");
+    }
+    if (c.pending) {
+        hipError_t e = hipEventSynchronize(c.ev);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (block-move staging)");
+        c.pending = false;
+    }
+    if (c.cap < n) {
+        if (c.pairs) (void)hipHostFree(c.pairs);
+        c.pairs = nullptr;
+        c.cap = 0;
+        const int64_t cap = std::max<int64_t>(n, 1024);
+        hipError_t e = hipHostMalloc((void**)&c.pairs, sizeof(int32_t) * 2 * (size_t)cap,
+                                     hipHostMallocCoherent | hipHostMallocMapped);
+        if (e != hipSuccess) return fail_hip(e, "hipHostMalloc (block-move staging)");
+        c.cap = cap;
+    }
+    *out = &c;
+    return PKV_OK;
+}
+
+static int check_ids(const pkv_pool* p, int32_t n, const int32_t* seq_ids, const char* who) {
+    if (n < 0 || (n > 0 && !seq_ids)) return fail(PKV_EINVAL, "%s: bad n or seq_ids", who);
+    std::vector<uint8_t> mark(p->d.max_seqs, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        if (!p->valid_seq(s)) return fail(PKV_EINVAL, "%s: unknown sequence %d", who, s);
+        if (mark[s]) return fail(PKV_EINVAL, "%s: sequence %d listed twice", who, s);
+        mark[s] = 1;
+    }
+    return PKV_OK;
+}
+
+static int launch_moves(pkv_pool* p, pkv_pool::CopySlot* c, int64_t n, bool to_host, hipStream_t stream) {
+    if (n == 0) return PKV_OK;
+    pkv::TierCopyArgs a{};
+    const void* dev_k = p->k_cache;
+    const void* dev_v = p->v_cache;
+    a.k_src = static_cast<const uint4*>(to_host ? dev_k : p->k_host_dev);
+    a.v_src = static_cast<const uint4*>(to_host ? dev_v : p->v_host_dev);
+    a.k_dst = static_cast<uint4*>(to_host ? p->k_host_dev : p->k_cache);
+    a.v_dst = static_cast<uint4*>(to_host ? p->v_host_dev : p->v_cache);
+    a.pairs = c->pairs;
+    a.n = (int32_t)n;
+    a.vec_per_block = (int32_t)((int64_t)p->d.num_kv_heads * p->d.block_size * p->d.head_dim * 2 / 16);
+    hipError_t e = pkv::launch_tier_copy(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "block-move launch (pool state now ahead of the device)");
+    e = hipEventRecord(c->ev, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+    c->pending = true;
+    p->copy_next = (p->copy_next + 1) % kCopyRing;
+    return PKV_OK;
+}
+
+int kv_seq_offload(pkv_pool* p, int32_t n, const int32_t* seq_ids, int32_t gpu_window, pkv_stream_t stream) {
+    if (!p) return fail(PKV_EINVAL, "kv_seq_offload: null pool");
+    if (!p->num_host) return fail(PKV_EINVAL, "kv_seq_offload: the pool has no host tier");
+    if (gpu_window < 1) return fail(PKV_EINVAL, "kv_seq_offload: gpu_window %d (must be >= 1)", gpu_window);
+    if (!p->k_cache || !p->v_cache) return fail(PKV_EINVAL, "kv_seq_offload: the pool has no device caches");
+    int rc = check_ids(p, n, seq_ids, "kv_seq_offload");
+    if (rc) return rc;
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const auto& b = p->blocks[seq_ids[i]];
+        const int64_t cold = (int64_t)b.size() > gpu_window ? (int64_t)b.size() - gpu_window : 0;
+        for (int64_t j = 0; j < cold; ++j) need += is_host(b[j]) ? 0 : 1;
+    }
+    if (need > (int64_t)p->host_stack.size())
+        return fail(PKV_ENOMEM, "kv_seq_offload: need %lld host blocks, %zu free", (long long)need, p->host_stack.size());
+    pkv_pool::CopySlot* c = nullptr;
+    if (need) {
+        rc = copy_slot(p, need, &c);
+        if (rc) return rc;
+    }
+    int64_t k = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        auto& b = p->blocks[s];
+        const int64_t cold = (int64_t)b.size() > gpu_window ? (int64_t)b.size() - gpu_window : 0;
+        for (int64_t j = 0; j < cold; ++j) {
+            const int32_t g = b[j];
+            if (is_host(g)) continue;
+            const int32_t h = p->host_stack.back();
+            p->host_stack.pop_back();
+            p->host_ref[h] = 1;
+            c->pairs[2 * k] = g;
+            c->pairs[2 * k + 1] = h;
+            ++k;
+            b[j] = host_entry(h);
+            ++p->nhost[s];
+            p->unref(g);
+        }
+    }
+    return launch_moves(p, c, k, true, (hipStream_t)stream);
+}
+
+int kv_seq_restore(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv_stream_t stream) {
+    if (!p) return fail(PKV_EINVAL, "kv_seq_restore: null pool");
+    if (!p->num_host) return fail(PKV_EINVAL, "kv_seq_restore: the pool has no host tier");
+    if (!p->k_cache || !p->v_cache) return fail(PKV_EINVAL, "kv_seq_restore: the pool has no device caches");
+    int rc = check_ids(p, n, seq_ids, "kv_seq_restore");
+    if (rc) return rc;
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) need += p->nhost[seq_ids[i]];
+    if (need > p->num_free)
+        return fail(PKV_ENOMEM, "kv_seq_restore: need %lld blocks, %d free", (long long)need, p->num_free);
+    pkv_pool::CopySlot* c = nullptr;
+    if (need) {
+        rc = copy_slot(p, need, &c);
+        if (rc) return rc;
+    }
+    int64_t k = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        if (!p->nhost[s]) continue;
+        for (auto& e : p->blocks[s]) {
+            if (!is_host(e)) continue;
+            const int32_t g = p->pop_free();
+            p->ref[g] = 1;
+            c->pairs[2 * k] = host_id(e);
+            c->pairs[2 * k + 1] = g;
+            ++k;
+            p->unref(e);
+            e = g;
+        }
+        p->nhost[s] = 0;
+    }
+    return launch_moves(p, c, k, false, (hipStream_t)stream);
 }
 
 int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t table_stride, int32_t table_width,

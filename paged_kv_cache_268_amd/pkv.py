@@ -23,7 +23,8 @@ EXPORTS = (
     "pkv_last_error", "pkv_version",
     "kv_block_pool_create", "kv_block_pool_destroy", "kv_seq_add", "kv_seq_import", "kv_seq_fork",
     "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_write_tables",
-    "kv_validate_tables", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
+    "kv_validate_tables", "kv_block_pool_attach_host_tier", "kv_seq_offload", "kv_seq_restore",
+    "kv_host_tier_stats", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
 )
 
@@ -74,6 +75,10 @@ def load(path: str = LIB_PATH):
         "kv_append": ([P, I32, P, P, P, P, P, P], ctypes.c_int),
         "kv_write_tables": ([P, P, P, P], ctypes.c_int),
         "kv_validate_tables": ([I32, P, I32, I32, P, I32, I32], ctypes.c_int),
+        "kv_block_pool_attach_host_tier": ([P, I32, P, P], ctypes.c_int),
+        "kv_seq_offload": ([P, I32, P, I32, P], ctypes.c_int),
+        "kv_seq_restore": ([P, I32, P, P], ctypes.c_int),
+        "kv_host_tier_stats": ([P, PI32, I32, PI32], ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], SZ),
@@ -314,3 +319,24 @@ class BlockPool:
 
     def write_tables(self, block_tables, context_lens, stream=None):
         check(self.lib.kv_write_tables(self.handle, _ptr(block_tables), _ptr(context_lens), _stream(stream)))
+
+    # -- host tier ----------------------------------------------------------
+    def attach_host_tier(self, num_host_blocks: int, k_host, v_host):
+        """k_host / v_host: pinned CPU tensors [num_host_blocks][Hkv][bs][D] (torch pin_memory=True)."""
+        check(self.lib.kv_block_pool_attach_host_tier(self.handle, num_host_blocks, _ptr(k_host), _ptr(v_host)))
+        self.k_host, self.v_host = k_host, v_host
+
+    def offload(self, seq_ids, gpu_window: int, stream=None):
+        ids = _i32(seq_ids)
+        check(self.lib.kv_seq_offload(self.handle, ids.size, ids.ctypes.data if ids.size else None, gpu_window,
+                                      _stream(stream)))
+
+    def restore(self, seq_ids, stream=None):
+        ids = _i32(seq_ids)
+        check(self.lib.kv_seq_restore(self.handle, ids.size, ids.ctypes.data if ids.size else None,
+                                      _stream(stream)))
+
+    def host_stats(self, block: int = -1):
+        nf, rc = ctypes.c_int32(), ctypes.c_int32(-1)
+        check(self.lib.kv_host_tier_stats(self.handle, ctypes.byref(nf), block, ctypes.byref(rc)))
+        return nf.value, rc.value
