@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
-F16, BF16 = 0, 1
+F16, BF16, FP8 = 0, 1, 3
 
 
 def compile_c(src: str, out: str) -> str:
@@ -50,6 +50,15 @@ class OracleLib:
         lib.oracle_paged_decode.argtypes = [i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P,
                                             ctypes.c_float, P, P, i]
         lib.oracle_paged_decode.restype = i
+        lib.oracle_paged_decode_kv.argtypes = [i, i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P,
+                                               ctypes.c_float, P, P, i]
+        lib.oracle_paged_decode_kv.restype = i
+        lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+        lib.oracle_fp8_encode.restype = ctypes.c_uint8
+        lib.oracle_fp8_encode_array.argtypes = [P, ctypes.c_int64, P]
+        lib.oracle_fp8_encode_array.restype = None
+        lib.oracle_quantize_fp8.argtypes = [P, i, i, i, i, P, P]
+        lib.oracle_quantize_fp8.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i
         lib.oracle_decode_value.argtypes = [ctypes.c_uint16, i]
@@ -63,18 +72,44 @@ class OracleLib:
     def decode_value(self, bits: int, dtype: int) -> float:
         return self.lib.oracle_decode_value(bits, dtype)
 
+    def fp8_encode(self, x) -> np.ndarray:
+        """Nearest E4M3 codes (saturating, ties to even) of fp32 values."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_fp8_encode_array(_ptr(x), x.size, _ptr(out))
+        return out
+
+    def quantize_fp8(self, src_bits, src_dtype: int, ntok: int):
+        """One (block, kv head) tile [bs][D] of 16-bit values -> (E4M3 codes [bs][D], fp32 scale)."""
+        src = np.ascontiguousarray(src_bits, dtype=np.uint16)
+        bs, D = src.shape
+        codes = np.empty((bs, D), dtype=np.uint8)
+        sc = np.empty(1, dtype=np.float32)
+        self.lib.oracle_quantize_fp8(_ptr(src), src_dtype, ntok, bs, D, _ptr(codes), _ptr(sc))
+        return codes, np.float32(sc[0])
+
     def paged_decode(self, q_bits, k_bits, v_bits, block_tables, context_lens, scale, *,
                      num_kv_heads, block_size, dtype, tok_lo=None, tok_hi=None,
-                     nthreads=None, table_width=None):
+                     nthreads=None, table_width=None, kv_dtype=None, k_scale=None, v_scale=None):
         """fp64 reference output [B][Hq][D] and lse [B][Hq] (natural log).
 
-        q_bits [B][Hq][D], k_bits/v_bits [NB][Hkv][bs][D]: raw uint16 storage of
-        fp16 (dtype=F16) or bf16 (dtype=BF16) values.  block_tables int32 [B][W],
-        context_lens int32 [B].  scale: the fp32 scale the GPU call receives.
+        q_bits [B][Hq][D]: raw uint16 storage of fp16 (dtype=F16) or bf16
+        (dtype=BF16) values.  k_bits/v_bits [NB][Hkv][bs][D]: the same storage
+        as q, or with kv_dtype=FP8 uint8 E4M3 codes with fp32 k_scale/v_scale
+        [NB][Hkv].  block_tables int32 [B][W], context_lens int32 [B].  scale:
+        the fp32 scale the GPU call receives.
         """
+        kv_dtype = dtype if kv_dtype is None else kv_dtype
+        kvt = np.uint8 if kv_dtype == FP8 else np.uint16
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
-        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
-        v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+        k_bits = np.ascontiguousarray(k_bits, dtype=kvt)
+        v_bits = np.ascontiguousarray(v_bits, dtype=kvt)
+        if kv_dtype == FP8:
+            k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+            v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+            assert k_scale.shape == v_scale.shape == (k_bits.shape[0], num_kv_heads)
+        else:
+            k_scale = v_scale = None
         tables = np.ascontiguousarray(block_tables, dtype=np.int32)
         ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
         B, Hq, D = q_bits.shape
@@ -87,10 +122,10 @@ class OracleLib:
         lse = np.empty((B, Hq), dtype=np.float64)
         width = tables.shape[1] if table_width is None else table_width
         nt = self.max_threads() if nthreads is None else int(nthreads)
-        rc = self.lib.oracle_paged_decode(
-            B, Hq, num_kv_heads, D, block_size, NB, tables.shape[1], width, dtype,
-            _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(tables), _ptr(ctx), _ptr(lo), _ptr(hi),
-            ctypes.c_float(scale), _ptr(out), _ptr(lse), nt)
+        rc = self.lib.oracle_paged_decode_kv(
+            B, Hq, num_kv_heads, D, block_size, NB, tables.shape[1], width, dtype, kv_dtype,
+            _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(k_scale), _ptr(v_scale), _ptr(tables), _ptr(ctx),
+            _ptr(lo), _ptr(hi), ctypes.c_float(scale), _ptr(out), _ptr(lse), nt)
         if rc != 0:
             raise ValueError(f"oracle_paged_decode failed with status {rc}")
         return out, lse
@@ -120,6 +155,14 @@ def decode_value(bits: int, dtype: int) -> float:
 
 def paged_decode(*args, **kw):
     return default().paged_decode(*args, **kw)
+
+
+def fp8_encode(x):
+    return default().fp8_encode(x)
+
+
+def quantize_fp8(src_bits, src_dtype, ntok):
+    return default().quantize_fp8(src_bits, src_dtype, ntok)
 
 
 def _bits16(t) -> np.ndarray:

@@ -32,6 +32,17 @@
  *   out = 0 and lse = -inf.  That reading of an empty context (the pages do not
  *   speak of one) is also what the GPU library writes.
  *
+ * Reduced-precision KV (oracle_paged_decode_kv with kv_dtype ORACLE_FP8): the
+ * cache holds one byte per value in the OCP 8-bit floating-point format E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 fraction bits; exponent field 0 is
+ * subnormal; the all-ones exponent with all-ones fraction is NaN; no
+ * infinities), and every (block, kv head) of K and of V carries one fp32
+ * scale: the value a code stands for is its E4M3 value times the scale of its
+ * block and kv head.  This is the KV-compression idea of
+ * "LLM+Agent 全栈推理底座" 5.2 (historical KV kept at reduced precision) carried
+ * to an 8-bit format with per-block scales; the pages fix neither the format
+ * nor the scale granularity.
+ *
  * Return value: 0 on success; -1 if a table entry that the context reaches is
  * outside [0, num_blocks) or a context length is negative or exceeds the table
  * width times block_size; -2 on a bad argument.  No output is defined on error.
@@ -44,7 +55,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1, ORACLE_FP8 = 3 };
 
 /* IEEE-754 binary16: 1 sign, 5 exponent, 10 fraction bits. */
 static double half_bits_to_double(uint16_t h) {
@@ -76,16 +87,90 @@ static double bf16_bits_to_double(uint16_t b) {
     return sign ? -v : v;
 }
 
+/* OCP E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; S.1111.111 is NaN. */
+static double e4m3_bits_to_double(uint8_t c) {
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xf;
+    int f = c & 0x7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -9);                  /* f/8 * 2^(1-7) */
+    else if (e == 15 && f == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(f + 8), e - 10);        /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 double oracle_decode_value(uint16_t bits, int dtype) {
+    if (dtype == ORACLE_FP8) return e4m3_bits_to_double((uint8_t)bits);
     return dtype == ORACLE_BF16 ? bf16_bits_to_double(bits) : half_bits_to_double(bits);
 }
 
-int oracle_paged_decode(
+/* The E4M3 code nearest to x (saturating: beyond the largest finite value 448
+ * the nearest finite code is 448's), ties to the code with an even last
+ * fraction bit; NaN gives the NaN code.  Brute force over the 127 non-negative
+ * finite codes, so it needs no rounding arithmetic of its own. */
+uint8_t oracle_fp8_encode(float x) {
+    if (x != x) return 0x7f;
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 127; ++c) {
+        const double d = fabs(e4m3_bits_to_double((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+void oracle_fp8_encode_array(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_encode(x[i]);
+}
+
+/* Quantise one (block, kv head): the first ntok rows of a [bs][D] tile of
+ * 16-bit values become E4M3 codes with one scale.  amax = max |x| over those
+ * rows; scale = amax / 448 in fp32 (1 when amax is 0); code = nearest E4M3 to
+ * x / scale, the division in fp32; rows from ntok on become code 0. */
+void oracle_quantize_fp8(const uint16_t* src, int src_dtype, int ntok, int bs, int D,
+                         uint8_t* codes, float* scale_out) {
+    float amax = 0.0f;
+    for (int i = 0; i < ntok * D; ++i) {
+        const float x = (float)oracle_decode_value(src[i], src_dtype);
+        if (fabsf(x) > amax) amax = fabsf(x);
+    }
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int i = 0; i < bs * D; ++i) {
+        if (i < ntok * D) {
+            const float x = (float)oracle_decode_value(src[i], src_dtype);
+            const float y = x / scale;
+            codes[i] = oracle_fp8_encode(y);
+        } else {
+            codes[i] = 0;
+        }
+    }
+    *scale_out = scale;
+}
+
+/* One cache value: 16-bit storage decoded exactly, or an E4M3 code times the
+ * scale of its (block, kv head). */
+static double kv_value(const void* cache, int64_t idx, int kv_dtype, const float* scales, int64_t bg) {
+    if (kv_dtype == ORACLE_FP8)
+        return e4m3_bits_to_double(((const uint8_t*)cache)[idx]) * (double)scales[bg];
+    return oracle_decode_value(((const uint16_t*)cache)[idx], kv_dtype);
+}
+
+int oracle_paged_decode_kv(
     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-    int block_size, int num_blocks, int table_stride, int table_width, int dtype,
-    const uint16_t* q,            /* [B][Hq][D] */
-    const uint16_t* k_cache,      /* [NB][Hkv][bs][D] */
-    const uint16_t* v_cache,      /* [NB][Hkv][bs][D] */
+    int block_size, int num_blocks, int table_stride, int table_width, int dtype, int kv_dtype,
+    const uint16_t* q,            /* [B][Hq][D], dtype */
+    const void* k_cache,          /* [NB][Hkv][bs][D], kv_dtype */
+    const void* v_cache,          /* [NB][Hkv][bs][D], kv_dtype */
+    const float* k_scale,         /* [NB][Hkv] when kv_dtype is ORACLE_FP8, else unused */
+    const float* v_scale,
     const int32_t* block_tables,  /* [B][table_stride], table_width used */
     const int32_t* context_lens,  /* [B] */
     const int32_t* tok_lo,        /* nullable [B] */
@@ -96,7 +181,9 @@ int oracle_paged_decode(
     int nthreads)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        block_size <= 0 || num_q_heads % num_kv_heads != 0 || table_width > table_stride)
+        block_size <= 0 || num_q_heads % num_kv_heads != 0 || table_width > table_stride ||
+        (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+        (kv_dtype == ORACLE_FP8 ? (!k_scale || !v_scale) : kv_dtype != dtype))
         return -2;
     const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads, D = head_dim;
     const int bs = block_size, G = Hq / Hkv;
@@ -153,8 +240,8 @@ int oracle_paged_decode(
             const int64_t b = block_tables[(int64_t)s * table_stride + t / bs];
             const int64_t row = ((b * Hkv + g) * bs + (t % bs)) * D;
             for (int d = 0; d < D; ++d) {
-                Kc[(int64_t)i * D + d] = oracle_decode_value(k_cache[row + d], dtype);
-                Vc[(int64_t)i * D + d] = oracle_decode_value(v_cache[row + d], dtype);
+                Kc[(int64_t)i * D + d] = kv_value(k_cache, row + d, kv_dtype, k_scale, b * Hkv + g);
+                Vc[(int64_t)i * D + d] = kv_value(v_cache, row + d, kv_dtype, v_scale, b * Hkv + g);
             }
         }
 
@@ -183,6 +270,19 @@ int oracle_paged_decode(
         free(Kc); free(Vc); free(z); free(acc);
     }
     return status;
+}
+
+/* Same-precision K/V and q (fp16 or bf16 everywhere). */
+int oracle_paged_decode(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, int table_stride, int table_width, int dtype,
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* tok_lo, const int32_t* tok_hi,
+    float scale, double* out, double* lse, int nthreads)
+{
+    return oracle_paged_decode_kv(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  table_stride, table_width, dtype, dtype, q, k_cache, v_cache, NULL, NULL,
+                                  block_tables, context_lens, tok_lo, tok_hi, scale, out, lse, nthreads);
 }
 
 /* Threads OpenMP would use for nthreads <= 0 requests (reported by the bench). */

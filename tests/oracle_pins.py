@@ -18,7 +18,7 @@ import torch
 
 from paged_kv_cache_268_amd import workloads as W
 
-F16, BF16 = 0, 1
+F16, BF16, FP8 = 0, 1, 3
 
 
 # ---------------------------------------------------------------------------
@@ -328,11 +328,86 @@ def pin_bad_table_rejected(lib):
     raise AssertionError("out-of-range block id was accepted")
 
 
+# ---------------------------------------------------------------------------
+# E4M3 (8-bit KV) pins: torch's float8_e4m3fn type is the library reference
+# ---------------------------------------------------------------------------
+
+def _e4m3_values(codes) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def pin_decode_fp8_all_codes(lib):
+    codes = np.arange(256, dtype=np.uint8)
+    got = np.array([lib.decode_value(int(c), FP8) for c in codes])
+    assert np.array_equal(got, _e4m3_values(codes), equal_nan=True)
+
+
+def pin_fp8_encode_matches_torch(lib):
+    """Every finite value, every midpoint of neighbours (ties) and random values inside the range."""
+    vals = _e4m3_values(np.arange(127, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    rnd = np.random.default_rng(7).uniform(-447.0, 447.0, 20000)
+    x = np.concatenate([vals, -vals, mids, -mids, rnd]).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64)[:2 * len(vals) + 2 * len(mids)],
+                          np.concatenate([vals, -vals, mids, -mids])), "midpoints not exact in fp32"
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(lib.fp8_encode(x), want)
+
+
+def pin_fp8_encode_saturates(lib):
+    """Beyond 448 (the largest finite E4M3 value) the nearest finite code is 448's: 0x7E / 0xFE."""
+    x = np.array([448.0, 449.0, 464.0, 479.0, 480.0, 1e6, np.inf, -500.0, -np.inf], np.float32)
+    assert lib.fp8_encode(x).tolist() == [0x7E] * 7 + [0xFE] * 2
+    assert lib.fp8_encode(np.array([np.nan], np.float32))[0] & 0x7F == 0x7F
+
+
+def pin_fp8_quantize_bound(lib):
+    """amax/448 scale; the amax element hits +-448; every code within half a step of x/scale."""
+    rng = np.random.default_rng(8)
+    for ntok, spread in ((11, 3.0), (16, 1e-3), (1, 50.0)):
+        x = (rng.standard_normal((16, 64)) * spread).astype(np.float32)
+        bits = to_bits((x.view(np.uint32) & 0xFFFF0000).view(np.float32), "bf16")
+        xv = from_bits(bits, "bf16")
+        codes, sc = lib.quantize_fp8(bits, BF16, ntok)
+        amax = np.float32(np.abs(xv[:ntok]).max())
+        assert sc == amax / np.float32(448.0)
+        assert np.all(codes[ntok:] == 0)
+        i = np.unravel_index(np.argmax(np.abs(xv[:ntok])), (ntok, 64))
+        assert codes[i] & 0x7F == 0x7E
+        deq = _e4m3_values(codes[:ntok])
+        y = xv[:ntok] / np.float64(sc)
+        step = np.where(np.abs(y) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3),
+                        2.0 ** -9)
+        assert np.all(np.abs(deq - y) <= step / 2 * (1 + 1e-6) + 1e-6 * np.abs(y))
+    codes, sc = lib.quantize_fp8(np.zeros((16, 64), np.uint16), BF16, 5)
+    assert sc == 1.0 and not codes.any()
+
+
+def pin_fp8_equals_exact_bf16(lib):
+    """E4M3 codes with power-of-two scales per (block, kv head) are exact bf16 values: the 8-bit
+    path must give bit for bit what the 16-bit path gives on those values."""
+    wl, qb, _, _ = random_case(B=3, Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", ctx=(5, 33, 47), seed=9)
+    rng = np.random.default_rng(10)
+    NB, Hkv = wl.num_blocks, wl.num_kv_heads
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    kc = rng.choice(finite, (NB, Hkv, 16, 64)).astype(np.uint8)
+    vc = rng.choice(finite, (NB, Hkv, 16, 64)).astype(np.uint8)
+    ks = (2.0 ** rng.integers(-3, 4, (NB, Hkv))).astype(np.float32)
+    vs = (2.0 ** rng.integers(-3, 4, (NB, Hkv))).astype(np.float32)
+    kb = to_bits(_e4m3_values(kc) * ks[:, :, None, None], "bf16")
+    vb = to_bits(_e4m3_values(vc) * vs[:, :, None, None], "bf16")
+    o16, l16 = run(lib, wl, qb, kb, vb)
+    o8, l8 = run(lib, wl, qb, kc, vc, kv_dtype=FP8, k_scale=ks, v_scale=vs)
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+
+
 ALL_PINS = [
     pin_decode_f16_all_bits, pin_decode_bf16_all_bits, pin_ctx1_returns_v,
     pin_equal_scores_mean, pin_equal_keys_mean, pin_two_token_closed_form,
     pin_permutation_invariance, pin_shared_equals_duplicated, pin_gqa_equals_replicated_mha,
     pin_split_merge, pin_tail_poison, pin_convex_bound, pin_key_shift_invariance,
     pin_scale_q_tradeoff, pin_torch_sdpa, pin_brute_force, pin_empty_context,
-    pin_bad_table_rejected,
+    pin_bad_table_rejected, pin_decode_fp8_all_codes, pin_fp8_encode_matches_torch,
+    pin_fp8_encode_saturates, pin_fp8_quantize_bound, pin_fp8_equals_exact_bf16,
 ]

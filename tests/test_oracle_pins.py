@@ -36,6 +36,13 @@ MUTANTS = [
     ("wrong-sign-score", "z[i] = sc * dot;", "z[i] = -sc * dot;"),
     ("q-head-of-kv", "q + ((int64_t)s * Hq + h) * D;", "q + ((int64_t)s * Hq + g) * D;"),
     ("range-off-by-one", "const int n = hi > lo ? hi - lo : 0;", "const int n = hi > lo ? hi - lo - (lo > 0) : 0;"),
+    ("fp8-exponent-bias", "(double)(f + 8), e - 10);", "(double)(f + 8), e - 9);"),
+    ("fp8-subnormal", "ldexp((double)f, -9);", "ldexp((double)f, -10);"),
+    ("fp8-scale-transposed", "k_scale, b * Hkv + g);", "k_scale, g * num_blocks + b);"),
+    ("fp8-v-with-k-scale", "kv_dtype, v_scale, b * Hkv + g);", "kv_dtype, k_scale, b * Hkv + g);"),
+    ("fp8-ties-odd", "(c & 1) == 0", "(c & 1) == 1"),
+    ("fp8-quant-scale", "amax / 448.0f", "amax / 480.0f"),
+    ("fp8-quant-tail", "if (i < ntok * D) {", "if (i <= ntok * D) {"),
 ]
 
 
