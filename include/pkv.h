@@ -53,7 +53,9 @@ enum {
     PKV_EWORKSPACE = -5     /* workspace missing or smaller than paged_attn_workspace_bytes() */
 };
 
-enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2 };
+/* PKV_FP8_E4M3: OCP 8-bit float E4M3 (1 sign, 4 exponent bits, bias 7, 3
+ * fraction bits, no infinities, S.1111.111 = NaN), one byte per value. */
+enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2, PKV_FP8_E4M3 = 3 };
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
@@ -77,7 +79,7 @@ typedef struct pkv_pool_desc {
     int32_t block_size;          /* tokens per block: 16 or 32 */
     int32_t num_kv_heads;        /* >= 1 */
     int32_t head_dim;            /* 64 or 128 */
-    int32_t kv_dtype;            /* PKV_F16 or PKV_BF16 */
+    int32_t kv_dtype;            /* PKV_F16, PKV_BF16, or PKV_FP8_E4M3 (then set scales, below) */
     int32_t max_seqs;            /* rows of block_tables / context_lens (>= 1) */
     int32_t max_blocks_per_seq;  /* columns of block_tables (>= 1) */
 } pkv_pool_desc;
@@ -149,6 +151,34 @@ int kv_reserve(pkv_pool* pool, int32_t n, const int32_t* seq_ids, int32_t* items
 int kv_append(pkv_pool* pool, int32_t n, const int32_t* seq_ids,
               const void* k_new, const void* v_new,
               int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream);
+
+/* 8-bit pools (kv_dtype PKV_FP8_E4M3; k_cache / v_cache hold one E4M3 code per
+ * value): the device scales of every (block, kv head), k_scale / v_scale
+ * float [num_blocks][num_kv_heads], and the default scales of new blocks,
+ * k_init / v_init float [num_kv_heads] (device, caller-owned, borrowed).
+ * kv_append on such a pool takes bf16 k_new / v_new, divides each value by
+ * its block's scale (fp32) and stores the nearest code (ties to even,
+ * saturating at +-448); a row that starts a block this call took first
+ * records k_init / v_init as that block's scales; copy-on-write copies the
+ * scales with the codes.  Required before kv_append on an 8-bit pool. */
+int kv_block_pool_set_fp8_scales(pkv_pool* pool, float* k_scale, float* v_scale,
+                                 const float* k_init, const float* v_init);
+
+/* Quantise 16-bit K/V blocks into an 8-bit cache, on `stream`.  items: device
+ * int32 [n][3] = (source block, destination block, used rows).  For each item
+ * and kv head g, separately for K and V: amax = max |x| over the first `used`
+ * rows of the source (block, g) tile; scale = amax / 448 (fp32; 1 when amax is
+ * 0) goes to k_scale (v_scale)[destination][g]; every used value becomes the
+ * E4M3 code nearest to x / scale (fp32 division; ties to even; saturating);
+ * rows from `used` on become code 0.
+ *   src_k, src_v : device [*][num_kv_heads][block_size][head_dim] of src_dtype (F16 / BF16)
+ *   dst_k, dst_v : device uint8 [*][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale : device float [*][num_kv_heads]
+ * Destination blocks must be distinct. */
+int kv_quantize_fp8(int32_t n, const int32_t* items, const void* src_k, const void* src_v,
+                    int32_t src_dtype, void* dst_k, void* dst_v, float* k_scale, float* v_scale,
+                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                    pkv_stream_t stream);
 
 /* Publish the whole host view to the device tables (-1 past each length,
  * length 0 for free rows and for sequences parked in the host tier), ordered
@@ -249,8 +279,8 @@ typedef struct pkv_attn_desc {
     int32_t table_stride;        /* int32 elements between block-table rows */
     int32_t max_context_len;     /* host upper bound of context_lens[] (sizes grid and workspace) */
     int32_t partition_size;      /* 0 = balanced split; else a multiple of block_size (fixed partitions) */
-    int32_t q_dtype;             /* PKV_F16 / PKV_BF16, equal to kv_dtype */
-    int32_t kv_dtype;            /* PKV_F16 / PKV_BF16 */
+    int32_t q_dtype;             /* PKV_F16 / PKV_BF16: equal to kv_dtype, or PKV_BF16 with 8-bit K/V */
+    int32_t kv_dtype;            /* PKV_F16 / PKV_BF16, or PKV_FP8_E4M3 (decode through the _fp8 calls) */
     int32_t out_dtype;           /* PKV_F32, or the same as q_dtype */
     int32_t num_waves;           /* waves in the grid; 0 = every wave that fits the device at once */
 } pkv_attn_desc;
@@ -288,6 +318,29 @@ int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const v
 int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, void* out,
                      float* lse, const void* workspace, size_t workspace_bytes,
                      pkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode over an 8-bit K/V cache (kv_dtype PKV_FP8_E4M3, q_dtype PKV_BF16).
+ * Reduced-precision storage of cached K/V ("LLM+Agent 全栈推理底座" 5.2 keeps
+ * historical KV at reduced precision) in the OCP E4M3 format with one fp32
+ * scale per (block, kv head):
+ *   k_cache, v_cache : device uint8 [num_blocks][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale : device float [num_blocks][num_kv_heads]
+ * A K (V) code c in block b, kv head g stands for e4m3(c) * k_scale[b][g]
+ * (v_scale[b][g]); everything else is paged_attn_decode: scores, softmax and
+ * sums in fp32, same split, same workspace, same outputs.  The 16-bit entry
+ * points reject an 8-bit descriptor (PKV_EINVAL) and these reject a 16-bit one.
+ * ------------------------------------------------------------------------ */
+int paged_attn_decode_fp8(const pkv_attn_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          pkv_stream_t stream);
+int paged_attn_decode_partials_fp8(const pkv_attn_desc* desc, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   float scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, pkv_stream_t stream);
 
 /* Debug: the segments of the split for host context lengths, in (seq, kv
  * head, slot) order, as rows of 5 int32: seq, kv_head, slot, tok_lo, tok_hi.

@@ -16,12 +16,19 @@
 // ("架构解构：推理引擎的四层抽象", PagedAttention section: logical->physical block
 // table; "LLM+Agent 全栈推理底座" 4.2: blocks taken from a free list on demand).
 //
+// 8-bit (E4M3) pools: the new bf16 rows are divided by their block's scale
+// and rounded to the nearest code; a row that starts a new block (slot at
+// offset 0 of a block this call took) uses, and records as that block's
+// scales, the pool's default scales of its kv head; copy-on-write also copies
+// the source block's scales.
+//
 // Step 1 runs as its own launch before steps 2-3 whenever some item copies:
 // a block one item copies from may be the tail that another item of the same
 // call writes into (its last other holder), so every copy must finish first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_fp8.h"
 #include "pkv_kernels.h"
 
 namespace pkv {
@@ -34,9 +41,14 @@ __global__ void __launch_bounds__(256) kv_append_cow_kernel(AppendArgs a) {
     __syncthreads();
     const AppendItem it = s_it;
     if (it.cow_src < 0) return;
-    const int bs = a.block_size, Hkv = a.num_kv_heads, vec_per_row = a.head_dim / 8;   // uint4 per row
+    const int bs = a.block_size, Hkv = a.num_kv_heads;
+    const int vec_per_row = a.kv8 ? a.head_dim / 16 : a.head_dim / 8;   // uint4 per row
     uint4* kc = reinterpret_cast<uint4*>(a.k_cache);
     uint4* vc = reinterpret_cast<uint4*>(a.v_cache);
+    if (a.kv8 && (int)threadIdx.x < Hkv) {
+        a.k_scale[(int64_t)it.new_block * Hkv + threadIdx.x] = a.k_scale[(int64_t)it.cow_src * Hkv + threadIdx.x];
+        a.v_scale[(int64_t)it.new_block * Hkv + threadIdx.x] = a.v_scale[(int64_t)it.cow_src * Hkv + threadIdx.x];
+    }
     const int per_head = it.cow_ntok * vec_per_row;
     for (int x = threadIdx.x; x < Hkv * per_head; x += blockDim.x) {
         const int g = x / per_head, r = x % per_head;
@@ -49,8 +61,54 @@ __global__ void __launch_bounds__(256) kv_append_cow_kernel(AppendArgs a) {
 
 // Write phase: one 256-thread workgroup per item moves 16-byte pieces of the
 // new K/V row of every kv head into the slot, then updates the tables.
+// 8-bit pool: 8 bf16 values of the new row per thread -> 8 codes.
+__device__ __forceinline__ void append_row_fp8(const AppendArgs& a, int i, int blk, int off, bool fresh) {
+    const int bs = a.block_size, Hkv = a.num_kv_heads, per_row = a.head_dim / 8;
+    const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
+    const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
+    uint2* kc = reinterpret_cast<uint2*>(a.k_cache);
+    uint2* vc = reinterpret_cast<uint2*>(a.v_cache);
+    for (int x = threadIdx.x; x < Hkv * per_row; x += blockDim.x) {
+        const int g = x / per_row, r = x % per_row;
+        const int64_t bg = (int64_t)blk * Hkv + g;
+        const float ks = fresh ? a.k_init[g] : a.k_scale[bg];
+        const float vs = fresh ? a.v_init[g] : a.v_scale[bg];
+        const int64_t src = ((int64_t)i * Hkv + g) * per_row + r;
+        const int64_t row = (bg * bs + off) * per_row + r;
+        const uint4 w[2] = {kn[src], vn[src]};
+        const float sc[2] = {ks, vs};
+        uint2 o[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t ws[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+            uint32_t b[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                b[2 * e] = f32_to_e4m3(__builtin_bit_cast(float, ws[e] << 16) / sc[t]);
+                b[2 * e + 1] = f32_to_e4m3(__builtin_bit_cast(float, ws[e] & 0xFFFF0000u) / sc[t]);
+            }
+            o[t] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+        }
+        kc[row] = o[0];
+        vc[row] = o[1];
+    }
+    if (fresh && (int)threadIdx.x < Hkv) {
+        a.k_scale[(int64_t)blk * Hkv + threadIdx.x] = a.k_init[threadIdx.x];
+        a.v_scale[(int64_t)blk * Hkv + threadIdx.x] = a.v_init[threadIdx.x];
+    }
+}
+
 __device__ __forceinline__ void append_item(const AppendArgs& a, int i, int seq, int slot, int new_block,
                                             int new_len) {
+    if (a.kv8) {
+        const int bs = a.block_size;
+        append_row_fp8(a, i, slot / bs, slot % bs, new_block >= 0 && slot % bs == 0);
+        if (threadIdx.x == 0) {
+            if (new_block >= 0) a.block_tables[(int64_t)seq * a.table_stride + (new_len - 1) / bs] = new_block;
+            a.context_lens[seq] = new_len;
+        }
+        return;
+    }
     const int bs = a.block_size, Hkv = a.num_kv_heads, vec_per_row = a.head_dim / 8;
     uint4* kc = reinterpret_cast<uint4*>(a.k_cache);
     uint4* vc = reinterpret_cast<uint4*>(a.v_cache);

@@ -103,6 +103,29 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
     return xsum32(xsum16(x));
 }
 
+template <bool C, class T, class F> struct Pick { using type = T; };
+template <class T, class F> struct Pick<false, T, F> { using type = F; };
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Four OCP E4M3 codes (bytes of w, low byte first) -> two words of packed
+// bf16, exact: the hardware conversion yields the fp32 values and every E4M3
+// value has at most 4 significant bits, so the top half of each is its bf16.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    const bf16x2 pa = {(__bf16)a[0], (__bf16)a[1]};     // exact: at most 4 significant bits
+    const bf16x2 pb = {(__bf16)b[0], (__bf16)b[1]};
+    lo = __builtin_bit_cast(uint32_t, pa);
+    hi = __builtin_bit_cast(uint32_t, pb);
+}
+// Four E4M3 codes -> four floats (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+    const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+}
+
 // Two packed 16-bit values -> two floats (exact widening).
 template <bool BF16>
 __device__ __forceinline__ void widen2(uint32_t w, float& lo, float& hi) {
@@ -166,15 +189,18 @@ __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
 // A chunk's part inside one (s, g) is a segment; it writes its normalised
 // output and log2-domain lse to slot k = c - first(s, g) / C, or the final
 // output directly when it covers all of (s, g).
-template <int D, int BS, int GP, bool BF16>
+template <int D, int BS, int GP, bool BF16, bool KV8>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_split_kernel(DecodeArgs a) {
-    constexpr int KS = D / 32;            // MFMA k-steps = K load instructions per tile
-    constexpr int LPR = D / 8;            // V: lanes per row
+    constexpr int KS = D / 32;            // MFMA k-steps per tile
+    constexpr int KL = KV8 ? D / 64 : KS; // K load instructions per tile (16 bytes per lane each)
+    constexpr int LPR = D / 8;            // V: lanes per row (8 values per lane)
     constexpr int RPI = 64 / LPR;         // V: rows per wave load instruction
     constexpr int NI = kTile / RPI;       // V: load instructions per tile
     static_assert(NI * RPI == kTile && GP <= 16, "tile shape");
+    static_assert(!KV8 || BF16, "8-bit K/V pair with a bf16 query");
     using MfmaIn = typename MfmaType<BF16>::vec;
+    using VLoad = typename Pick<KV8, uint2, uint4>::type;   // one lane's 8 V values
 
     __shared__ int s_pre[kMaxSeqs + 1];
     __shared__ int s_wsum[kWaves];
@@ -240,9 +266,14 @@ paged_decode_split_kernel(DecodeArgs a) {
     const int c = lane % LPR;
     const int r = lane / LPR;
     const float sl2 = a.scale * kLog2e;
-    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
-    const int k_off = mrow * D + kq * 8;  // lane's K element offset inside a tile (+ 32 * ks)
+    using KvElem = typename Pick<KV8, uint8_t, uint16_t>::type;
+    const KvElem* kc = reinterpret_cast<const KvElem*>(a.k_cache);
+    const KvElem* vc = reinterpret_cast<const KvElem*>(a.v_cache);
+    // Lane's K element offset inside a tile (+ 32 * ks for 16-bit values).  With
+    // 8-bit values a lane loads 16 codes, d in [16 cq, 16 cq + 16) with
+    // cq = 4 u + kq, which feed k-steps 2u and 2u + 1; the q operand follows
+    // the same d order, so the dot products are unchanged.
+    const int k_off = KV8 ? mrow * D + kq * 16 : mrow * D + kq * 8;
     const int v_off = r * D + c * 8;      // lane's V element offset inside a tile (+ i * RPI * D)
 
     // One segment: tiles [j0, j1) of kv head g of sequence s.
@@ -256,8 +287,9 @@ paged_decode_split_kernel(DecodeArgs a) {
         for (int ks = 0; ks < KS; ++ks) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (mrow < G) {
+                const int d0 = KV8 ? 16 * (4 * (ks / 2) + kq) + 8 * (ks % 2) : ks * 32 + kq * 8;
                 const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                                     ((int64_t)s * a.num_q_heads + h0 + mrow) * D + ks * 32 + kq * 8;
+                                     ((int64_t)s * a.num_q_heads + h0 + mrow) * D + d0;
                 w = *reinterpret_cast<const uint4*>(qp);
             }
             qb[ks] = __builtin_bit_cast(MfmaIn, w);
@@ -280,18 +312,35 @@ paged_decode_split_kernel(DecodeArgs a) {
             return (((int64_t)blk * Hkv + g) * BS + (j * kTile) % BS) * D;
         };
         // QK on the matrix core, then the online-softmax update; the tile's
-        // weights go to this wave's LDS slot.
-        auto qk_softmax = [&](int j, const uint4 (&kb)[KS]) {
+        // weights go to this wave's LDS slot.  8-bit K: codes widened to bf16
+        // in registers, the tile's K scale folded into the score scale and
+        // its V scale into the weights written for PV (the weight sum l keeps
+        // the unscaled weights).
+        auto qk_softmax = [&](int j, const uint4 (&kb)[KL], float ksc, float vsc) {
             const int t0 = j * kTile;
             const bool full = t0 + kTile <= ctx;
             floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (KV8) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
+                for (int u = 0; u < KL; ++u) {
+                    uint4 lo, hi;
+                    fp8x4_to_bf16x4(kb[u].x, lo.x, lo.y);
+                    fp8x4_to_bf16x4(kb[u].y, lo.z, lo.w);
+                    fp8x4_to_bf16x4(kb[u].z, hi.x, hi.y);
+                    fp8x4_to_bf16x4(kb[u].w, hi.z, hi.w);
+                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, lo), qb[2 * u], sc);
+                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, hi), qb[2 * u + 1], sc);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
+            }
+            const float sk = KV8 ? sl2 * ksc : sl2;
             float x[4];
             bool need = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i] = sc[i] * sl2;
+                x[i] = sc[i] * sk;
                 if (!full && t0 + 4 * kq + i >= ctx) x[i] = -INFINITY;
                 need |= x[i] > m_lane + kTau;
             }
@@ -320,12 +369,12 @@ paged_decode_split_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const float e = __builtin_amdgcn_exp2f(x[i] - m_lane);
                 l_lane += e;
-                s_p[wave][4 * kq + i][mrow] = e;
+                s_p[wave][4 * kq + i][mrow] = KV8 ? e * vsc : e;
             }
             __builtin_amdgcn_wave_barrier();
         };
         // PV on the vector ALUs, V rows in the coalesced layout.
-        auto pv = [&](int j, const uint4 (&vb)[NI]) {
+        auto pv = [&](int j, const VLoad (&vb)[NI]) {
             const int t0 = j * kTile;
             const bool full = t0 + kTile <= ctx;
 #pragma unroll
@@ -343,10 +392,15 @@ paged_decode_split_kernel(DecodeArgs a) {
                     for (int h = 0; h < GP; ++h) ph[h] = s_p[wave][row][h];
                 }
                 float vf[8];
-                widen2<BF16>(vb[i].x, vf[0], vf[1]);
-                widen2<BF16>(vb[i].y, vf[2], vf[3]);
-                widen2<BF16>(vb[i].z, vf[4], vf[5]);
-                widen2<BF16>(vb[i].w, vf[6], vf[7]);
+                if constexpr (KV8) {
+                    fp8x4_to_f32(vb[i].x, vf);
+                    fp8x4_to_f32(vb[i].y, vf + 4);
+                } else {
+                    widen2<BF16>(vb[i].x, vf[0], vf[1]);
+                    widen2<BF16>(vb[i].y, vf[2], vf[3]);
+                    widen2<BF16>(vb[i].z, vf[4], vf[5]);
+                    widen2<BF16>(vb[i].w, vf[6], vf[7]);
+                }
                 if (!full) {
                     // Unused slots may hold anything (NaN included): never let them into a sum.
                     const bool valid = t0 + row < ctx;
@@ -360,16 +414,17 @@ paged_decode_split_kernel(DecodeArgs a) {
             }
             __builtin_amdgcn_wave_barrier();
         };
-        auto load_k = [&](int j, int32_t blk, uint4 (&kb)[KS]) {
+        auto load_k = [&](int j, int32_t blk, uint4 (&kb)[KL]) {
             const int64_t base = tile_base(j, blk);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const uint4*>(kc + base + k_off + ks * 32);
+            for (int u = 0; u < KL; ++u)
+                kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto load_v = [&](int j, int32_t blk, uint4 (&vb)[NI]) {
+        auto load_v = [&](int j, int32_t blk, VLoad (&vb)[NI]) {
             const int64_t base = tile_base(j, blk);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const uint4*>(vc + base + v_off + i * RPI * D);
+            for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const VLoad*>(vc + base + v_off + i * RPI * D);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -379,27 +434,46 @@ paged_decode_split_kernel(DecodeArgs a) {
         // re-read that tile (in bounds, served by the cache); a window with an
         // odd tile count ends with one tile past the segment, which every row
         // treats as outside the context (weight 0, V never used).  Block ids
-        // come 128 tiles at a time, two per lane, read back with v_readlane.
+        // come 128 tiles at a time, two per lane, read back with v_readlane;
+        // with 8-bit K/V each lane also loads the K and V scales of its two
+        // blocks (vector loads: they stay in order with the tile loads).
         for (int c0 = j0; c0 < j1; c0 += 128) {
             const int cn = min(128, j1 - c0);
             const int32_t blo = lane < cn ? table[((c0 + lane) * kTile) / BS] : 0;
             const int32_t bhi = lane + 64 < cn ? table[((c0 + 64 + lane) * kTile) / BS] : 0;
+            float kslo = 1.f, kshi = 1.f, vslo = 1.f, vshi = 1.f;
+            if constexpr (KV8) {
+                if (lane < cn) {
+                    kslo = a.k_scale[(int64_t)blo * Hkv + g];
+                    vslo = a.v_scale[(int64_t)blo * Hkv + g];
+                }
+                if (lane + 64 < cn) {
+                    kshi = a.k_scale[(int64_t)bhi * Hkv + g];
+                    vshi = a.v_scale[(int64_t)bhi * Hkv + g];
+                }
+            }
             auto blk = [&](int it) {
                 const int i = min(it, cn - 1);
                 return i < 64 ? __builtin_amdgcn_readlane(blo, i) : __builtin_amdgcn_readlane(bhi, i - 64);
             };
+            auto lane_pick = [&](float lo, float hi, int it) {
+                const int i = min(it, cn - 1);
+                return __builtin_bit_cast(float, i < 64 ? __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), i)
+                                                        : __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), i - 64));
+            };
             auto tile = [&](int it) { return c0 + min(it, cn - 1); };
-            uint4 ka[KS], va[NI], kb2[KS], vb2[NI];
+            uint4 ka[KL], kb2[KL];
+            VLoad va[NI], vb2[NI];
             load_k(tile(0), blk(0), ka);
             load_v(tile(0), blk(0), va);
             load_k(tile(1), blk(1), kb2);
             load_v(tile(1), blk(1), vb2);
             for (int it = 0; it < cn; it += 2) {
-                qk_softmax(c0 + it, ka);
+                qk_softmax(c0 + it, ka, lane_pick(kslo, kshi, it), lane_pick(vslo, vshi, it));
                 load_k(tile(it + 2), blk(it + 2), ka);
                 pv(c0 + it, va);
                 load_v(tile(it + 2), blk(it + 2), va);
-                qk_softmax(c0 + it + 1, kb2);
+                qk_softmax(c0 + it + 1, kb2, lane_pick(kslo, kshi, it + 1), lane_pick(vslo, vshi, it + 1));
                 load_k(tile(it + 3), blk(it + 3), kb2);
                 pv(c0 + it + 1, vb2);
                 load_v(tile(it + 3), blk(it + 3), vb2);
@@ -542,9 +616,9 @@ paged_decode_merge_kernel(MergeArgs a) {
 // Launchers.
 // ---------------------------------------------------------------------------
 
-template <int D, int BS, int GP, bool BF16>
+template <int D, int BS, int GP, bool BF16, bool KV8>
 static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStream_t stream) {
-    auto kern = paged_decode_split_kernel<D, BS, GP, BF16>;
+    auto kern = paged_decode_split_kernel<D, BS, GP, BF16, KV8>;
     if (waves_per_cu) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kThreads, 0);
@@ -556,38 +630,49 @@ static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStre
     return hipGetLastError();
 }
 
-template <int D, int BS, bool BF16>
+template <int D, int BS, bool BF16, bool KV8>
 static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st) {
     switch (gp) {
-        case 1: return split_dispatch<D, BS, 1, BF16>(a, wpc, st);
-        case 2: return split_dispatch<D, BS, 2, BF16>(a, wpc, st);
-        case 4: return split_dispatch<D, BS, 4, BF16>(a, wpc, st);
-        case 8: return split_dispatch<D, BS, 8, BF16>(a, wpc, st);
+        case 1: return split_dispatch<D, BS, 1, BF16, KV8>(a, wpc, st);
+        case 2: return split_dispatch<D, BS, 2, BF16, KV8>(a, wpc, st);
+        case 4: return split_dispatch<D, BS, 4, BF16, KV8>(a, wpc, st);
+        case 8: return split_dispatch<D, BS, 8, BF16, KV8>(a, wpc, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool KV8>
 static hipError_t split_b(const DecodeArgs* a, int bs, int gp, int* wpc, hipStream_t st) {
-    if (bs == 16) return split_g<D, 16, BF16>(a, gp, wpc, st);
-    if (bs == 32) return split_g<D, 32, BF16>(a, gp, wpc, st);
+    if (bs == 16) return split_g<D, 16, BF16, KV8>(a, gp, wpc, st);
+    if (bs == 32) return split_g<D, 32, BF16, KV8>(a, gp, wpc, st);
     return hipErrorInvalidValue;
 }
 
-static hipError_t split_any(const DecodeArgs* a, int head_dim, int bs, int gp, bool bf16, int* wpc, hipStream_t st) {
-    if (head_dim == 128) return bf16 ? split_b<128, true>(a, bs, gp, wpc, st) : split_b<128, false>(a, bs, gp, wpc, st);
-    if (head_dim == 64) return bf16 ? split_b<64, true>(a, bs, gp, wpc, st) : split_b<64, false>(a, bs, gp, wpc, st);
+template <int D>
+static hipError_t split_t(const DecodeArgs* a, int bs, int gp, KvKind kind, int* wpc, hipStream_t st) {
+    switch (kind) {
+        case KvKind::F16: return split_b<D, false, false>(a, bs, gp, wpc, st);
+        case KvKind::BF16: return split_b<D, true, false>(a, bs, gp, wpc, st);
+        case KvKind::FP8_BF16Q: return split_b<D, true, true>(a, bs, gp, wpc, st);
+    }
     return hipErrorInvalidValue;
 }
 
-hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, bool bf16, int* waves_per_cu) {
-    return split_any(nullptr, head_dim, block_size, group_pad, bf16, waves_per_cu, nullptr);
+static hipError_t split_any(const DecodeArgs* a, int head_dim, int bs, int gp, KvKind kind, int* wpc, hipStream_t st) {
+    if (head_dim == 128) return split_t<128>(a, bs, gp, kind, wpc, st);
+    if (head_dim == 64) return split_t<64>(a, bs, gp, kind, wpc, st);
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
+hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu) {
+    return split_any(nullptr, head_dim, block_size, group_pad, kind, waves_per_cu, nullptr);
+}
+
+hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream) {
     if (a.num_waves < kWaves || a.num_waves % kWaves) return hipErrorInvalidValue;
-    return split_any(&a, head_dim, block_size, group_pad, bf16, nullptr, stream);
+    if (kind == KvKind::FP8_BF16Q && (!a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
+    return split_any(&a, head_dim, block_size, group_pad, kind, nullptr, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

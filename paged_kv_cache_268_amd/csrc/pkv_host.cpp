@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "pkv.h"
+#include "pkv_fp8.h"
 #include "pkv_kernels.h"
 #include "pkv_tier.h"
 
@@ -60,6 +61,11 @@ struct pkv_pool {
     pkv_pool_desc d{};
     void* k_cache = nullptr;
     void* v_cache = nullptr;
+    // 8-bit pools: per-(block, kv head) scales and the default scales of new blocks (device).
+    float* k_scale = nullptr;
+    float* v_scale = nullptr;
+    const float* k_init = nullptr;
+    const float* v_init = nullptr;
 
     // Free list: a stack (allocation pops the back).  Removing a block from
     // the middle (kv_seq_import) leaves a tombstone (-1) so the order of the
@@ -175,8 +181,8 @@ int kv_block_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cache
         return fail(PKV_EUNSUPPORTED, "block_size %d (16 or 32)", d.block_size);
     if (d.head_dim != 64 && d.head_dim != 128)
         return fail(PKV_EUNSUPPORTED, "head_dim %d (64 or 128)", d.head_dim);
-    if (d.kv_dtype != PKV_F16 && d.kv_dtype != PKV_BF16)
-        return fail(PKV_EUNSUPPORTED, "kv_dtype %d (PKV_F16 or PKV_BF16)", d.kv_dtype);
+    if (d.kv_dtype != PKV_F16 && d.kv_dtype != PKV_BF16 && d.kv_dtype != PKV_FP8_E4M3)
+        return fail(PKV_EUNSUPPORTED, "kv_dtype %d (PKV_F16, PKV_BF16 or PKV_FP8_E4M3)", d.kv_dtype);
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
         return fail(PKV_EINVAL, "k_cache / v_cache must be 16-byte aligned");
     std::vector<uint8_t> seen(d.num_blocks, 0);
@@ -392,10 +398,26 @@ static int ensure_ring(pkv_pool* p) {
     return PKV_OK;
 }
 
+int kv_block_pool_set_fp8_scales(pkv_pool* p, float* k_scale, float* v_scale, const float* k_init,
+                                 const float* v_init) {
+    if (!p) return fail(PKV_EINVAL, "kv_block_pool_set_fp8_scales: null pool");
+    if (p->d.kv_dtype != PKV_FP8_E4M3) return fail(PKV_EINVAL, "kv_block_pool_set_fp8_scales: not an 8-bit pool");
+    if (!k_scale || !v_scale || !k_init || !v_init || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+        !aligned(k_init, 4) || !aligned(v_init, 4))
+        return fail(PKV_EINVAL, "kv_block_pool_set_fp8_scales: null or misaligned pointer");
+    p->k_scale = k_scale;
+    p->v_scale = v_scale;
+    p->k_init = k_init;
+    p->v_init = v_init;
+    return PKV_OK;
+}
+
 int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new, const void* v_new,
               int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream) {
     if (!p) return fail(PKV_EINVAL, "kv_append: null pool");
     if (n == 0) return PKV_OK;
+    const bool kv8 = p->d.kv_dtype == PKV_FP8_E4M3;
+    if (kv8 && !p->k_scale) return fail(PKV_EINVAL, "kv_append: 8-bit pool without scales (kv_block_pool_set_fp8_scales)");
     if (!k_new || !v_new || !block_tables || !context_lens || !p->k_cache || !p->v_cache)
         return fail(PKV_EINVAL, "kv_append: null device pointer");
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
@@ -425,6 +447,11 @@ int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new,
     a.head_dim = p->d.head_dim;
     a.block_size = p->d.block_size;
     a.table_stride = p->d.max_blocks_per_seq;
+    a.kv8 = kv8 ? 1 : 0;
+    a.k_scale = p->k_scale;
+    a.v_scale = p->v_scale;
+    a.k_init = p->k_init;
+    a.v_init = p->v_init;
     pkv::ArgItems inl;
     const bool small = n <= pkv::kArgItems;
     if (small)
@@ -477,6 +504,8 @@ int kv_write_tables(pkv_pool* p, int32_t* block_tables, int32_t* context_lens, p
 int kv_block_pool_attach_host_tier(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host) {
     if (!p || !k_host || !v_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: null argument");
     if (p->num_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: the pool already has a host tier");
+    if (p->d.kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_EUNSUPPORTED, "kv_block_pool_attach_host_tier: 8-bit pools have no host tier (their scales do not move)");
     if (num_host_blocks < 1) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: %d host blocks", num_host_blocks);
     if (!aligned(k_host, 16) || !aligned(v_host, 16))
         return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers must be 16-byte aligned");
@@ -656,6 +685,38 @@ int kv_seq_restore(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv_stream_t 
     return launch_moves(p, c, k, false, (hipStream_t)stream);
 }
 
+int kv_quantize_fp8(int32_t n, const int32_t* items, const void* src_k, const void* src_v, int32_t src_dtype,
+                    void* dst_k, void* dst_v, float* k_scale, float* v_scale, int32_t num_kv_heads,
+                    int32_t block_size, int32_t head_dim, pkv_stream_t stream) {
+    if (n < 0) return fail(PKV_EINVAL, "kv_quantize_fp8: n = %d", n);
+    if (n == 0) return PKV_OK;
+    if (!items || !src_k || !src_v || !dst_k || !dst_v || !k_scale || !v_scale)
+        return fail(PKV_EINVAL, "kv_quantize_fp8: null pointer");
+    if (src_dtype != PKV_F16 && src_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "kv_quantize_fp8: src_dtype %d", src_dtype);
+    if (num_kv_heads < 1 || (block_size != 16 && block_size != 32) || (head_dim != 64 && head_dim != 128))
+        return fail(PKV_EUNSUPPORTED, "kv_quantize_fp8: shape (Hkv %d, block %d, head_dim %d)", num_kv_heads, block_size,
+                    head_dim);
+    if (!aligned(items, 4) || !aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 8) || !aligned(dst_v, 8) ||
+        !aligned(k_scale, 4) || !aligned(v_scale, 4))
+        return fail(PKV_EINVAL, "kv_quantize_fp8: misaligned pointer");
+    pkv::QuantArgs a{};
+    a.src_k = src_k;
+    a.src_v = src_v;
+    a.dst_k = static_cast<uint8_t*>(dst_k);
+    a.dst_v = static_cast<uint8_t*>(dst_v);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.items = items;
+    a.n = n;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.head_dim = head_dim;
+    a.src_bf16 = src_dtype == PKV_BF16;
+    hipError_t e = pkv::launch_quantize_fp8(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "kv_quantize_fp8 launch");
+    return PKV_OK;
+}
+
 int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t table_stride, int32_t table_width,
                        const int32_t* context_lens, int32_t num_blocks, int32_t block_size) {
     if (n_seqs < 0 || (n_seqs > 0 && (!block_tables || !context_lens)) || block_size <= 0 ||
@@ -695,7 +756,7 @@ struct Plan {
     int32_t max_seg = 0;
     int32_t num_waves = 0;                  // resolved grid size (0 until resolved)
     int32_t group_pad = 0;
-    bool bf16 = false;
+    pkv::KvKind kind = pkv::KvKind::F16;
     int32_t out_kind = pkv::kOutF32;
     size_t hdr_bytes = 0, out_bytes = 0, ws_bytes = 0;
 };
@@ -714,8 +775,12 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
     if (d->head_dim != 64 && d->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
     if (d->block_size != 16 && d->block_size != 32)
         return fail(PKV_EUNSUPPORTED, "block_size %d (16 or 32)", d->block_size);
-    if (d->kv_dtype != PKV_F16 && d->kv_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "kv_dtype %d", d->kv_dtype);
-    if (d->q_dtype != d->kv_dtype) return fail(PKV_EUNSUPPORTED, "q_dtype must equal kv_dtype");
+    if (d->kv_dtype == PKV_FP8_E4M3) {
+        if (d->q_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "8-bit K/V needs a bf16 query");
+    } else {
+        if (d->kv_dtype != PKV_F16 && d->kv_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "kv_dtype %d", d->kv_dtype);
+        if (d->q_dtype != d->kv_dtype) return fail(PKV_EUNSUPPORTED, "q_dtype must equal kv_dtype");
+    }
     if (d->out_dtype == PKV_F32)
         pl->out_kind = pkv::kOutF32;
     else if (d->out_dtype == d->q_dtype)
@@ -743,7 +808,9 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
     if ((int64_t)d->num_seqs * d->num_kv_heads * per_seq >= (int64_t)1 << 30)
         return fail(PKV_EUNSUPPORTED, "too many tiles in one call (num_seqs x kv heads x tiles >= 2^30)");
     pl->group_pad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    pl->bf16 = d->kv_dtype == PKV_BF16;
+    pl->kind = d->kv_dtype == PKV_FP8_E4M3 ? pkv::KvKind::FP8_BF16Q
+             : d->kv_dtype == PKV_BF16    ? pkv::KvKind::BF16
+                                          : pkv::KvKind::F16;
     const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_seg;
     pl->hdr_bytes = up256(sizeof(int32_t) * (3 + (size_t)d->num_seqs));
     pl->out_bytes = up256(rows * d->head_dim * sizeof(float));
@@ -757,7 +824,7 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
 int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
     int64_t nw = d->num_waves;
     if (nw == 0) {
-        static int cache[4][2][4][2][64];          // [D][bs][gp][bf16][device] -> waves per CU
+        static int cache[2][2][4][3][64];          // [D][bs][gp][kv kind][device] -> waves per CU
         static int cus[64];
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -765,9 +832,9 @@ int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
         if (dev < 0 || dev >= 64) return fail(PKV_EUNSUPPORTED, "device index %d", dev);
         const int di = d->head_dim == 128 ? 1 : 0, bi = d->block_size == 32 ? 1 : 0;
         const int gi = pl->group_pad == 1 ? 0 : pl->group_pad == 2 ? 1 : pl->group_pad == 4 ? 2 : 3;
-        int& wpc = cache[di][bi][gi][pl->bf16 ? 1 : 0][dev];
+        int& wpc = cache[di][bi][gi][(int)pl->kind][dev];
         if (wpc == 0) {
-            e = pkv::split_waves_per_cu(d->head_dim, d->block_size, pl->group_pad, pl->bf16, &wpc);
+            e = pkv::split_waves_per_cu(d->head_dim, d->block_size, pl->group_pad, pl->kind, &wpc);
             if (e != hipSuccess) return fail_hip(e, "occupancy query");
         }
         if (cus[dev] == 0) {
@@ -855,12 +922,19 @@ size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
     return pl.ws_bytes;
 }
 
-int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                               float* lse, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, pkv_stream_t stream, bool fp8_call) {
     Plan pl;
     int rc = resolve(d, &pl);
     if (rc) return rc;
+    const bool kv8 = pl.kind == pkv::KvKind::FP8_BF16Q;
+    if (kv8 != fp8_call)
+        return fail(PKV_EINVAL, kv8 ? "kv_dtype PKV_FP8_E4M3 goes through the _fp8 entry points (they take the scales)"
+                                    : "the _fp8 entry points need kv_dtype PKV_FP8_E4M3");
+    if (kv8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+        return fail(PKV_EINVAL, "8-bit K/V: null or misaligned k_scale / v_scale");
     if (d->num_seqs == 0) return PKV_OK;
     rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, workspace, workspace_bytes, true);
     if (rc) return rc;
@@ -871,6 +945,8 @@ int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
+    a.k_scale = kv8 ? k_scale : nullptr;
+    a.v_scale = kv8 ? v_scale : nullptr;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = out;
@@ -888,9 +964,24 @@ int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void
     a.max_seg = pl.max_seg;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
-    hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.bf16, (hipStream_t)stream);
+    hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.kind, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "split kernel launch");
     return PKV_OK;
+}
+
+int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+    return partials_impl(d, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out, lse,
+                         workspace, workspace_bytes, stream, false);
+}
+
+int paged_attn_decode_partials_fp8(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                                   const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, pkv_stream_t stream) {
+    return partials_impl(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out, lse,
+                         workspace, workspace_bytes, stream, true);
 }
 
 int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* out, float* lse,
@@ -927,6 +1018,16 @@ int paged_attn_decode(const pkv_attn_desc* d, const void* q, const void* k_cache
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
     int rc = paged_attn_decode_partials(d, q, k_cache, v_cache, block_tables, context_lens, scale, out, lse,
                                         workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_fp8(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, pkv_stream_t stream) {
+    int rc = paged_attn_decode_partials_fp8(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                                            scale, out, lse, workspace, workspace_bytes, stream);
     if (rc) return rc;
     return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
 }

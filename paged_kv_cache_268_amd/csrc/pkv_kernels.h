@@ -13,10 +13,15 @@ constexpr int kOutF32 = 0, kOutF16 = 1, kOutBF16 = 2;
 constexpr int kMaxSeqs = 4096;   // sequences per decode call (prefix of tile counts kept in LDS)
 constexpr int kTileTokens = 16;  // tokens per tile of the split
 
+// K/V storage and query type of a decode call.
+enum class KvKind { F16, BF16, FP8_BF16Q };   // FP8_BF16Q: OCP E4M3 K/V with scales, bf16 q
+
 struct DecodeArgs {
     const void* q;
     const void* k_cache;
     const void* v_cache;
+    const float* k_scale;    // [num_blocks][Hkv] scales of 8-bit K (null for 16-bit K/V)
+    const float* v_scale;
     const int32_t* block_tables;
     const int32_t* context_lens;
     void* out;
@@ -80,12 +85,19 @@ struct AppendArgs {
     int32_t head_dim;
     int32_t block_size;
     int32_t table_stride;
+    // 8-bit (E4M3) pools: new rows (bf16) are quantised with their block's
+    // scale; a block started by this call takes the default scales.
+    int32_t kv8;
+    float* k_scale;              // [num_blocks][Hkv]
+    float* v_scale;
+    const float* k_init;         // [Hkv] default scales of new blocks
+    const float* v_init;
 };
 
-hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, bool bf16,
+hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream);
 // Resident waves per CU of the split kernel instance (occupancy query).
-hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, bool bf16, int* waves_per_cu);
+hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 // items_in_args: a.n <= kArgItems and `inl` holds the items (copy-on-write
 // still reads a.items, in the separate copy launch).

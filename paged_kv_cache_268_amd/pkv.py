@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOMEM, PKV_EUNSUPPORTED, PKV_EHIP, PKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
-PKV_F16, PKV_BF16, PKV_F32 = 0, 1, 2
+PKV_F16, PKV_BF16, PKV_F32, PKV_FP8_E4M3 = 0, 1, 2, 3
 
 # Every entry point include/pkv.h declares.
 EXPORTS = (
@@ -24,7 +24,8 @@ EXPORTS = (
     "kv_block_pool_create", "kv_block_pool_destroy", "kv_seq_add", "kv_seq_import", "kv_seq_fork",
     "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_write_tables",
     "kv_validate_tables", "kv_block_pool_attach_host_tier", "kv_seq_offload", "kv_seq_restore",
-    "kv_host_tier_stats", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
+    "kv_host_tier_stats", "kv_block_pool_set_fp8_scales", "kv_quantize_fp8", "paged_attn_decode_fp8",
+    "paged_attn_decode_partials_fp8", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
 )
 
@@ -79,6 +80,12 @@ def load(path: str = LIB_PATH):
         "kv_seq_offload": ([P, I32, P, I32, P], ctypes.c_int),
         "kv_seq_restore": ([P, I32, P, P], ctypes.c_int),
         "kv_host_tier_stats": ([P, PI32, I32, PI32], ctypes.c_int),
+        "kv_block_pool_set_fp8_scales": ([P, P, P, P, P], ctypes.c_int),
+        "kv_quantize_fp8": ([I32, P, P, P, I32, P, P, P, P, I32, I32, I32, P], ctypes.c_int),
+        "paged_attn_decode_fp8": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P],
+                                  ctypes.c_int),
+        "paged_attn_decode_partials_fp8": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, ctypes.c_float, P, P, P,
+                                            SZ, P], ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], SZ),
@@ -122,8 +129,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def dtype_code(t) -> int:
+    """Library dtype of a tensor; uint8 storage means E4M3 codes."""
     import torch
-    return {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.float32: PKV_F32}[t.dtype]
+    return {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16, torch.float32: PKV_F32,
+            torch.uint8: PKV_FP8_E4M3}[t.dtype]
 
 
 def _i32(a) -> np.ndarray:
@@ -135,9 +144,11 @@ def _i32(a) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def attn_desc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, table_stride,
-              max_context_len, partition_size=0, dtype=PKV_BF16, out_dtype=PKV_F32, num_waves=0) -> AttnDesc:
+              max_context_len, partition_size=0, dtype=PKV_BF16, out_dtype=PKV_F32, num_waves=0,
+              kv_dtype=None) -> AttnDesc:
     return AttnDesc(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, table_stride,
-                    max_context_len, partition_size, dtype, dtype, out_dtype, num_waves)
+                    max_context_len, partition_size, dtype, dtype if kv_dtype is None else kv_dtype, out_dtype,
+                    num_waves)
 
 
 def desc_for(q, k_cache, block_tables, max_context_len, partition_size=0, out_dtype=None, num_waves=0) -> AttnDesc:
@@ -146,7 +157,7 @@ def desc_for(q, k_cache, block_tables, max_context_len, partition_size=0, out_dt
     assert D == D2
     od = PKV_F32 if out_dtype is None else out_dtype
     return attn_desc(B, Hq, Hkv, D, bs, NB, block_tables.stride(0), max_context_len, partition_size,
-                     dtype_code(q), od, num_waves)
+                     dtype_code(q), od, num_waves, kv_dtype=dtype_code(k_cache))
 
 
 def partition_size(desc: AttnDesc) -> int:
@@ -214,6 +225,41 @@ def decode_partials(desc, q, k_cache, v_cache, block_tables, context_lens, scale
                                             _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale),
                                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                             _stream(stream)))
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale: float,
+               max_context_len: int, *, out=None, lse=None, partition_size: int = 0, workspace=None, stream=None,
+               out_dtype=None, num_waves: int = 0, desc: Optional[AttnDesc] = None):
+    """paged_attn_decode_fp8: k_cache / v_cache uint8 E4M3 codes, k_scale / v_scale float [NB][Hkv]."""
+    import torch
+    if desc is None:
+        od = out_dtype if out_dtype is not None else (dtype_code(out) if out is not None else PKV_F32)
+        desc = desc_for(q, k_cache, block_tables, max_context_len, partition_size, od, num_waves)
+    if out is None:
+        tdt = {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16}[desc.out_dtype]
+        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    check(load().paged_attn_decode_fp8(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale),
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_partials_fp8(desc, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out, lse,
+                        workspace, stream=None):
+    check(load().paged_attn_decode_partials_fp8(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                                ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                workspace.numel(), _stream(stream)))
+
+
+def quantize_fp8(items, src_k, src_v, dst_k, dst_v, k_scale, v_scale, stream=None):
+    """kv_quantize_fp8: items device int32 [n][3] (source block, destination block, used rows)."""
+    n = items.shape[0]
+    NB, Hkv, bs, D = src_k.shape
+    check(load().kv_quantize_fp8(n, _ptr(items), _ptr(src_k), _ptr(src_v), dtype_code(src_k), _ptr(dst_k),
+                                 _ptr(dst_v), _ptr(k_scale), _ptr(v_scale), Hkv, bs, D, _stream(stream)))
 
 
 def merge(desc, context_lens, out, lse, workspace, stream=None):
@@ -319,6 +365,12 @@ class BlockPool:
 
     def write_tables(self, block_tables, context_lens, stream=None):
         check(self.lib.kv_write_tables(self.handle, _ptr(block_tables), _ptr(context_lens), _stream(stream)))
+
+    def set_fp8_scales(self, k_scale, v_scale, k_init, v_init):
+        """8-bit pools: device scales [NB][Hkv] and default scales of new blocks [Hkv]."""
+        check(self.lib.kv_block_pool_set_fp8_scales(self.handle, _ptr(k_scale), _ptr(v_scale), _ptr(k_init),
+                                                    _ptr(v_init)))
+        self._fp8_scales = (k_scale, v_scale, k_init, v_init)
 
     # -- host tier ----------------------------------------------------------
     def attach_host_tier(self, num_host_blocks: int, k_host, v_host):

@@ -295,3 +295,36 @@ def bits16(t) -> np.ndarray:
     """Raw 16-bit storage of a fp16/bf16 tensor, as a contiguous uint16 array."""
     import torch
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def make_fp8_cache(wl: DecodeWorkload, device="cpu", poison: bool = False, seed_offset: int = 0,
+                   scale_log2=(-9.0, -6.0)):
+    """An 8-bit K/V cache for the workload's pool: (k_codes, v_codes uint8 [NB][Hkv][bs][D],
+    k_scale, v_scale float32 [NB][Hkv]).
+
+    Codes are drawn uniformly over the 254 finite E4M3 codes (0x7F and 0xFF, the
+    NaN codes, are skipped); each (block, kv head) scale is 2^u with u uniform in
+    scale_log2.  With poison=True every unused slot holds the NaN code 0x7F.
+    """
+    import torch
+    base = (wl.seed * 7919 + seed_offset + 101) & 0x7FFFFFFF
+    gen = torch.Generator(device=device)
+    shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    out = []
+    for i in range(2):
+        gen.manual_seed(base + i)
+        c = torch.randint(0, 254, shape, generator=gen, device=device, dtype=torch.int16)
+        c = c + (c >= 127).to(torch.int16)               # 0..126, 128..254
+        out.append(c.to(torch.uint8))
+    scales = []
+    for i in range(2):
+        gen.manual_seed(base + 10 + i)
+        u = torch.rand((wl.num_blocks, wl.num_kv_heads), generator=gen, device=device, dtype=torch.float32)
+        scales.append(torch.exp2(scale_log2[0] + (scale_log2[1] - scale_log2[0]) * u))
+    kc, vc = out
+    if poison:
+        used = torch.from_numpy(used_slot_mask(wl)).to(device)
+        mask = (~used)[:, None, :, None].expand_as(kc)
+        kc.masked_fill_(mask, 0x7F)
+        vc.masked_fill_(mask, 0x7F)
+    return kc, vc, scales[0], scales[1]
