@@ -59,6 +59,8 @@ class OracleLib:
         lib.oracle_fp8_encode_array.restype = None
         lib.oracle_quantize_fp8.argtypes = [P, i, i, i, i, P, P]
         lib.oracle_quantize_fp8.restype = None
+        lib.oracle_paged_prefill.argtypes = [i, i, i, i, i, i, i, i, i, P, P, P, P, P, P, ctypes.c_float, P, P, i]
+        lib.oracle_paged_prefill.restype = i
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i
         lib.oracle_decode_value.argtypes = [ctypes.c_uint16, i]
@@ -131,6 +133,35 @@ class OracleLib:
         return out, lse
 
 
+    def paged_prefill(self, q_bits, k_bits, v_bits, block_tables, context_lens, cu_q, scale, *,
+                      num_kv_heads, block_size, dtype, nthreads=None, table_width=None):
+        """fp64 chunked-prefill output [total_q][Hq][D] and lse [total_q][Hq] (natural log).
+
+        q_bits [total_q][Hq][D] (16-bit storage): rows cu_q[s] .. cu_q[s+1]-1 are
+        sequence s's chunk, the last tokens of its context_lens[s]-token context.
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+        tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+        cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+        T, Hq, D = q_bits.shape
+        B = ctx.shape[0]
+        assert cu.shape == (B + 1,) and cu[-1] == T and tables.shape[0] == B
+        NB = k_bits.shape[0]
+        out = np.empty((T, Hq, D), dtype=np.float64)
+        lse = np.empty((T, Hq), dtype=np.float64)
+        width = tables.shape[1] if table_width is None else table_width
+        nt = self.max_threads() if nthreads is None else int(nthreads)
+        rc = self.lib.oracle_paged_prefill(B, Hq, num_kv_heads, D, block_size, NB, tables.shape[1], width, dtype,
+                                           _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(tables), _ptr(ctx),
+                                           _ptr(cu), ctypes.c_float(scale), _ptr(out), _ptr(lse), nt)
+        if rc != 0:
+            raise ValueError(f"oracle_paged_prefill failed with status {rc}")
+        return out, lse
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -155,6 +186,10 @@ def decode_value(bits: int, dtype: int) -> float:
 
 def paged_decode(*args, **kw):
     return default().paged_decode(*args, **kw)
+
+
+def paged_prefill(*args, **kw):
+    return default().paged_prefill(*args, **kw)
 
 
 def fp8_encode(x):

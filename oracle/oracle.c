@@ -285,6 +285,49 @@ int oracle_paged_decode(
                                   block_tables, context_lens, tok_lo, tok_hi, scale, out, lse, nthreads);
 }
 
+/* Chunked prefill ("架构解构：推理引擎的四层抽象", FlashAttention section: many
+ * queries per sequence over the paged context, causal).  Sequence s has
+ * context_lens[s] = n tokens in the cache, the last m = cu_q[s+1] - cu_q[s] of
+ * which are this chunk; chunk query i (row cu_q[s] + i of q and out) sits at
+ * position n - m + i and attends to the tokens at positions 0 .. n - m + i.
+ * That is decode attention over a context of n - m + i + 1 tokens, so each
+ * query row is computed by oracle_paged_decode_kv with that length.
+ *   q, out : [total_q][Hq][D];  lse : [total_q][Hq] (nullable)
+ * Returns -1 if some m exceeds its n or cu_q is not non-decreasing from 0. */
+int oracle_paged_prefill(
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, int table_stride, int table_width, int dtype,
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_q,
+    float scale, double* out, double* lse, int nthreads)
+{
+    if (num_seqs < 0 || table_width > table_stride || cu_q[0] != 0) return -1;
+    const int total = cu_q[num_seqs];
+    for (int s = 0; s < num_seqs; ++s) {
+        const int m = cu_q[s + 1] - cu_q[s];
+        if (m < 0 || m > context_lens[s]) return -1;
+    }
+    if (total == 0) return 0;
+    int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)total * table_stride);
+    int32_t* lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)total);
+    if (!rows || !lens) { free(rows); free(lens); return -2; }
+    for (int s = 0; s < num_seqs; ++s) {
+        const int n = context_lens[s], m = cu_q[s + 1] - cu_q[s];
+        for (int i = 0; i < m; ++i) {
+            const int r = cu_q[s] + i;
+            memcpy(rows + (int64_t)r * table_stride, block_tables + (int64_t)s * table_stride,
+                   sizeof(int32_t) * (size_t)table_stride);
+            lens[r] = n - m + i + 1;
+        }
+    }
+    const int rc = oracle_paged_decode_kv(total, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                          table_stride, table_width, dtype, dtype, q, k_cache, v_cache, NULL, NULL,
+                                          rows, lens, NULL, NULL, scale, out, lse, nthreads);
+    free(rows);
+    free(lens);
+    return rc;
+}
+
 /* Threads OpenMP would use for nthreads <= 0 requests (reported by the bench). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -402,6 +402,69 @@ def pin_fp8_equals_exact_bf16(lib):
     assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
 
 
+# ---------------------------------------------------------------------------
+# Chunked prefill pins
+# ---------------------------------------------------------------------------
+
+def _prefill(lib, wl, qb, kb, vb, cu):
+    return lib.paged_prefill(qb, kb, vb, wl.block_tables, wl.context_lens, cu, wl.scale,
+                             num_kv_heads=wl.num_kv_heads, block_size=wl.block_size, dtype=_dt(wl))
+
+
+def _chunk_q(wl, m, seed):
+    """q rows for chunks of m[s] tokens per sequence, and cu_q."""
+    m = np.asarray(m)
+    cu = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
+    x = np.random.default_rng(seed).standard_normal((int(cu[-1]), wl.num_q_heads, wl.head_dim))
+    if wl.dtype == "f16":
+        qb = x.astype(np.float16).view(np.uint16)
+    else:
+        qb = to_bits((x.astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32), "bf16")
+    return qb, cu
+
+
+def pin_prefill_full_vs_sdpa_causal(lib):
+    """Whole-sequence prefill (the chunk is the whole context) against torch's causal
+    scaled_dot_product_attention in fp64 on the gathered K/V."""
+    for dtype, Hq, Hkv, D in (("f16", 4, 4, 64), ("bf16", 8, 2, 128)):
+        wl, _, kb, vb = random_case(B=2, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, ctx=(37, 70), seed=21)
+        qb, cu = _chunk_q(wl, wl.context_lens, 22)
+        out, _ = _prefill(lib, wl, qb, kb, vb, cu)
+        q = from_bits(qb, dtype); k = from_bits(kb, dtype); v = from_bits(vb, dtype)
+        Gq = Hq // Hkv
+        for s in range(wl.num_seqs):
+            n = int(wl.context_lens[s])
+            for h in range(Hq):
+                K = torch.from_numpy(gather_rows(wl, k, s, h // Gq))[None, None]
+                V = torch.from_numpy(gather_rows(wl, v, s, h // Gq))[None, None]
+                Q = torch.from_numpy(q[cu[s]:cu[s] + n, h])[None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    Q, K, V, is_causal=True, scale=float(np.float32(wl.scale)))
+                assert np.allclose(out[cu[s]:cu[s] + n, h], ref[0, 0].numpy(), rtol=0, atol=1e-12), (dtype, s, h)
+
+
+def pin_prefill_chunk_is_tail_of_full(lib):
+    """A chunk of the last m tokens gives exactly the last m rows of the whole-sequence prefill,
+    and its last row is decode over the whole context."""
+    wl, _, kb, vb = random_case(B=3, Hq=8, Hkv=2, D=64, dtype="bf16", ctx=(5, 40, 90), seed=23)
+    n = wl.context_lens
+    qf, cuf = _chunk_q(wl, n, 24)
+    full, full_lse = _prefill(lib, wl, qf, kb, vb, cuf)
+    m = np.array([2, 17, 33])
+    rows = np.concatenate([np.arange(cuf[s] + n[s] - m[s], cuf[s] + n[s]) for s in range(3)])
+    cu = np.concatenate([[0], np.cumsum(m)]).astype(np.int32)
+    part, part_lse = _prefill(lib, wl, qf[rows], kb, vb, cu)
+    assert np.array_equal(part, full[rows]) and np.array_equal(part_lse, full_lse[rows])
+    last = np.array([cu[s + 1] - 1 for s in range(3)])
+    dec, dec_lse = run(lib, wl, qf[rows][last], kb, vb)
+    assert np.array_equal(part[last], dec) and np.array_equal(part_lse[last], dec_lse)
+    try:
+        _prefill(lib, wl, qf[:10], kb, vb, np.array([0, 6, 6, 10], np.int32))   # 6 > n[0] = 5
+    except ValueError:
+        return
+    raise AssertionError("a chunk longer than its context was accepted")
+
+
 ALL_PINS = [
     pin_decode_f16_all_bits, pin_decode_bf16_all_bits, pin_ctx1_returns_v,
     pin_equal_scores_mean, pin_equal_keys_mean, pin_two_token_closed_form,
@@ -410,4 +473,5 @@ ALL_PINS = [
     pin_scale_q_tradeoff, pin_torch_sdpa, pin_brute_force, pin_empty_context,
     pin_bad_table_rejected, pin_decode_fp8_all_codes, pin_fp8_encode_matches_torch,
     pin_fp8_encode_saturates, pin_fp8_quantize_bound, pin_fp8_equals_exact_bf16,
+    pin_prefill_full_vs_sdpa_causal, pin_prefill_chunk_is_tail_of_full,
 ]

@@ -43,6 +43,9 @@ MUTANTS = [
     ("fp8-ties-odd", "(c & 1) == 0", "(c & 1) == 1"),
     ("fp8-quant-scale", "amax / 448.0f", "amax / 480.0f"),
     ("fp8-quant-tail", "if (i < ntok * D) {", "if (i <= ntok * D) {"),
+    ("prefill-no-causal-mask", "lens[r] = n - m + i + 1;", "lens[r] = n;"),
+    ("prefill-position-from-start", "lens[r] = n - m + i + 1;", "lens[r] = i + 1;"),
+    ("prefill-first-table-row", "block_tables + (int64_t)s * table_stride,", "block_tables + (int64_t)0 * table_stride,"),
 ]
 
 
