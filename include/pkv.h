@@ -342,6 +342,48 @@ int paged_attn_decode_partials_fp8(const pkv_attn_desc* desc, const void* q, con
                                    float scale, void* out, float* lse, void* workspace,
                                    size_t workspace_bytes, pkv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Chunked prefill attention ("架构解构：推理引擎的四层抽象", FlashAttention
+ * section: tiled attention with an online softmax over K/V reached through
+ * the block table).  Many query tokens per sequence, causal.
+ *
+ *   q            : device [total_q][num_q_heads][head_dim], q_dtype
+ *   k_cache,
+ *   v_cache      : device [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype (= q_dtype)
+ *   block_tables : device int32, row s at block_tables + s * table_stride
+ *   context_lens : device int32 [num_seqs]: tokens of sequence s in the cache,
+ *                  this chunk's included (its K/V must already be written)
+ *   cu_seqlens_q : device int32 [num_seqs + 1], non-decreasing from 0 to total_q:
+ *                  rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q and out are
+ *                  sequence s's chunk, m_s of them, m_s <= context_lens[s]
+ *   out          : device [total_q][num_q_heads][head_dim], out_dtype
+ *   lse          : device float [total_q][num_q_heads] or NULL (natural log)
+ * Chunk row i of sequence s sits at position context_lens[s] - m_s + i and
+ * attends to the tokens at positions 0 .. that position: out = softmax(scale *
+ * q . K) V over them, fp32 accumulation.  No workspace; asynchronous on
+ * `stream`.  A row whose position would be negative (m_s > context_lens[s],
+ * outside the contract) gets out = 0, lse = -inf.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_prefill_desc {
+    int32_t num_seqs;            /* at most 4096 per call */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;        /* divides num_q_heads */
+    int32_t head_dim;            /* 64 or 128 */
+    int32_t block_size;          /* 16 or 32 */
+    int32_t num_blocks;          /* for documentation and validation only */
+    int32_t table_stride;        /* int32 elements between block-table rows */
+    int32_t total_q;             /* rows of q / out (= cu_seqlens_q[num_seqs]) */
+    int32_t max_context_len;     /* host upper bound of context_lens[] */
+    int32_t q_dtype;             /* PKV_F16 / PKV_BF16 */
+    int32_t kv_dtype;            /* equal to q_dtype */
+    int32_t out_dtype;           /* PKV_F32 or q_dtype */
+} pkv_prefill_desc;
+
+int paged_attn_prefill(const pkv_prefill_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* cu_seqlens_q, float scale,
+                       void* out, float* lse, pkv_stream_t stream);
+
 /* Debug: the segments of the split for host context lengths, in (seq, kv
  * head, slot) order, as rows of 5 int32: seq, kv_head, slot, tok_lo, tok_hi.
  * Writes min(count, cap) rows to items_out (nullable) and the count to *n_out.

@@ -23,6 +23,7 @@
 #include "pkv.h"
 #include "pkv_fp8.h"
 #include "pkv_kernels.h"
+#include "pkv_prefill.h"
 #include "pkv_tier.h"
 
 namespace {
@@ -1030,6 +1031,66 @@ int paged_attn_decode_fp8(const pkv_attn_desc* d, const void* q, const void* k_c
                                             scale, out, lse, workspace, workspace_bytes, stream);
     if (rc) return rc;
     return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_prefill(const pkv_prefill_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_seqlens_q,
+                       float scale, void* out, float* lse, pkv_stream_t stream) {
+    if (!d) return fail(PKV_EINVAL, "paged_attn_prefill: null descriptor");
+    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_q < 0 || d->max_context_len < 0)
+        return fail(PKV_EINVAL, "paged_attn_prefill: bad sizes");
+    if (d->num_seqs > pkv::kPrefillMaxSeqs)
+        return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: num_seqs %d > %d", d->num_seqs, pkv::kPrefillMaxSeqs);
+    if (d->num_q_heads % d->num_kv_heads)
+        return fail(PKV_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d", d->num_q_heads, d->num_kv_heads);
+    if (d->head_dim != 64 && d->head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+    if (d->block_size != 16 && d->block_size != 32)
+        return fail(PKV_EUNSUPPORTED, "block_size %d (16 or 32)", d->block_size);
+    if ((d->q_dtype != PKV_F16 && d->q_dtype != PKV_BF16) || d->kv_dtype != d->q_dtype)
+        return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: q_dtype %d / kv_dtype %d (both PKV_F16 or both PKV_BF16)",
+                    d->q_dtype, d->kv_dtype);
+    int out_kind;
+    if (d->out_dtype == PKV_F32)
+        out_kind = pkv::kOutF32;
+    else if (d->out_dtype == d->q_dtype)
+        out_kind = d->q_dtype == PKV_BF16 ? pkv::kOutBF16 : pkv::kOutF16;
+    else
+        return fail(PKV_EUNSUPPORTED, "out_dtype must be PKV_F32 or equal q_dtype");
+    const int64_t need_w = ceil_div(d->max_context_len, d->block_size);
+    if (d->table_stride < need_w)
+        return fail(PKV_EINVAL, "table_stride %d < ceil(max_context_len / block_size) = %lld", d->table_stride,
+                    (long long)need_w);
+    if (d->num_seqs == 0 || d->total_q == 0) return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_seqlens_q || !out)
+        return fail(PKV_EINVAL, "paged_attn_prefill: null pointer");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4) || !aligned(out, out_kind == pkv::kOutF32 ? 16 : 8) ||
+        (lse && !aligned(lse, 4)))
+        return fail(PKV_EINVAL, "paged_attn_prefill: misaligned pointer (q, caches 16 bytes; out 16 (fp32) or 8)");
+    // Query tiles: sum over s of ceil(m_s / 64) <= total_q / 64 + num_seqs.
+    const int64_t tiles = ceil_div(d->total_q, pkv::kPrefillQ) + d->num_seqs;
+    if (tiles * d->num_q_heads > 0x7FFFFFFF) return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: grid too large");
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu_q = cu_seqlens_q;
+    a.out = out;
+    a.lse = lse;
+    a.scale = scale;
+    a.num_seqs = d->num_seqs;
+    a.num_q_heads = d->num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.table_stride = d->table_stride;
+    a.total_q = d->total_q;
+    a.max_context_len = d->max_context_len;
+    a.out_dtype = out_kind;
+    a.grid_tiles = (int32_t)tiles;
+    hipError_t e = pkv::launch_prefill(a, d->head_dim, d->block_size, d->q_dtype == PKV_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "prefill kernel launch");
+    return PKV_OK;
 }
 
 int paged_attn_plan(const pkv_attn_desc* d, const int32_t* context_lens_host, int32_t* items_out, int64_t cap,

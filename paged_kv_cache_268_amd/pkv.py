@@ -25,7 +25,7 @@ EXPORTS = (
     "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_write_tables",
     "kv_validate_tables", "kv_block_pool_attach_host_tier", "kv_seq_offload", "kv_seq_restore",
     "kv_host_tier_stats", "kv_block_pool_set_fp8_scales", "kv_quantize_fp8", "paged_attn_decode_fp8",
-    "paged_attn_decode_partials_fp8", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
+    "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
 )
 
@@ -40,6 +40,12 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_blocks", "block_size", "num_kv_heads", "head_dim", "kv_dtype", "max_seqs",
         "max_blocks_per_seq")]
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks", "table_stride",
+        "total_q", "max_context_len", "q_dtype", "kv_dtype", "out_dtype")]
 
 
 class AttnDesc(ctypes.Structure):
@@ -94,6 +100,7 @@ def load(path: str = LIB_PATH):
         "paged_attn_decode_partials": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P],
                                        ctypes.c_int),
         "paged_attn_merge": ([ctypes.POINTER(AttnDesc), P, P, P, P, SZ, P], ctypes.c_int),
+        "paged_attn_prefill": ([ctypes.POINTER(PrefillDesc), P, P, P, P, P, P, ctypes.c_float, P, P, P], ctypes.c_int),
         "paged_attn_plan": ([ctypes.POINTER(AttnDesc), P, P, I64, ctypes.POINTER(I64)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -260,6 +267,26 @@ def quantize_fp8(items, src_k, src_v, dst_k, dst_v, k_scale, v_scale, stream=Non
     NB, Hkv, bs, D = src_k.shape
     check(load().kv_quantize_fp8(n, _ptr(items), _ptr(src_k), _ptr(src_v), dtype_code(src_k), _ptr(dst_k),
                                  _ptr(dst_v), _ptr(k_scale), _ptr(v_scale), Hkv, bs, D, _stream(stream)))
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, scale: float, max_context_len: int, *,
+            out=None, lse=None, out_dtype=None, stream=None, desc: Optional[PrefillDesc] = None):
+    """paged_attn_prefill.  q [total_q][Hq][D]; cu_seqlens_q device int32 [B + 1].  Returns out."""
+    import torch
+    T, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    assert D == D2
+    if desc is None:
+        od = out_dtype if out_dtype is not None else (dtype_code(out) if out is not None else PKV_F32)
+        desc = PrefillDesc(context_lens.shape[0], Hq, Hkv, D, bs, NB, block_tables.stride(0), T, max_context_len,
+                           dtype_code(q), dtype_code(k_cache), od)
+    if out is None:
+        tdt = {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16}[desc.out_dtype]
+        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    check(load().paged_attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                    _ptr(context_lens), _ptr(cu_seqlens_q), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                    _stream(stream)))
+    return out
 
 
 def merge(desc, context_lens, out, lse, workspace, stream=None):

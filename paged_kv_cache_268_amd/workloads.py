@@ -328,3 +328,31 @@ def make_fp8_cache(wl: DecodeWorkload, device="cpu", poison: bool = False, seed_
         kc.masked_fill_(mask, 0x7F)
         vc.masked_fill_(mask, 0x7F)
     return kc, vc, scales[0], scales[1]
+
+
+def make_prefill_workload(num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int, dtype: str,
+                          prefix_lens, chunk_lens, seed: int, name: str = "prefill"):
+    """A chunked-prefill batch: sequence s has prefix_lens[s] cached tokens and a chunk of
+    chunk_lens[s] new ones (already in the cache); its context is their sum.  Returns the
+    workload and cu_q (int32 [B + 1], the chunk rows of each sequence)."""
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    chk = np.asarray(chunk_lens, dtype=np.int64)
+    wl = make_workload(len(pre), num_q_heads, num_kv_heads, head_dim, block_size, dtype, pre + chk, seed, name=name)
+    cu = np.concatenate([[0], np.cumsum(chk)]).astype(np.int32)
+    return wl, cu
+
+
+def llama3_8b_prefill(seed: int = 2003):
+    """Chunked prefill on the Llama-3-8B GQA shape (32 q / 8 kv heads, head_dim 128, block 16,
+    bf16): 16 sequences, each with a cached prefix drawn uniformly from [0, 3584] tokens and a
+    512-token chunk."""
+    rng = np.random.default_rng(seed)
+    prefix = rng.integers(0, 3585, 16)
+    return make_prefill_workload(32, 8, 128, 16, "bf16", prefix, [512] * 16, seed, name="llama3-8b-chunked-prefill")
+
+
+def make_prefill_q(wl: DecodeWorkload, cu_q, device="cpu", seed_offset: int = 0):
+    """q [total_q][Hq][D] of N(0,1) samples rounded to the workload's dtype."""
+    import torch
+    q = torch.empty((int(cu_q[-1]), wl.num_q_heads, wl.head_dim), dtype=_torch_dtype(wl.dtype), device=device)
+    return fill_normal_(q, (wl.seed * 7919 + seed_offset + 211) & 0x7FFFFFFF)
