@@ -14,8 +14,12 @@
 // once per workgroup (16-byte loads through the block table) into LDS, double
 // buffered: the next tile's loads are in flight while this one is consumed.
 // K sits row-major (rows padded by 16 bytes), V transposed ([d][key], rows
-// padded to 72 bytes).  Keys at or past the context end are written as zeros,
-// never loaded.
+// padded to 72 bytes).  Waves 2-3 load K (four 16-byte pieces per thread);
+// waves 0-1 load V as units of 4 consecutive keys x 8 d values and store, for
+// each d, the 4 keys as one 8-byte word: with 18-dword rows those stores hit
+// every LDS bank once per half wave (2-byte stores of a transposed row would
+// conflict 8- to 16-fold).  Keys at or past the context end are written as
+// zeros, never loaded.
 //
 // Both contractions run on v_mfma_f32_16x16x32 (bf16 or f16 inputs, fp32
 // accumulation):
@@ -95,8 +99,12 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
     constexpr int VROW = kPKeys * 2 + 8;          // bytes per transposed V row (8-byte aligned)
     constexpr int KBUF = kPKeys * KROW, VBUF = D * VROW;
     constexpr int CPR = D / 8;                    // 16-byte pieces per K/V row
-    constexpr int CPT = kPKeys * CPR / kPThreads; // pieces per thread per tile, for K and for V
-    static_assert(CPT * kPThreads == kPKeys * CPR, "tile shape");
+    constexpr int HT = kPThreads / 2;             // threads of the K half and of the V half
+    constexpr int KPT = kPKeys * CPR / HT;        // K pieces per K-half thread
+    constexpr int VU = (kPKeys / 4) * CPR;        // V units (4 keys x 8 d) per tile
+    constexpr int VPT = (VU + HT - 1) / HT;       // V units per V-half thread
+    constexpr int SR = KPT > 4 * VPT ? KPT : 4 * VPT;   // staging registers per thread
+    static_assert(KPT * HT == kPKeys * CPR && VU <= VPT * HT, "tile shape");
     constexpr int LDS = 2 * (KBUF + VBUF);
     static_assert(LDS >= (kPrefillMaxSeqs + 1) * 4, "tile prefix fits the tile buffers");
     __shared__ __align__(16) uint8_t s_mem[LDS];
@@ -181,36 +189,65 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
     const uint4* kg = reinterpret_cast<const uint4*>(a.k_cache);
     const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache);
 
-    auto gload = [&](int kt, uint4 (&kr)[CPT], uint4 (&vr)[CPT]) {
+    // 16-byte piece of token t (d chunk cd), or zeros past the context end.
+    auto fetch = [&](const uint4* base, int t, int cd) {
+        uint4 z = make_uint4(0, 0, 0, 0);
+        if (t < n) {
+            const int32_t blk = table[t / BS];
+            z = base[(((int64_t)blk * Hkv + g) * BS + t % BS) * CPR + cd];
+        }
+        return z;
+    };
+    const bool k_half = wave >= 2;                 // uniform per wave
+    const int ht = tid & (HT - 1);
+    // K half: piece ht + HT c is key (ht + HT c) / CPR, chunk (ht + HT c) % CPR.
+    // V half: unit ht + HT c is keys 4 ((ht + HT c) % 8) .. +3, chunk (ht + HT c) / 8.
+    auto gload = [&](int kt, uint4 (&r)[SR]) {
+        if (k_half) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int piece = tid + c * kPThreads;
-            const int key = piece / CPR, cd = piece % CPR;
-            const int t = kt * kPKeys + key;
-            uint4 zk = make_uint4(0, 0, 0, 0), zv = zk;
-            if (t < n) {
-                const int32_t blk = table[t / BS];
-                const int64_t idx = (((int64_t)blk * Hkv + g) * BS + t % BS) * CPR + cd;
-                zk = kg[idx];
-                zv = vg[idx];
+            for (int c = 0; c < KPT; ++c) {
+                const int piece = ht + HT * c;
+                r[c] = fetch(kg, kt * kPKeys + piece / CPR, piece % CPR);
             }
-            kr[c] = zk;
-            vr[c] = zv;
+        } else {
+#pragma unroll
+            for (int c = 0; c < VPT; ++c) {
+                const int u = ht + HT * c;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    r[4 * c + kk] = u < VU ? fetch(vg, kt * kPKeys + 4 * (u % 8) + kk, u / 8) : make_uint4(0, 0, 0, 0);
+            }
         }
     };
-    auto lstore = [&](int b, const uint4 (&kr)[CPT], const uint4 (&vr)[CPT]) {
-        uint8_t* kb = s_mem + b * KBUF;
-        uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
+    auto lstore = [&](int b, const uint4 (&r)[SR]) {
+        if (k_half) {
+            uint8_t* kb = s_mem + b * KBUF;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int piece = tid + c * kPThreads;
-            const int key = piece / CPR, cd = piece % CPR;
-            *reinterpret_cast<uint4*>(kb + key * KROW + cd * 16) = kr[c];
-            const uint32_t w[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
+            for (int c = 0; c < KPT; ++c) {
+                const int piece = ht + HT * c;
+                *reinterpret_cast<uint4*>(kb + (piece / CPR) * KROW + (piece % CPR) * 16) = r[c];
+            }
+        } else {
+            uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint16_t*>(vb + (cd * 8 + 2 * e) * VROW + key * 2) = (uint16_t)(w[e] & 0xFFFFu);
-                *reinterpret_cast<uint16_t*>(vb + (cd * 8 + 2 * e + 1) * VROW + key * 2) = (uint16_t)(w[e] >> 16);
+            for (int c = 0; c < VPT; ++c) {
+                const int u = ht + HT * c;
+                if (u >= VU) continue;
+                const int q4 = u % 8, cd = u / 8;
+                const uint32_t w0[4] = {r[4 * c].x, r[4 * c].y, r[4 * c].z, r[4 * c].w};
+                const uint32_t w1[4] = {r[4 * c + 1].x, r[4 * c + 1].y, r[4 * c + 1].z, r[4 * c + 1].w};
+                const uint32_t w2[4] = {r[4 * c + 2].x, r[4 * c + 2].y, r[4 * c + 2].z, r[4 * c + 2].w};
+                const uint32_t w3[4] = {r[4 * c + 3].x, r[4 * c + 3].y, r[4 * c + 3].z, r[4 * c + 3].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // d = 8 cd + 2e from the low halves, 8 cd + 2e + 1 from the high halves
+                    const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u),
+                                                __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
+                    const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u),
+                                                __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
+                    *reinterpret_cast<uint2*>(vb + (cd * 8 + 2 * e) * VROW + q4 * 8) = lo;
+                    *reinterpret_cast<uint2*>(vb + (cd * 8 + 2 * e + 1) * VROW + q4 * 8) = hi;
+                }
             }
         }
     };
@@ -268,17 +305,17 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
         }
     };
 
-    uint4 kr[CPT], vr[CPT];
+    uint4 stage[SR];
     if (NT > 0) {
-        gload(0, kr, vr);
-        lstore(0, kr, vr);
+        gload(0, stage);
+        lstore(0, stage);
     }
     __syncthreads();
     for (int kt = 0; kt < NT; ++kt) {
         const int b = kt & 1;
-        if (kt + 1 < NT) gload(kt + 1, kr, vr);
+        if (kt + 1 < NT) gload(kt + 1, stage);
         compute(b, kt);
-        if (kt + 1 < NT) lstore(b ^ 1, kr, vr);
+        if (kt + 1 < NT) lstore(b ^ 1, stage);
         __syncthreads();
     }
 
