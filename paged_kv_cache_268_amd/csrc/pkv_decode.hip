@@ -201,6 +201,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     static_assert(!KV8 || BF16, "8-bit K/V pair with a bf16 query");
     using MfmaIn = typename MfmaType<BF16>::vec;
     using VLoad = typename Pick<KV8, uint2, uint4>::type;   // one lane's 8 V values
+    constexpr int DEPTH = 2;              // tiles in flight per wave
 
     __shared__ int s_pre[kMaxSeqs + 1];
     __shared__ int s_wsum[kWaves];
@@ -428,12 +429,15 @@ paged_decode_split_kernel(DecodeArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         };
 
-        // Two K and two V register buffers: the loads of tile j + 2 are issued
-        // as soon as tile j's K (after QK) or V (after PV) is consumed, so two
-        // tiles stay in flight per wave.  Loads past the window's last tile
-        // re-read that tile (in bounds, served by the cache); a window with an
-        // odd tile count ends with one tile past the segment, which every row
-        // treats as outside the context (weight 0, V never used).  Block ids
+        // DEPTH K and DEPTH V register buffers: the loads of tile j + DEPTH are
+        // issued as soon as tile j's K (after QK) or V (after PV) is consumed,
+        // so DEPTH tiles stay in flight per wave.  (Four tiles in flight for
+        // 8-bit K/V, the same bytes as two 16-bit tiles, measured slower: that
+        // kernel is limited by its per-tile vector work, not by latency.)
+        // Loads past the window's last tile re-read that tile (in bounds,
+        // served by the cache); a window whose tile count is not a multiple
+        // of DEPTH ends with tiles past the segment, which every row treats as
+        // outside the context (weight 0, V never used).  Block ids
         // come 128 tiles at a time, two per lane, read back with v_readlane;
         // with 8-bit K/V each lane also loads the K and V scales of its two
         // blocks (vector loads: they stay in order with the tile loads).
@@ -462,21 +466,21 @@ paged_decode_split_kernel(DecodeArgs a) {
                                                         : __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), i - 64));
             };
             auto tile = [&](int it) { return c0 + min(it, cn - 1); };
-            uint4 ka[KL], kb2[KL];
-            VLoad va[NI], vb2[NI];
-            load_k(tile(0), blk(0), ka);
-            load_v(tile(0), blk(0), va);
-            load_k(tile(1), blk(1), kb2);
-            load_v(tile(1), blk(1), vb2);
-            for (int it = 0; it < cn; it += 2) {
-                qk_softmax(c0 + it, ka, lane_pick(kslo, kshi, it), lane_pick(vslo, vshi, it));
-                load_k(tile(it + 2), blk(it + 2), ka);
-                pv(c0 + it, va);
-                load_v(tile(it + 2), blk(it + 2), va);
-                qk_softmax(c0 + it + 1, kb2, lane_pick(kslo, kshi, it + 1), lane_pick(vslo, vshi, it + 1));
-                load_k(tile(it + 3), blk(it + 3), kb2);
-                pv(c0 + it + 1, vb2);
-                load_v(tile(it + 3), blk(it + 3), vb2);
+            uint4 kbuf[DEPTH][KL];
+            VLoad vbuf[DEPTH][NI];
+#pragma unroll
+            for (int st = 0; st < DEPTH; ++st) {
+                load_k(tile(st), blk(st), kbuf[st]);
+                load_v(tile(st), blk(st), vbuf[st]);
+            }
+            for (int it = 0; it < cn; it += DEPTH) {
+#pragma unroll
+                for (int st = 0; st < DEPTH; ++st) {
+                    qk_softmax(c0 + it + st, kbuf[st], lane_pick(kslo, kshi, it + st), lane_pick(vslo, vshi, it + st));
+                    load_k(tile(it + st + DEPTH), blk(it + st + DEPTH), kbuf[st]);
+                    pv(c0 + it + st, vbuf[st]);
+                    load_v(tile(it + st + DEPTH), blk(it + st + DEPTH), vbuf[st]);
+                }
             }
         }
 
