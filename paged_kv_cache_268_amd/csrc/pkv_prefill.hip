@@ -29,7 +29,10 @@
 //   O^T += V^T P^T: those 8 weights are already lane l's B operand (query
 //   l % 16, 8 keys), and the A operand is the same 8 keys of one d row of the
 //   transposed V tile (two 8-byte LDS reads), D/16 output blocks.
-// The weights enter the second product as a bf16 (f16) pair hi + lo with
+// Softmax per query column: a reference max that moves only when a score
+// exceeds it by more than 8 (log2 units), so the accumulator rescale is a rare
+// event (skipped for the whole wave when no column needs it) and every weight
+// stays <= 2^8.  The weights enter the second product as a bf16 (f16) pair hi + lo with
 // hi = round(p) and lo = round(p - hi), two MFMAs per block: one rounded
 // 16-bit weight carries up to 2^-9 relative error, which is too coarse for
 // outputs checked to 2e-3; the pair carries about 2^-17.  The running max,
@@ -48,6 +51,7 @@ constexpr int kPThreads = 256;
 constexpr int kPKeys = 32;                      // keys per tile
 constexpr float kPLog2e = 1.4426950408889634f;
 constexpr float kPLn2 = 0.6931471805599453f;
+constexpr float kPTau = 8.0f;                   // lazy-rescale threshold (log2 units)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -277,15 +281,16 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
             x[4 + r] = (qvalid && t0 + 16 + r <= qpos) ? c1[r] * sl2 : -INFINITY;
             mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
         }
-        mx = pmax32(pmax16(mx));
-        const float m_new = fmaxf(m_l, mx);
+        mx = pmax32(pmax16(mx));                       // column max of this tile
+        const bool need = mx > m_l + kPTau;            // uniform over the column's 4 lanes
+        const float m_new = need ? mx : m_l;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_l - m_new) : 1.f;   // 0 while nothing was seen
         const float ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_l - ref);    // 0 while nothing was seen
         V8 ph, pl;
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - ref);    // 0 for a masked key
+            const float p = __builtin_amdgcn_exp2f(x[i] - ref);    // <= 2^8; 0 for a masked key
             ps += p;
             const E hi = (E)p;
             ph[i] = hi;
@@ -293,9 +298,12 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
         }
         l_l = l_l * alpha + ps;
         m_l = m_new;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            acc[db] *= alpha;
             const uint8_t* row = vb + (db * 16 + col) * VROW;
             const uint2 lo4 = *reinterpret_cast<const uint2*>(row + 8 * quad);        // keys 4 quad + 0..3
             const uint2 hi4 = *reinterpret_cast<const uint2*>(row + 32 + 8 * quad);   // keys 16 + 4 quad + 0..3
