@@ -180,6 +180,21 @@ int kv_quantize_fp8(int32_t n, const int32_t* items, const void* src_k, const vo
                     int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                     pkv_stream_t stream);
 
+/* Append counts[i] tokens to each of the n listed sequences (a prefill chunk):
+ * the same as appending them one at a time, each sequence's tokens in a row,
+ * sequences in list order (so the same blocks, slots and copy-on-write), in
+ * one call on `stream`.  All or nothing (PKV_ENOMEM, PKV_EINVAL as kv_append;
+ * counts may be 0).
+ *   seq_ids, counts : host int32 [n]
+ *   k_new, v_new    : device [sum(counts)][num_kv_heads][head_dim] of kv_dtype
+ *                     (bf16 for 8-bit pools), rows of seq_ids[0] first
+ *   block_tables, context_lens : device, as for kv_append
+ * The per-token metadata travels through a pinned host ring; a call waits
+ * only if the ring slot it reuses is still in flight. */
+int kv_append_tokens(pkv_pool* pool, int32_t n, const int32_t* seq_ids, const int32_t* counts,
+                     const void* k_new, const void* v_new, int32_t* block_tables,
+                     int32_t* context_lens, pkv_stream_t stream);
+
 /* Publish the whole host view to the device tables (-1 past each length,
  * length 0 for free rows and for sequences parked in the host tier), ordered
  * on `stream`. */

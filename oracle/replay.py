@@ -261,6 +261,36 @@ class PoolReplay:
             items.append(AppendItem(s, slot, tpos, new_block, cow_src, cow_n, t + 1))
         return items
 
+    # -- append several tokens per sequence (all-or-nothing) ----------------
+    def append_tokens(self, seq_ids: Sequence[int], counts: Sequence[int]) -> List[AppendItem]:
+        """counts[i] tokens to seq_ids[i]: the same as appending them one at a time, each
+        sequence's tokens in a row, sequences in list order; nothing changes on an error."""
+        ids = [int(s) for s in seq_ids]
+        cnt = [int(c) for c in counts]
+        if len(ids) != len(cnt) or len(set(ids)) != len(ids) or any(c < 0 for c in cnt):
+            raise PoolError("EINVAL", "bad sequence list or counts")
+        need = 0
+        for s, c in zip(ids, cnt):
+            if s not in self.seqs:
+                raise PoolError("EINVAL", "unknown sequence")
+            if self.parked(s):
+                raise PoolError("EINVAL", "sequence has blocks in the host tier")
+            blocks, t = self.seqs[s]
+            if c == 0:
+                continue
+            if blocks_needed(t + c, self.bs) > self.max_blocks_per_seq:
+                raise PoolError("EINVAL", "sequence would exceed max_blocks_per_seq")
+            need += blocks_needed(t + c, self.bs) - blocks_needed(t, self.bs)
+            if t % self.bs and self.ref[blocks[-1]] > 1:
+                need += 1
+        if need > len(self.free):
+            raise PoolError("ENOMEM", "pool exhausted")
+        items = []
+        for s, c in zip(ids, cnt):
+            for _ in range(c):
+                items += self.append([s])
+        return items
+
     # -- views ------------------------------------------------------------
     def tables(self, width: Optional[int] = None):
         """(block_tables [max_seqs][width] with -1 fill, context_lens [max_seqs])."""

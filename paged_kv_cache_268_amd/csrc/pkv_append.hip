@@ -28,8 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_append.h"
 #include "pkv_fp8.h"
-#include "pkv_kernels.h"
 
 namespace pkv {
 
@@ -61,8 +61,12 @@ __global__ void __launch_bounds__(256) kv_append_cow_kernel(AppendArgs a) {
 
 // Write phase: one 256-thread workgroup per item moves 16-byte pieces of the
 // new K/V row of every kv head into the slot, then updates the tables.
-// 8-bit pool: 8 bf16 values of the new row per thread -> 8 codes.
-__device__ __forceinline__ void append_row_fp8(const AppendArgs& a, int i, int blk, int off, bool fresh) {
+// 8-bit pool: 8 bf16 values of the new row per thread -> 8 codes.  use_init:
+// the block was opened in this call, so its scales are the defaults (another
+// workgroup of the same call may not have recorded them yet); record: this
+// row opens the block and records them.
+__device__ __forceinline__ void append_row_fp8(const AppendArgs& a, int i, int blk, int off, bool use_init,
+                                               bool record) {
     const int bs = a.block_size, Hkv = a.num_kv_heads, per_row = a.head_dim / 8;
     const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
     const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
@@ -71,8 +75,8 @@ __device__ __forceinline__ void append_row_fp8(const AppendArgs& a, int i, int b
     for (int x = threadIdx.x; x < Hkv * per_row; x += blockDim.x) {
         const int g = x / per_row, r = x % per_row;
         const int64_t bg = (int64_t)blk * Hkv + g;
-        const float ks = fresh ? a.k_init[g] : a.k_scale[bg];
-        const float vs = fresh ? a.v_init[g] : a.v_scale[bg];
+        const float ks = use_init ? a.k_init[g] : a.k_scale[bg];
+        const float vs = use_init ? a.v_init[g] : a.v_scale[bg];
         const int64_t src = ((int64_t)i * Hkv + g) * per_row + r;
         const int64_t row = (bg * bs + off) * per_row + r;
         const uint4 w[2] = {kn[src], vn[src]};
@@ -92,27 +96,17 @@ __device__ __forceinline__ void append_row_fp8(const AppendArgs& a, int i, int b
         kc[row] = o[0];
         vc[row] = o[1];
     }
-    if (fresh && (int)threadIdx.x < Hkv) {
+    if (record && (int)threadIdx.x < Hkv) {
         a.k_scale[(int64_t)blk * Hkv + threadIdx.x] = a.k_init[threadIdx.x];
         a.v_scale[(int64_t)blk * Hkv + threadIdx.x] = a.v_init[threadIdx.x];
     }
 }
 
-__device__ __forceinline__ void append_item(const AppendArgs& a, int i, int seq, int slot, int new_block,
-                                            int new_len) {
-    if (a.kv8) {
-        const int bs = a.block_size;
-        append_row_fp8(a, i, slot / bs, slot % bs, new_block >= 0 && slot % bs == 0);
-        if (threadIdx.x == 0) {
-            if (new_block >= 0) a.block_tables[(int64_t)seq * a.table_stride + (new_len - 1) / bs] = new_block;
-            a.context_lens[seq] = new_len;
-        }
-        return;
-    }
+// 16-bit pool: the new row of every kv head, 16-byte pieces, bit-exact.
+__device__ __forceinline__ void append_row16(const AppendArgs& a, int i, int blk, int off) {
     const int bs = a.block_size, Hkv = a.num_kv_heads, vec_per_row = a.head_dim / 8;
     uint4* kc = reinterpret_cast<uint4*>(a.k_cache);
     uint4* vc = reinterpret_cast<uint4*>(a.v_cache);
-    const int blk = slot / bs, off = slot % bs;
     const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
     const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
     for (int x = threadIdx.x; x < Hkv * vec_per_row; x += blockDim.x) {
@@ -121,6 +115,17 @@ __device__ __forceinline__ void append_item(const AppendArgs& a, int i, int seq,
         const int64_t src = ((int64_t)i * Hkv + g) * vec_per_row + r;
         kc[row] = kn[src];
         vc[row] = vn[src];
+    }
+}
+
+__device__ __forceinline__ void append_item(const AppendArgs& a, int i, int seq, int slot, int new_block,
+                                            int new_len) {
+    const int bs = a.block_size;
+    if (a.kv8) {
+        const bool fresh = new_block >= 0 && slot % bs == 0;
+        append_row_fp8(a, i, slot / bs, slot % bs, fresh, fresh);
+    } else {
+        append_row16(a, i, slot / bs, slot % bs);
     }
     if (threadIdx.x == 0) {
         if (new_block >= 0) a.block_tables[(int64_t)seq * a.table_stride + (new_len - 1) / bs] = new_block;
@@ -138,6 +143,38 @@ __global__ void __launch_bounds__(256) kv_append_kernel_host(AppendArgs a) {
     if (threadIdx.x == 0) s_it = a.items[blockIdx.x];   // host memory: read once
     __syncthreads();
     append_item(a, blockIdx.x, s_it.seq, s_it.slot, s_it.new_block, s_it.new_len);
+}
+
+// Multi-token append: one workgroup per token (row i of k_new / v_new).  Only
+// a sequence's last token of the call writes its length; a token that opened
+// or copied a block publishes the table entry.
+__global__ void __launch_bounds__(256) kv_append_tokens_kernel(AppendArgs a, const TokenItem* tokens) {
+    __shared__ TokenItem s_t;
+    if (threadIdx.x == 0) s_t = tokens[blockIdx.x];     // host memory: read once
+    __syncthreads();
+    const TokenItem t = s_t;
+    const int bs = a.block_size, blk = t.slot / bs, off = t.slot % bs;
+    if (a.kv8) {
+        const bool fresh = (t.flags & kTokFresh) != 0;
+        append_row_fp8(a, blockIdx.x, blk, off, fresh, fresh && off == 0);
+    } else {
+        append_row16(a, blockIdx.x, blk, off);
+    }
+    if (threadIdx.x == 0) {
+        if (t.flags & kTokTable) a.block_tables[(int64_t)t.seq * a.table_stride + t.tpos] = blk;
+        if (t.flags & kTokLast) a.context_lens[t.seq] = t.tpos * bs + off + 1;
+    }
+}
+
+hipError_t launch_append_tokens(const AppendArgs& a, int32_t n_tokens, const TokenItem* tokens, bool any_copy,
+                                hipStream_t stream) {
+    if (any_copy && a.n > 0) {
+        hipLaunchKernelGGL(kv_append_cow_kernel, dim3((unsigned)a.n), dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (n_tokens > 0) hipLaunchKernelGGL(kv_append_tokens_kernel, dim3((unsigned)n_tokens), dim3(256), 0, stream, a, tokens);
+    return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream) {

@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "pkv.h"
+#include "pkv_append.h"
 #include "pkv_fp8.h"
 #include "pkv_kernels.h"
 #include "pkv_prefill.h"
@@ -110,6 +111,14 @@ struct pkv_pool {
     };
     CopySlot copy_ring[kCopyRing];
     int copy_next = 0;
+    struct TokSlot {                             // kv_append_tokens staging (pinned, device-readable)
+        uint8_t* buf = nullptr;
+        size_t cap = 0;
+        hipEvent_t ev = nullptr;
+        bool pending = false;
+    };
+    TokSlot tok_ring[kCopyRing];
+    int tok_next = 0;
 
     int32_t pop_free() {
         while (!stack.empty() && stack.back() < 0) stack.pop_back();
@@ -228,6 +237,11 @@ void kv_block_pool_destroy(pkv_pool* p) {
         if (c.ev) (void)hipEventDestroy(c.ev);
         if (c.pairs) (void)hipHostFree(c.pairs);
     }
+    for (auto& t : p->tok_ring) {
+        if (t.pending) (void)hipEventSynchronize(t.ev);
+        if (t.ev) (void)hipEventDestroy(t.ev);
+        if (t.buf) (void)hipHostFree(t.buf);
+    }
     if (p->tab_pending) (void)hipEventSynchronize(p->tab_ev);
     if (p->tab_ev) (void)hipEventDestroy(p->tab_ev);
     if (p->tab_host) (void)hipHostFree(p->tab_host);
@@ -330,6 +344,32 @@ int kv_pool_stats(const pkv_pool* p, int32_t* num_free_out, int32_t* num_seqs_ou
     return PKV_OK;
 }
 
+// The slot of sequence s's next token (capacity checked by the caller): a new
+// block when its length is a multiple of block_size, else a copy of a shared,
+// partly filled tail (copy-on-write), else the tail itself.
+static pkv::AppendItem take_slot(pkv_pool* p, int32_t s) {
+    const int32_t bs = p->d.block_size;
+    auto& blk = p->blocks[s];
+    const int32_t t = p->len[s];
+    const int32_t tpos = t / bs, off = t % bs;
+    pkv::AppendItem it{s, 0, tpos, -1, -1, 0, t + 1};
+    if (off == 0) {
+        it.new_block = p->pop_free();
+        p->ref[it.new_block] = 1;
+        blk.push_back(it.new_block);
+    } else if (p->ref[blk.back()] > 1) {
+        it.new_block = p->pop_free();
+        p->ref[it.new_block] = 1;
+        it.cow_src = blk.back();
+        it.cow_ntok = off;
+        --p->ref[it.cow_src];
+        blk.back() = it.new_block;
+    }
+    it.slot = blk[tpos] * bs + off;
+    p->len[s] = t + 1;
+    return it;
+}
+
 static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::AppendItem* items, bool* any_copy) {
     if (n < 0 || (n > 0 && !seq_ids)) return fail(PKV_EINVAL, "kv_reserve: bad n or seq_ids");
     const int32_t bs = p->d.block_size;
@@ -354,26 +394,8 @@ static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::App
         return fail(PKV_ENOMEM, "kv_reserve: need %lld blocks, %d free", (long long)need, p->num_free);
     bool copy = false;
     for (int32_t i = 0; i < n; ++i) {
-        const int32_t s = seq_ids[i];
-        auto& blk = p->blocks[s];
-        const int32_t t = p->len[s];
-        const int32_t tpos = t / bs, off = t % bs;
-        pkv::AppendItem it{s, 0, tpos, -1, -1, 0, t + 1};
-        if (off == 0) {
-            it.new_block = p->pop_free();
-            p->ref[it.new_block] = 1;
-            blk.push_back(it.new_block);
-        } else if (p->ref[blk.back()] > 1) {
-            it.new_block = p->pop_free();
-            p->ref[it.new_block] = 1;
-            it.cow_src = blk.back();
-            it.cow_ntok = off;
-            --p->ref[it.cow_src];
-            blk.back() = it.new_block;
-            copy = true;
-        }
-        it.slot = blk[tpos] * bs + off;
-        p->len[s] = t + 1;
+        const pkv::AppendItem it = take_slot(p, seq_ids[i]);
+        copy |= it.cow_src >= 0;
         if (items) items[i] = it;
     }
     if (any_copy) *any_copy = copy;
@@ -464,6 +486,111 @@ int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new,
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
     slot.pending = true;
     p->next = (p->next + 1) % kRing;
+    return PKV_OK;
+}
+
+int kv_append_tokens(pkv_pool* p, int32_t n, const int32_t* seq_ids, const int32_t* counts, const void* k_new,
+                     const void* v_new, int32_t* block_tables, int32_t* context_lens, pkv_stream_t stream) {
+    if (!p) return fail(PKV_EINVAL, "kv_append_tokens: null pool");
+    if (n < 0 || n > p->d.max_seqs || (n > 0 && (!seq_ids || !counts)))
+        return fail(PKV_EINVAL, "kv_append_tokens: bad n, seq_ids or counts");
+    const bool kv8 = p->d.kv_dtype == PKV_FP8_E4M3;
+    if (kv8 && !p->k_scale) return fail(PKV_EINVAL, "kv_append_tokens: 8-bit pool without scales (kv_block_pool_set_fp8_scales)");
+    const int32_t bs = p->d.block_size;
+    std::vector<uint8_t> mark(p->d.max_seqs, 0);
+    int64_t need = 0, total = 0, cows = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i], c = counts[i];
+        if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_append_tokens: unknown sequence %d", s);
+        if (mark[s]) return fail(PKV_EINVAL, "kv_append_tokens: sequence %d listed twice", s);
+        mark[s] = 1;
+        if (p->nhost[s]) return fail(PKV_EINVAL, "kv_append_tokens: sequence %d has blocks in the host tier", s);
+        if (c < 0) return fail(PKV_EINVAL, "kv_append_tokens: count %d", c);
+        if (c == 0) continue;
+        const int64_t t = p->len[s];
+        if (ceil_div(t + c, bs) > p->d.max_blocks_per_seq)
+            return fail(PKV_EINVAL, "kv_append_tokens: sequence %d would exceed %d blocks", s, p->d.max_blocks_per_seq);
+        need += ceil_div(t + c, bs) - ceil_div(t, bs);
+        if (t % bs && p->ref[p->blocks[s].back()] > 1) {
+            ++need;
+            ++cows;
+        }
+        total += c;
+    }
+    if (need > p->num_free)
+        return fail(PKV_ENOMEM, "kv_append_tokens: need %lld blocks, %d free", (long long)need, p->num_free);
+    if (total == 0) return PKV_OK;
+    if (total > 0x7FFFFFFF) return fail(PKV_EINVAL, "kv_append_tokens: too many tokens");
+    if (!k_new || !v_new || !block_tables || !context_lens || !p->k_cache || !p->v_cache)
+        return fail(PKV_EINVAL, "kv_append_tokens: null device pointer");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return fail(PKV_EINVAL, "kv_append_tokens: k_new / v_new must be 16-byte aligned");
+    // Staging: tokens, then copy-on-write items, in one pinned buffer of a small ring.
+    const size_t tok_bytes = sizeof(pkv::TokenItem) * (size_t)total;
+    const size_t cow_off = (tok_bytes + 255) / 256 * 256;
+    const size_t bytes = cow_off + sizeof(pkv::AppendItem) * (size_t)std::max<int64_t>(cows, 1);
+    auto& sl = p->tok_ring[p->tok_next];
+    if (!sl.ev) {
+        hipError_t e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+        if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags (token staging)");
+    }
+    if (sl.pending) {
+        hipError_t e = hipEventSynchronize(sl.ev);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (token staging)");
+        sl.pending = false;
+    }
+    if (sl.cap < bytes) {
+        if (sl.buf) (void)hipHostFree(sl.buf);
+        sl.buf = nullptr;
+        sl.cap = 0;
+        const size_t cap = std::max<size_t>(bytes, 65536);
+        hipError_t e = hipHostMalloc((void**)&sl.buf, cap, hipHostMallocCoherent | hipHostMallocMapped);
+        if (e != hipSuccess) return fail_hip(e, "hipHostMalloc (token staging)");
+        sl.cap = cap;
+    }
+    auto* tok = reinterpret_cast<pkv::TokenItem*>(sl.buf);
+    auto* cow = reinterpret_cast<pkv::AppendItem*>(sl.buf + cow_off);
+    int64_t k = 0, nc = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i], c = counts[i];
+        int32_t fresh_block = -1;                // block this sequence opened (not copied) in this call
+        for (int32_t j = 0; j < c; ++j) {
+            const pkv::AppendItem it = take_slot(p, s);
+            int32_t flags = 0;
+            if (j == c - 1) flags |= pkv::kTokLast;
+            if (it.new_block >= 0) {
+                flags |= pkv::kTokTable;
+                fresh_block = it.cow_src >= 0 ? -1 : it.new_block;
+            }
+            if (it.cow_src >= 0) cow[nc++] = it;
+            if (fresh_block >= 0 && it.slot / bs == fresh_block) flags |= pkv::kTokFresh;
+            tok[k++] = pkv::TokenItem{s, it.slot, it.tpos, flags};
+        }
+    }
+    pkv::AppendArgs a{};
+    a.items = cow;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = p->k_cache;
+    a.v_cache = p->v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.n = (int32_t)nc;
+    a.num_kv_heads = p->d.num_kv_heads;
+    a.head_dim = p->d.head_dim;
+    a.block_size = bs;
+    a.table_stride = p->d.max_blocks_per_seq;
+    a.kv8 = kv8 ? 1 : 0;
+    a.k_scale = p->k_scale;
+    a.v_scale = p->v_scale;
+    a.k_init = p->k_init;
+    a.v_init = p->v_init;
+    hipError_t e = pkv::launch_append_tokens(a, (int32_t)total, tok, nc > 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "kv_append_tokens launch (pool state now ahead of the device)");
+    e = hipEventRecord(sl.ev, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+    sl.pending = true;
+    p->tok_next = (p->tok_next + 1) % kCopyRing;
     return PKV_OK;
 }
 

@@ -57,50 +57,11 @@ struct MergeArgs {
     int32_t out_dtype;
 };
 
-// One append item, as staged by the host (7 int32).
-struct AppendItem {
-    int32_t seq, slot, tpos, new_block, cow_src, cow_ntok, new_len;
-};
-
-// Items small enough to travel in the kernel arguments (no host-memory read
-// on the device): 16 bytes each, up to kArgItems of them.
-struct ArgItem {
-    int32_t seq, slot, new_block, new_len;     // table_pos = (new_len - 1) / block_size
-};
-constexpr int kArgItems = 160;
-struct ArgItems {
-    ArgItem it[kArgItems];
-};
-
-struct AppendArgs {
-    const AppendItem* items;     // device-readable (pinned host) [n]
-    const void* k_new;           // [n][Hkv][D]
-    const void* v_new;
-    void* k_cache;               // [NB][Hkv][bs][D]
-    void* v_cache;
-    int32_t* block_tables;       // [max_seqs][table_stride]
-    int32_t* context_lens;       // [max_seqs]
-    int32_t n;
-    int32_t num_kv_heads;
-    int32_t head_dim;
-    int32_t block_size;
-    int32_t table_stride;
-    // 8-bit (E4M3) pools: new rows (bf16) are quantised with their block's
-    // scale; a block started by this call takes the default scales.
-    int32_t kv8;
-    float* k_scale;              // [num_blocks][Hkv]
-    float* v_scale;
-    const float* k_init;         // [Hkv] default scales of new blocks
-    const float* v_init;
-};
 
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream);
 // Resident waves per CU of the split kernel instance (occupancy query).
 hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
-// items_in_args: a.n <= kArgItems and `inl` holds the items (copy-on-write
-// still reads a.items, in the separate copy launch).
-hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream);
 
 }  // namespace pkv

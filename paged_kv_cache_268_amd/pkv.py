@@ -22,7 +22,7 @@ PKV_F16, PKV_BF16, PKV_F32, PKV_FP8_E4M3 = 0, 1, 2, 3
 EXPORTS = (
     "pkv_last_error", "pkv_version",
     "kv_block_pool_create", "kv_block_pool_destroy", "kv_seq_add", "kv_seq_import", "kv_seq_fork",
-    "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_write_tables",
+    "kv_seq_free", "kv_seq_info", "kv_pool_stats", "kv_reserve", "kv_append", "kv_append_tokens", "kv_write_tables",
     "kv_validate_tables", "kv_block_pool_attach_host_tier", "kv_seq_offload", "kv_seq_restore",
     "kv_host_tier_stats", "kv_block_pool_set_fp8_scales", "kv_quantize_fp8", "paged_attn_decode_fp8",
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "kv_reserve": ([P, I32, P, P], ctypes.c_int),
         "kv_append": ([P, I32, P, P, P, P, P, P], ctypes.c_int),
         "kv_write_tables": ([P, P, P, P], ctypes.c_int),
+        "kv_append_tokens": ([P, I32, P, P, P, P, P, P, P], ctypes.c_int),
         "kv_validate_tables": ([I32, P, I32, I32, P, I32, I32], ctypes.c_int),
         "kv_block_pool_attach_host_tier": ([P, I32, P, P], ctypes.c_int),
         "kv_seq_offload": ([P, I32, P, I32, P], ctypes.c_int),
@@ -389,6 +390,13 @@ class BlockPool:
         ids = _i32(seq_ids)
         check(self.lib.kv_append(self.handle, ids.size, ids.ctypes.data if ids.size else None, _ptr(k_new),
                                  _ptr(v_new), _ptr(block_tables), _ptr(context_lens), _stream(stream)))
+
+    def append_tokens(self, seq_ids, counts, k_new, v_new, block_tables, context_lens, stream=None):
+        ids, cnt = _i32(seq_ids), _i32(counts)
+        assert ids.size == cnt.size
+        check(self.lib.kv_append_tokens(self.handle, ids.size, ids.ctypes.data if ids.size else None,
+                                        cnt.ctypes.data if cnt.size else None, _ptr(k_new), _ptr(v_new),
+                                        _ptr(block_tables), _ptr(context_lens), _stream(stream)))
 
     def write_tables(self, block_tables, context_lens, stream=None):
         check(self.lib.kv_write_tables(self.handle, _ptr(block_tables), _ptr(context_lens), _stream(stream)))

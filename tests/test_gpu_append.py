@@ -190,3 +190,158 @@ def test_append_large_batch():
     assert tab.cpu().numpy().tolist() == want_tab
     assert np.array_equal(W.bits16(k), mirror.k) and np.array_equal(W.bits16(v), mirror.v)
     pool.close()
+
+
+@pytest.mark.parametrize("bs,D,dtype", [(16, 128, "bf16"), (32, 64, "f16")])
+def test_append_tokens_bit_exact(bs, D, dtype):
+    """Multi-token appends (prefill chunks): the same blocks, slots, copy-on-write and bytes as
+    the replay's one-token-at-a-time appends."""
+    NB, Hkv, S, Wd = 64, 2, 5, 16
+    note(f"kv_append_tokens bs={bs} D={D} {dtype}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    code = pkv.PKV_BF16 if dtype == "bf16" else pkv.PKV_F16
+    order = np.random.default_rng(7).permutation(NB).astype(np.int32)
+    k = torch.empty((NB, Hkv, bs, D), dtype=tdt, device=DEV); W.fill_normal_(k, 41)
+    v = torch.empty_like(k); W.fill_normal_(v, 42)
+    tab = torch.full((S, Wd), -1, dtype=torch.int32, device=DEV)
+    lens = torch.zeros(S, dtype=torch.int32, device=DEV)
+    pool = pkv.BlockPool(NB, bs, Hkv, D, code, S, Wd, k_cache=k, v_cache=v, alloc_order=order)
+    ref = R.PoolReplay(NB, bs, S, Wd, alloc_order=order)
+    mirror = Mirror(k, v)
+    ids = [pool.add() for _ in range(3)]
+    assert ids == [ref.add_seq() for _ in range(3)]
+    pool.write_tables(tab, lens)
+    rng = np.random.default_rng(8)
+    seed = 900
+
+    def chunk(seq_ids, counts):
+        nonlocal seed
+        n = int(sum(counts))
+        kn = torch.empty((max(n, 1), Hkv, D), dtype=tdt, device=DEV); W.fill_normal_(kn, seed)
+        vn = torch.empty_like(kn); W.fill_normal_(vn, seed + 1)
+        seed += 2
+        items = ref.append_tokens(seq_ids, counts)
+        pool.append_tokens(seq_ids, counts, kn, vn, tab, lens)
+        mirror.apply(items, kn, vn, bs)
+
+    def check():
+        torch.cuda.synchronize()
+        want_tab, want_len = ref.tables(Wd)
+        got_tab, got_len = tab.cpu().numpy(), lens.cpu().numpy()
+        for s in sorted(ref.seqs):
+            assert got_len[s] == want_len[s]
+            n = -(-want_len[s] // bs)
+            assert got_tab[s, :n].tolist() == want_tab[s][:n]
+        assert np.array_equal(W.bits16(k), mirror.k) and np.array_equal(W.bits16(v), mirror.v)
+
+    chunk(ids, [37, 0, 16])
+    chunk(ids[::-1], [5, 40, 1])
+    check()
+    child = pool.fork(ids[0]); assert child == ref.fork(ids[0])
+    pool.write_tables(tab, lens)
+    ids.append(child)
+    chunk([child, ids[0]], [20, 3])              # both copy the shared partly filled tail
+    for _ in range(6):
+        sel = sorted(rng.choice(ids, rng.integers(1, len(ids) + 1), replace=False).tolist())
+        chunk(sel, rng.integers(0, 30, len(sel)).tolist())
+    check()
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append_tokens([ids[0]], [Wd * bs], torch.zeros((Wd * bs, Hkv, D), dtype=tdt, device=DEV),
+                           torch.zeros((Wd * bs, Hkv, D), dtype=tdt, device=DEV), tab, lens)
+    assert e.value.code == pkv.PKV_EINVAL
+    check()
+    pool.close()
+
+
+def test_append_tokens_8bit():
+    NB, Hkv, D, bs, S, Wd = 48, 2, 128, 16, 4, 12
+    note("kv_append_tokens, 8-bit pool")
+    kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((NB, Hkv), device=DEV)
+    vs = torch.zeros_like(ks)
+    k_init = torch.tensor([0.0101, 0.0087], device=DEV)
+    v_init = torch.tensor([0.0093, 0.0111], device=DEV)
+    tab = torch.full((S, Wd), -1, dtype=torch.int32, device=DEV)
+    lens = torch.zeros(S, dtype=torch.int32, device=DEV)
+    pool = pkv.BlockPool(NB, bs, Hkv, D, pkv.PKV_FP8_E4M3, S, Wd, k_cache=kc, v_cache=vc)
+    pool.set_fp8_scales(ks, vs, k_init, v_init)
+    ref = R.PoolReplay(NB, bs, S, Wd)
+    ids = [pool.add() for _ in range(2)]
+    assert ids == [ref.add_seq() for _ in range(2)]
+    pool.write_tables(tab, lens)
+    mk, mv = np.zeros((NB, Hkv, bs, D), np.uint8), np.zeros((NB, Hkv, bs, D), np.uint8)
+    msk, msv = np.zeros((NB, Hkv), np.float32), np.zeros((NB, Hkv), np.float32)
+    ki, vi = k_init.cpu().numpy(), v_init.cpu().numpy()
+    seed = 70
+
+    def chunk(seq_ids, counts):
+        nonlocal seed
+        n = int(sum(counts))
+        kn = torch.empty((n, Hkv, D), dtype=torch.bfloat16, device=DEV); W.fill_normal_(kn, seed)
+        vn = torch.empty_like(kn); W.fill_normal_(vn, seed + 1)
+        seed += 2
+        items = ref.append_tokens(seq_ids, counts)
+        pool.append_tokens(seq_ids, counts, kn, vn, tab, lens)
+        knf = (W.bits16(kn).astype(np.uint32) << 16).view(np.float32)
+        vnf = (W.bits16(vn).astype(np.uint32) << 16).view(np.float32)
+        for seq, slot, tpos, nb, cs, cn, nl in items:
+            if cs >= 0:
+                mk[nb, :, :cn], mv[nb, :, :cn] = mk[cs, :, :cn], mv[cs, :, :cn]
+                msk[nb], msv[nb] = msk[cs], msv[cs]
+        for i, (seq, slot, tpos, nb, cs, cn, nl) in enumerate(items):
+            b, off = slot // bs, slot % bs
+            if nb >= 0 and off == 0:
+                msk[b], msv[b] = ki, vi
+            for g in range(Hkv):
+                mk[b, g, off] = oracle.fp8_encode(knf[i, g] / np.float32(msk[b, g]))
+                mv[b, g, off] = oracle.fp8_encode(vnf[i, g] / np.float32(msv[b, g]))
+
+    chunk(ids, [45, 17])
+    child = pool.fork(ids[0]); assert child == ref.fork(ids[0])
+    pool.write_tables(tab, lens)
+    chunk([child, ids[1], ids[0]], [33, 2, 19])
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), mk) and np.array_equal(vc.cpu().numpy(), mv)
+    assert np.array_equal(ks.cpu().numpy(), msk) and np.array_equal(vs.cpu().numpy(), msv)
+    want_tab, want_len = ref.tables(Wd)
+    assert lens.cpu().tolist() == want_len
+    pool.close()
+
+
+def test_chunked_prefill_flow():
+    """Write a prefix chunk and a second chunk with kv_append_tokens, then prefill the second chunk
+    over the paged cache; compare with the oracle on the mirrored cache."""
+    NB, Hq, Hkv, D, bs, Wd = 80, 8, 2, 128, 16, 24
+    note("append_tokens + prefill flow")
+    order = np.random.default_rng(11).permutation(NB).astype(np.int32)
+    k = torch.full((NB, Hkv, bs, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v = torch.full_like(k, float("nan"))
+    tab = torch.full((3, Wd), -1, dtype=torch.int32, device=DEV)
+    lens = torch.zeros(3, dtype=torch.int32, device=DEV)
+    pool = pkv.BlockPool(NB, bs, Hkv, D, pkv.PKV_BF16, 3, Wd, k_cache=k, v_cache=v, alloc_order=order)
+    ref = R.PoolReplay(NB, bs, 3, Wd, alloc_order=order)
+    mirror = Mirror(k, v)
+    ids = [pool.add() for _ in range(3)]
+    assert ids == [ref.add_seq() for _ in range(3)]
+    pool.write_tables(tab, lens)
+    for j, counts in enumerate(([100, 0, 37], [64, 130, 9])):
+        n = sum(counts)
+        kn = torch.empty((n, Hkv, D), dtype=torch.bfloat16, device=DEV); W.fill_normal_(kn, 300 + j)
+        vn = torch.empty_like(kn); W.fill_normal_(vn, 400 + j)
+        items = ref.append_tokens(ids, counts)
+        pool.append_tokens(ids, counts, kn, vn, tab, lens)
+        mirror.apply(items, kn, vn, bs)
+    cu = np.array([0, 64, 194, 203], dtype=np.int32)
+    q = torch.empty((203, Hq, D), dtype=torch.bfloat16, device=DEV); W.fill_normal_(q, 77)
+    want_tab, want_len = ref.tables(Wd)
+    lse = torch.empty((203, Hq), device=DEV)
+    out = pkv.prefill(q, k, v, tab, lens, torch.from_numpy(cu).to(DEV), 0.0884, int(max(want_len)), lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(W.bits16(q), mirror.k, mirror.v, np.array(want_tab, np.int32),
+                                  np.array(want_len, np.int32), cu, 0.0884, num_kv_heads=Hkv, block_size=bs,
+                                  dtype=oracle.BF16)
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o)) and np.abs(o - ro).max() <= 2e-3
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 2e-3
+    pool.close()

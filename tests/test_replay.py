@@ -274,3 +274,49 @@ def test_random_tier_ops_conserve_blocks():
         assert all(pool.host_ref[b] == c for b, c in hheld.items())
         assert len(held) + len(pool.free) == 48 and not set(held) & set(pool.free)
         assert len(hheld) + len(pool.host_free) == 24 and not set(hheld) & set(pool.host_free)
+
+
+def test_append_tokens_is_sequential_single_appends():
+    rnd = random.Random(5)
+    for trial in range(40):
+        order = list(range(40))
+        rnd.shuffle(order)
+        setup = [rnd.randint(0, 9) for _ in range(3)]
+        fork = rnd.random() < 0.5
+        pools = []
+        for _ in range(2):
+            pool = R.PoolReplay(40, 4, max_seqs=6, max_blocks_per_seq=12, alloc_order=order)
+            for c in setup:
+                sid = pool.add_seq()
+                for _ in range(c):
+                    pool.append([sid])
+            if fork:
+                pool.fork(0)
+            pools.append(pool)
+        a, b = pools
+        ids = sorted(a.seqs)
+        rnd.shuffle(ids)
+        counts = [rnd.randint(0, 9) for _ in ids]
+        try:
+            got = a.append_tokens(ids, counts)
+        except R.PoolError:
+            continue
+        want = []
+        for s_, c in zip(ids, counts):
+            for _ in range(c):
+                want += b.append([s_])
+        assert got == want and a.seqs == b.seqs and a.free == b.free and a.ref == b.ref
+
+
+def test_append_tokens_all_or_nothing():
+    pool = R.PoolReplay(6, 4, max_seqs=3, max_blocks_per_seq=4)
+    s, t = pool.add_seq(), pool.add_seq()
+    snap = (list(pool.free), {k: (list(v[0]), v[1]) for k, v in pool.seqs.items()})
+    with pytest.raises(R.PoolError):
+        pool.append_tokens([s, t], [12, 13])      # 3 + 4 blocks > 6 free
+    with pytest.raises(R.PoolError):
+        pool.append_tokens([s], [17])             # 5 blocks > max_blocks_per_seq
+    assert snap == (list(pool.free), {k: (list(v[0]), v[1]) for k, v in pool.seqs.items()})
+    items = pool.append_tokens([s, t], [5, 3])
+    assert [it[0] for it in items] == [s] * 5 + [t] * 3
+    assert pool.seqs[s][1] == 5 and pool.seqs[t][1] == 3
