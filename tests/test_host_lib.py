@@ -276,3 +276,105 @@ def test_validate_tables():
         pkv.validate_tables(tab, [33, 16], num_blocks=4, block_size=16)   # third entry is -1
     with pytest.raises(pkv.PkvError):
         pkv.validate_tables(tab, [20, 16], num_blocks=3, block_size=16)   # id 3 out of range
+
+
+# ---------------------------------------------------------------- 8-bit descriptors
+
+def test_fp8_descriptor_rules():
+    lib = pkv.load()
+    fake = ctypes.c_void_p(1 << 20)
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0, num_waves=64, kv_dtype=pkv.PKV_FP8_E4M3)
+    assert pkv.workspace_bytes(d) > 0
+    # the 16-bit entry point refuses an 8-bit descriptor, before touching any pointer
+    rc = lib.paged_attn_decode(ctypes.byref(d), fake, fake, fake, fake, fake, ctypes.c_float(1.0), fake, None,
+                               fake, 1 << 30, None)
+    assert rc == pkv.PKV_EINVAL and "fp8" in pkv.last_error()
+    # the 8-bit entry points refuse a 16-bit descriptor and missing scales
+    d16 = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0, num_waves=64)
+    rc = lib.paged_attn_decode_fp8(ctypes.byref(d16), fake, fake, fake, fake, fake, fake, fake, ctypes.c_float(1.0),
+                                   fake, None, fake, 1 << 30, None)
+    assert rc == pkv.PKV_EINVAL
+    rc = lib.paged_attn_decode_fp8(ctypes.byref(d), fake, fake, fake, None, fake, fake, fake, ctypes.c_float(1.0),
+                                   fake, None, fake, 1 << 30, None)
+    assert rc == pkv.PKV_EINVAL
+    # an 8-bit cache needs a bf16 query
+    df = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0, dtype=pkv.PKV_F16, num_waves=64,
+                       kv_dtype=pkv.PKV_FP8_E4M3)
+    rc = lib.paged_attn_decode_fp8(ctypes.byref(df), fake, fake, fake, fake, fake, fake, fake, ctypes.c_float(1.0),
+                                   fake, None, fake, 1 << 30, None)
+    assert rc == pkv.PKV_EUNSUPPORTED
+    rc = lib.kv_quantize_fp8(1, fake, fake, fake, pkv.PKV_F32, fake, fake, fake, fake, 2, 16, 128, None)
+    assert rc == pkv.PKV_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- prefill descriptors
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_q_heads", 6, pkv.PKV_EINVAL),
+    ("head_dim", 96, pkv.PKV_EUNSUPPORTED),
+    ("block_size", 8, pkv.PKV_EUNSUPPORTED),
+    ("kv_dtype", pkv.PKV_F16, pkv.PKV_EUNSUPPORTED),      # q is bf16
+    ("out_dtype", pkv.PKV_F16, pkv.PKV_EUNSUPPORTED),
+    ("table_stride", 3, pkv.PKV_EINVAL),
+    ("num_seqs", 5000, pkv.PKV_EUNSUPPORTED),
+    ("total_q", -1, pkv.PKV_EINVAL),
+])
+def test_prefill_descriptor_errors(field, value, code):
+    d = pkv.PrefillDesc(2, 8, 4, 128, 16, 100, 64, 300, 1000, pkv.PKV_BF16, pkv.PKV_BF16, pkv.PKV_F32)
+    setattr(d, field, value)
+    lib = pkv.load()
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.paged_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, fake, fake, ctypes.c_float(1.0), fake,
+                                None, None)
+    assert rc == code, pkv.last_error()
+
+
+def test_prefill_misaligned_and_null_refused():
+    d = pkv.PrefillDesc(2, 8, 4, 128, 16, 100, 64, 300, 1000, pkv.PKV_BF16, pkv.PKV_BF16, pkv.PKV_F32)
+    lib = pkv.load()
+    ok, bad = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    rc = lib.paged_attn_prefill(ctypes.byref(d), bad, ok, ok, ok, ok, ok, ctypes.c_float(1.0), ok, None, None)
+    assert rc == pkv.PKV_EINVAL
+    rc = lib.paged_attn_prefill(ctypes.byref(d), ok, ok, ok, ok, ok, None, ctypes.c_float(1.0), ok, None, None)
+    assert rc == pkv.PKV_EINVAL
+    d.total_q = 0                                          # nothing to do: no pointer is looked at
+    rc = lib.paged_attn_prefill(ctypes.byref(d), None, None, None, None, None, None, ctypes.c_float(1.0), None,
+                                None, None)
+    assert rc == pkv.PKV_OK
+
+
+# ---------------------------------------------------------------- multi-token append
+
+def test_append_tokens_errors_leave_the_pool_unchanged():
+    order = list(range(12))
+    pool = pkv.BlockPool(12, 16, 2, 64, pkv.PKV_BF16, 4, 4, alloc_order=order)
+    ref = R.PoolReplay(12, 16, 4, 4, alloc_order=order)
+    a, b = pool.add(), pool.add()
+    assert [a, b] == [ref.add_seq(), ref.add_seq()]
+    fake = ctypes.c_void_p(1 << 20)
+    lib = pkv.load()
+
+    def call(ids, counts):
+        ids = np.asarray(ids, np.int32); counts = np.asarray(counts, np.int32)
+        return lib.kv_append_tokens(pool.handle, ids.size, ids.ctypes.data, counts.ctypes.data, fake, fake, fake,
+                                    fake, None)
+
+    before = (pool.stats(), pool.info(a), pool.info(b))
+    for ids, counts, code in (([a, 7], [1, 1], pkv.PKV_EINVAL),          # unknown sequence
+                              ([a, a], [1, 1], pkv.PKV_EINVAL),          # listed twice
+                              ([a], [-1], pkv.PKV_EINVAL),               # negative count
+                              ([a], [65], pkv.PKV_EINVAL),               # 5 blocks > max_blocks_per_seq 4
+                              ([a, b], [64, 1], pkv.PKV_EINVAL)):        # fits, but the pool has no caches
+        assert call(ids, counts) == code, (ids, counts, pkv.last_error())
+        assert (pool.stats(), pool.info(a), pool.info(b)) == before
+    # exhaustion: 48 + 64 tokens need 3 + 4 blocks, 6 are free
+    pool2 = pkv.BlockPool(6, 16, 2, 64, pkv.PKV_BF16, 3, 4)
+    x, y = pool2.add(), pool2.add()
+    ids = np.array([x, y], np.int32); counts = np.array([48, 64], np.int32)
+    rc = lib.kv_append_tokens(pool2.handle, 2, ids.ctypes.data, counts.ctypes.data, fake, fake, fake, fake, None)
+    assert rc == pkv.PKV_ENOMEM and pool2.stats()[0] == 6
+    # zero tokens everywhere: nothing to do, no pointer looked at
+    counts0 = np.zeros(2, np.int32)
+    assert lib.kv_append_tokens(pool2.handle, 2, ids.ctypes.data, counts0.ctypes.data, None, None, None, None,
+                                None) == pkv.PKV_OK
+    pool.close(); pool2.close()
