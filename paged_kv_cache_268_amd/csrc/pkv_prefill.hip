@@ -194,10 +194,18 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
     const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache);
 
     // 16-byte piece of token t (d chunk cd), or zeros past the context end.
-    auto fetch = [&](const uint4* base, int t, int cd) {
+    // Block ids of a tile (a 32-key tile spans one block of 32 or two of 16):
+    // lane l loads entry (first + (l & 1)) as a vector load one iteration
+    // before the tile's K/V loads need it, so the table read is off the
+    // critical path; read back with v_readlane.
+    const int last_blk = (n + BS - 1) / BS - 1;
+    auto load_ids = [&](int kt) {
+        return table[min((kt * kPKeys) / BS + (lane & 1), last_blk)];
+    };
+    auto fetch = [&](const uint4* base, int t, int cd, int32_t b0, int32_t b1) {
         uint4 z = make_uint4(0, 0, 0, 0);
         if (t < n) {
-            const int32_t blk = table[t / BS];
+            const int32_t blk = (BS == kPKeys || (t % kPKeys) < BS) ? b0 : b1;
             z = base[(((int64_t)blk * Hkv + g) * BS + t % BS) * CPR + cd];
         }
         return z;
@@ -206,12 +214,13 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
     const int ht = tid & (HT - 1);
     // K half: piece ht + HT c is key (ht + HT c) / CPR, chunk (ht + HT c) % CPR.
     // V half: unit ht + HT c is keys 4 ((ht + HT c) % 8) .. +3, chunk (ht + HT c) / 8.
-    auto gload = [&](int kt, uint4 (&r)[SR]) {
+    auto gload = [&](int kt, int32_t ids, uint4 (&r)[SR]) {
+        const int32_t b0 = __builtin_amdgcn_readlane(ids, 0), b1 = __builtin_amdgcn_readlane(ids, 1);
         if (k_half) {
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
                 const int piece = ht + HT * c;
-                r[c] = fetch(kg, kt * kPKeys + piece / CPR, piece % CPR);
+                r[c] = fetch(kg, kt * kPKeys + piece / CPR, piece % CPR, b0, b1);
             }
         } else {
 #pragma unroll
@@ -219,7 +228,8 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
                 const int u = ht + HT * c;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    r[4 * c + kk] = u < VU ? fetch(vg, kt * kPKeys + 4 * (u % 8) + kk, u / 8) : make_uint4(0, 0, 0, 0);
+                    r[4 * c + kk] = u < VU ? fetch(vg, kt * kPKeys + 4 * (u % 8) + kk, u / 8, b0, b1)
+                                           : make_uint4(0, 0, 0, 0);
             }
         }
     };
@@ -314,14 +324,19 @@ __global__ void __launch_bounds__(kPThreads) paged_prefill_kernel(PrefillArgs a)
     };
 
     uint4 stage[SR];
+    int32_t ids_next = 0;                          // block ids of the tile after the one in flight
     if (NT > 0) {
-        gload(0, stage);
+        gload(0, load_ids(0), stage);
         lstore(0, stage);
     }
+    if (NT > 1) ids_next = load_ids(1);
     __syncthreads();
     for (int kt = 0; kt < NT; ++kt) {
         const int b = kt & 1;
-        if (kt + 1 < NT) gload(kt + 1, stage);
+        if (kt + 1 < NT) {
+            gload(kt + 1, ids_next, stage);
+            if (kt + 2 < NT) ids_next = load_ids(kt + 2);
+        }
         compute(b, kt);
         if (kt + 1 < NT) lstore(b ^ 1, stage);
         __syncthreads();
