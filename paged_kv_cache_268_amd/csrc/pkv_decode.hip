@@ -109,15 +109,11 @@ template <class T, class F> struct Pick<false, T, F> { using type = F; };
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // Four OCP E4M3 codes (bytes of w, low byte first) -> two words of packed
-// bf16, exact: the hardware conversion yields the fp32 values and every E4M3
-// value has at most 4 significant bits, so the top half of each is its bf16.
+// bf16 (codes 0-1, codes 2-3), exact: v_cvt_scalef32_pk_bf16_fp8 with scale 1
+// (every E4M3 value has at most 4 significant bits; checked on all 256 codes).
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-    const bf16x2 pa = {(__bf16)a[0], (__bf16)a[1]};     // exact: at most 4 significant bits
-    const bf16x2 pb = {(__bf16)b[0], (__bf16)b[1]};
-    lo = __builtin_bit_cast(uint32_t, pa);
-    hi = __builtin_bit_cast(uint32_t, pb);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 // Four E4M3 codes -> four floats (exact).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
