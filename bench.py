@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tier", action="store_true", help="skip the host-tier offload/restore measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit K/V decode measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--gpu-window", type=int, default=32, help="blocks each sequence keeps on the GPU when offloaded")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) three times, "
@@ -94,6 +95,7 @@ def measured_traffic(config_id, steps, warmup):
 
 
 HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, per direction
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 
 
 def host_tier_leg(pool, wl, q, k, v, tables, lens, max_ctx, gpu_window, dev):
@@ -218,6 +220,47 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
         "tokens_per_s_decode_only": round(wl.num_seqs / (whole * 1e-3), 1),
         "speedup_vs_16bit_split": None,
         "max_abs_diff_vs_16bit_path": round(err, 5),
+    }
+
+
+def prefill_leg(steps, warmup, dev):
+    """Chunked prefill on the Llama-3-8B GQA shape: 16 sequences, cached prefix U[0, 3584], 512-token chunks."""
+    import torch
+    from paged_kv_cache_268_amd import pkv
+    from paged_kv_cache_268_amd import workloads as W
+    wl, cu = W.llama3_8b_prefill()
+    _, k, v = W.make_values(wl, dev)
+    q = W.make_prefill_q(wl, cu, dev)
+    tab = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(dev)
+    ctx = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(dev)
+    cud = torch.from_numpy(cu).to(dev)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: pkv.prefill(q, k, v, tab, ctx, cud, wl.scale, wl.max_context_len, out=out, stream=stream)
+    for _ in range(warmup):
+        run()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    m = np.diff(cu).astype(np.int64)
+    n = wl.context_lens.astype(np.int64)
+    pairs = int(sum(int((np.arange(n[s] - m[s], n[s]) + 1).sum()) for s in range(wl.num_seqs)))
+    flops = 4 * wl.head_dim * wl.num_q_heads * pairs          # QK and PV, 2 flops per multiply-add
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "kernel": "paged_prefill_kernel",
+        "workload": f"{wl.name}: 16 seqs, 32/8 heads, head_dim 128, block 16, bf16, cached prefix "
+                    f"U[0, 3584] (sum {int((n - m).sum())}), 512-token chunks (total_q {int(cu[-1])})",
+        "ms": round(ms, 4),
+        "tokens_per_s": round(int(cu[-1]) / (ms * 1e-3), 1),
+        "algorithmic_flops_per_launch": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
 
 
@@ -407,6 +450,9 @@ def main():
         log("[bench] 8-bit K/V: quantise the pool, time the 8-bit decode")
         res["fp8_kv"] = fp8_leg(wl, q, k, v, tables, lens, max_ctx, K, Wu, dev)
         res["fp8_kv"]["speedup_vs_16bit_split"] = round(part_ms / res["fp8_kv"]["split_ms"], 3)
+    if not args.no_prefill:
+        log("[bench] chunked prefill leg")
+        res["prefill"] = prefill_leg(20, 3, dev)
     if not args.no_tier:
         log("[bench] host tier: offload past the GPU window, restore, decode check")
         res["host_tier"] = host_tier_leg(pool, wl, q, k, v, tables, lens, max_ctx, args.gpu_window, dev)
