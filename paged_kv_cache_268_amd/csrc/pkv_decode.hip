@@ -23,21 +23,29 @@
 // QK on the matrix core.  The G q heads of the kv group form the B operand of
 // v_mfma_f32_16x16x32 (32 d x 16 heads, heads >= G zero) and stay in
 // registers, so every K row is read once per kv head, not once per q head.
-// The A operand is 16 K rows x 32 d: lane l loads 16 bytes of row l%16, so
-// one wave load instruction reads 64 contiguous bytes of each of the 16 rows.
-// D/32 MFMAs give the 16x16 score tile.
-// Softmax: one running reference max per head for the whole wave; it moves
-// only when a tile's max exceeds it by more than TAU (log2 units), so the
-// accumulator rescale is a rare, scalar-branch event and every weight stays
-// <= 2^TAU.  Rows past the context get weight 0 by selection and their V is
-// zeroed before use, so stale or NaN data in unused slots never reaches a sum.
-// PV on the vector ALUs: V rows are loaded so that LPR = D/8 lanes share a
-// row (16 bytes each) and a wave load instruction reads 1 KiB contiguous; the
-// tile's weights reach these lanes through a 1 KiB per-wave LDS slot.
-// End of a segment (the part of a chunk inside one (s, g)): the row-groups'
-// partial sums add up (shared reference) and the result is either the final
-// output (the segment covers all of (s, g)) or a normalised partial plus its
-// log2-domain lse in the workspace for the merge kernel.
+// The A operand is 16 K rows x 32 d: lane l loads 16 bytes of one row, so one
+// wave load instruction reads 64 contiguous bytes of each of the 16 rows.
+// D/32 MFMAs give the 16x16 score tile.  A-operand row m holds token
+// (m >> 2) + 4 (m & 3) of the tile, so lane l of the result holds the scores
+// of tokens l/16 + 4i (i = 0..3) for head l%16.
+// Softmax: one running reference max per head; it moves only when a tile's
+// max exceeds it by more than TAU (log2 units), so the accumulator rescale is
+// a rare event and every weight stays <= 2^TAU.  Rows past the context get
+// weight 0 by selection and their V is zeroed before use, so stale or NaN
+// data in unused slots never reaches a sum.
+// PV on the matrix core as well, with no data movement between the two: a V
+// row is loaded by 16 lanes (D/16 values each, so a wave load instruction
+// reads 4 whole rows, contiguous), and lane l's four loads of a tile hold
+// tokens l/16 + 4i for d in [D/16 (l%16), D/16 (l%16 + 1)) -- for each of its
+// D/16 values e, exactly the A operand of v_mfma_f32_16x16x16 (16 d rows x 16
+// tokens), while the score layout above is exactly its B operand (16 tokens x
+// 16 heads).  The weights go in as two 16-bit halves (hi + lo, about 16
+// significant bits), so PV is 2 D/16 small MFMAs per tile instead of a long
+// run of vector FMAs.
+// End of a segment (the part of a chunk inside one (s, g)): lane l holds
+// D/4 consecutive output values of head l%16 and the result is either the
+// final output (the segment covers all of (s, g)) or a normalised partial
+// plus its log2-domain lse in the workspace for the merge kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,21 +101,17 @@ __device__ __forceinline__ float xmax32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
     return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
-// Sum over the row-groups of the V layout: lanes with equal l % LPR.
-// LPR = 16: the four DPP rows; LPR = 8: first pair the two halves of each
-// row (DPP row_ror:8 maps lane i to lane i ^ 8 inside a 16-lane row).
-template <int LPR>
-__device__ __forceinline__ float rowgroup_sum(float x) {
-    if constexpr (LPR == 8)
-        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-    return xsum32(xsum16(x));
-}
-
 template <bool C, class T, class F> struct Pick { using type = T; };
 template <class T, class F> struct Pick<false, T, F> { using type = F; };
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
+// Two OCP E4M3 codes (bytes 0-1 of w, or bytes 2-3 with HI) -> one word of
+// packed bf16, exact (v_cvt_scalef32_pk_bf16_fp8, scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 // Four OCP E4M3 codes (bytes of w, low byte first) -> two words of packed
 // bf16 (codes 0-1, codes 2-3), exact: v_cvt_scalef32_pk_bf16_fp8 with scale 1
 // (every E4M3 value has at most 4 significant bits; checked on all 256 codes).
@@ -115,24 +119,52 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
     lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
-// Four E4M3 codes -> four floats (exact).
-__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
-    const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// C += A(16x16) * B(16x16), fp32 accumulate (v_mfma_f32_16x16x16_{bf16,f16});
+// a and b: four packed 16-bit values, the lane's k = 4 (l/16) .. 4 (l/16) + 3.
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma_16x16x16(uint2 a, uint2 b, floatx4 c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// Two packed 16-bit values -> two floats (exact widening).
+// Two floats -> their 16-bit roundings (hi, packed) and the roundings of what
+// is left (lo, packed): x = hi + lo to within 2^-18 |x| (bf16) or 2^-22 |x|
+// (f16, x in the normal range).
 template <bool BF16>
-__device__ __forceinline__ void widen2(uint32_t w, float& lo, float& hi) {
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     if constexpr (BF16) {
-        lo = __builtin_bit_cast(float, w << 16);
-        hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+        const bf16x2 l = {(__bf16)(x0 - (float)h.x), (__bf16)(x1 - (float)h.y)};
+        hi = __builtin_bit_cast(uint32_t, h);
+        lo = __builtin_bit_cast(uint32_t, l);
     } else {
-        f16x2 h = __builtin_bit_cast(f16x2, w);
-        lo = (float)h.x;
-        hi = (float)h.y;
+        const f16x2 h = {(_Float16)x0, (_Float16)x1};
+        const f16x2 l = {(_Float16)(x0 - (float)h.x), (_Float16)(x1 - (float)h.y)};
+        hi = __builtin_bit_cast(uint32_t, h);
+        lo = __builtin_bit_cast(uint32_t, l);
     }
+}
+
+// A lane's piece of one V row: NW 32-bit words.
+template <int NW> struct VPiece { uint32_t w[NW]; };
+template <int NW>
+__device__ __forceinline__ VPiece<NW> load_piece(const void* p) {
+    VPiece<NW> v;
+    if constexpr (NW == 4) {
+        const uint4 t = *reinterpret_cast<const uint4*>(p);
+        v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
+    } else if constexpr (NW == 2) {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        v.w[0] = t.x; v.w[1] = t.y;
+    } else {
+        v.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return v;
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -190,18 +222,22 @@ __global__ void __launch_bounds__(kThreads)
 paged_decode_split_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;            // MFMA k-steps per tile
     constexpr int KL = KV8 ? D / 64 : KS; // K load instructions per tile (16 bytes per lane each)
-    constexpr int LPR = D / 8;            // V: lanes per row (8 values per lane)
-    constexpr int RPI = 64 / LPR;         // V: rows per wave load instruction
-    constexpr int NI = kTile / RPI;       // V: load instructions per tile
-    static_assert(NI * RPI == kTile && GP <= 16, "tile shape");
+    constexpr int EPL = D / 16;           // V: values per lane of a row (16 lanes per row)
+    constexpr int NW = EPL * (KV8 ? 1 : 2) / 4;   // V: 32-bit words per lane of a row
+    constexpr int NI = 4;                 // V: load instructions per tile (4 rows each)
+    static_assert(GP <= 16, "kv group of at most 16 q heads");
     static_assert(!KV8 || BF16, "8-bit K/V pair with a bf16 query");
+    static_assert(NW == 1 || NW == 2 || NW == 4, "V piece of 4, 8 or 16 bytes");
     using MfmaIn = typename MfmaType<BF16>::vec;
-    using VLoad = typename Pick<KV8, uint2, uint4>::type;   // one lane's 8 V values
+    using VLoad = VPiece<NW>;
     constexpr int DEPTH = 2;              // tiles in flight per wave
+    static_assert(128 % DEPTH == 0, "a block-id window of 128 tiles holds whole pipeline steps");
+    // f16 weights go to PV times 2^7 (<= 2^15 with TAU = 8), clear of the f16
+    // subnormal range; the output divides it out.
+    constexpr float kPScale = BF16 ? 1.f : 128.f;
 
     __shared__ int s_pre[kMaxSeqs + 1];
     __shared__ int s_wsum[kWaves];
-    __shared__ float s_p[kWaves][kTile][16];   // p[token][head] of the current tile, per wave
 
     const int lane = threadIdx.x & 63;
     // Wave index as a uniform (scalar) value, so loops stay scalar.
@@ -259,9 +295,8 @@ paged_decode_split_kernel(DecodeArgs a) {
     // 32-wide k-step, and receives C[4*(l/16) + i][l%16], i = 0..3.
     const int mrow = lane & 15;           // K row (token in tile) / head of B and C
     const int kq = lane >> 4;             // d-chunk of the k-step / token quad of C
-    // V layout: LPR lanes share a row, lane owns the 8 values [8c, 8c+8).
-    const int c = lane % LPR;
-    const int r = lane / LPR;
+    // V layout: 16 lanes share a row; lane l owns the EPL values
+    // [EPL (l%16), EPL (l%16 + 1)) of rows l/16 + 4i, i = 0..3.
     const float sl2 = a.scale * kLog2e;
     using KvElem = typename Pick<KV8, uint8_t, uint16_t>::type;
     const KvElem* kc = reinterpret_cast<const KvElem*>(a.k_cache);
@@ -270,8 +305,9 @@ paged_decode_split_kernel(DecodeArgs a) {
     // 8-bit values a lane loads 16 codes, d in [16 cq, 16 cq + 16) with
     // cq = 4 u + kq, which feed k-steps 2u and 2u + 1; the q operand follows
     // the same d order, so the dot products are unchanged.
-    const int k_off = KV8 ? mrow * D + kq * 16 : mrow * D + kq * 8;
-    const int v_off = r * D + c * 8;      // lane's V element offset inside a tile (+ i * RPI * D)
+    const int krow = (mrow >> 2) + 4 * (mrow & 3);   // token of A-operand row mrow
+    const int k_off = KV8 ? krow * D + kq * 16 : krow * D + kq * 8;
+    const int v_off = kq * D + mrow * EPL;    // lane's V element offset inside a tile (+ i * 4 * D)
 
     // One segment: tiles [j0, j1) of kv head g of sequence s.
     auto run_segment = [&](int s, int g, int j0, int j1, int slot, bool direct) {
@@ -291,16 +327,14 @@ paged_decode_split_kernel(DecodeArgs a) {
             }
             qb[ks] = __builtin_bit_cast(MfmaIn, w);
         }
-        // Softmax state.  m[h]: one reference per head shared by the whole
-        // wave (uniform); m_lane = m[l%16] for the lanes of real heads (0
-        // elsewhere); l_lane: weight sums in the score layout; acc: V layout.
-        float m[GP], acc[GP][8];
+        // Softmax state, per lane for head l%16 (equal in the 4 lanes of a
+        // head): m_lane the reference (-inf before the first tile, 0 for the
+        // padding heads >= G), l_lane the sum of this lane's weights, acc[e]
+        // rows 4 (l/16) + i of PV MFMA e, i.e. output values
+        // d = EPL (4 (l/16) + i) + e of head l%16.
+        floatx4 acc[EPL];
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            m[h] = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        }
+        for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
         float m_lane = mrow < G ? -INFINITY : 0.f;
         float l_lane = 0.f;
         const int32_t* table = a.block_tables + (int64_t)s * a.table_stride;
@@ -308,12 +342,13 @@ paged_decode_split_kernel(DecodeArgs a) {
         auto tile_base = [&](int j, int32_t blk) -> int64_t {
             return (((int64_t)blk * Hkv + g) * BS + (j * kTile) % BS) * D;
         };
-        // QK on the matrix core, then the online-softmax update; the tile's
-        // weights go to this wave's LDS slot.  8-bit K: codes widened to bf16
-        // in registers, the tile's K scale folded into the score scale and
-        // its V scale into the weights written for PV (the weight sum l keeps
-        // the unscaled weights).
-        auto qk_softmax = [&](int j, const uint4 (&kb)[KL], float ksc, float vsc) {
+        // QK on the matrix core, then the online-softmax update.  The tile's
+        // weights come back in the B-operand layout of the PV MFMAs, split
+        // into 16-bit hi and lo parts, times the tile's V scale (8-bit V) or
+        // kPScale (the weight sum l keeps the unscaled weights).  8-bit K:
+        // codes widened to bf16 in registers, the tile's K scale folded into
+        // the score scale.
+        auto qk_softmax = [&](int j, const uint4 (&kb)[KL], float ksc, float vsc, uint2& phi, uint2& plo) {
             const int t0 = j * kTile;
             const bool full = t0 + kTile <= ctx;
             floatx4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -338,7 +373,7 @@ paged_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 x[i] = sc[i] * sk;
-                if (!full && t0 + 4 * kq + i >= ctx) x[i] = -INFINITY;
+                if (!full && t0 + kq + 4 * i >= ctx) x[i] = -INFINITY;
                 need |= x[i] > m_lane + kTau;
             }
             // Rare path: some score exceeds its head's reference by more than TAU.
@@ -346,70 +381,75 @@ paged_decode_split_kernel(DecodeArgs a) {
                 float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                 mx = xmax16(mx);
                 mx = xmax32(mx);                    // lane (j, n): tile max of head n
+                if (mrow < G && mx > m_lane + kTau) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_lane - mx);   // 0 when m = -inf
 #pragma unroll
-                for (int h = 0; h < GP; ++h) {
-                    if (h < G) {
-                        const float mt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), h));
-                        if (mt > m[h] + kTau) {
-                            const float alpha = __builtin_amdgcn_exp2f(m[h] - mt);   // 0 when m = -inf
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-                            l_lane = (mrow == h) ? l_lane * alpha : l_lane;
-                            m_lane = (mrow == h) ? mt : m_lane;
-                            m[h] = mt;
-                        }
-                    }
+                    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+                    l_lane *= alpha;
+                    m_lane = mx;
                 }
             }
             // Weights <= 2^TAU; a row past the context has x = -inf and weight 0.
+            const float pm = KV8 ? vsc : kPScale;
+            float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float e = __builtin_amdgcn_exp2f(x[i] - m_lane);
                 l_lane += e;
-                s_p[wave][4 * kq + i][mrow] = KV8 ? e * vsc : e;
+                p[i] = e * pm;
             }
-            __builtin_amdgcn_wave_barrier();
+            split2<BF16>(p[0], p[1], phi.x, plo.x);
+            split2<BF16>(p[2], p[3], phi.y, plo.y);
         };
-        // PV on the vector ALUs, V rows in the coalesced layout.
-        auto pv = [&](int j, const VLoad (&vb)[NI]) {
+        // PV on the matrix core.  For each of the lane's EPL values e the A
+        // operand is (V[l/16][e], V[l/16 + 4][e], V[l/16 + 8][e], V[l/16 + 12][e])
+        // of the tile in 16-bit form; the weights' hi parts, then lo parts,
+        // are the B operand.
+        auto pv = [&](int j, const VLoad (&vb)[NI], uint2 phi, uint2 plo) {
             const int t0 = j * kTile;
             const bool full = t0 + kTile <= ctx;
+            uint32_t w[NI][NW];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int row = i * RPI + r;
-                float ph[GP];
-                if constexpr (GP >= 4) {
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
-                    for (int h4 = 0; h4 < GP; h4 += 4) {
-                        const float4 q4 = *reinterpret_cast<const float4*>(&s_p[wave][row][h4]);
-                        ph[h4] = q4.x; ph[h4 + 1] = q4.y; ph[h4 + 2] = q4.z; ph[h4 + 3] = q4.w;
-                    }
-                } else {
+                for (int k = 0; k < NW; ++k) w[i][k] = vb[i].w[k];
+            if (!full) {
+                // Unused slots may hold anything (NaN included): never let them into a sum.
 #pragma unroll
-                    for (int h = 0; h < GP; ++h) ph[h] = s_p[wave][row][h];
-                }
-                float vf[8];
-                if constexpr (KV8) {
-                    fp8x4_to_f32(vb[i].x, vf);
-                    fp8x4_to_f32(vb[i].y, vf + 4);
-                } else {
-                    widen2<BF16>(vb[i].x, vf[0], vf[1]);
-                    widen2<BF16>(vb[i].y, vf[2], vf[3]);
-                    widen2<BF16>(vb[i].z, vf[4], vf[5]);
-                    widen2<BF16>(vb[i].w, vf[6], vf[7]);
-                }
-                if (!full) {
-                    // Unused slots may hold anything (NaN included): never let them into a sum.
-                    const bool valid = t0 + row < ctx;
+                for (int i = 0; i < NI; ++i)
+                    if (t0 + kq + 4 * i >= ctx)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vf[e] = valid ? vf[e] : 0.f;
-                }
-#pragma unroll
-                for (int h = 0; h < GP; ++h)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[h], vf[e], acc[h][e]);
+                        for (int k = 0; k < NW; ++k) w[i][k] = 0u;
             }
-            __builtin_amdgcn_wave_barrier();
+            uint2 av[EPL];
+            if constexpr (KV8) {
+                // Codes 4k .. 4k + 3 of the four rows: interleave rows (0, 1) and
+                // (2, 3) byte by byte, then v_cvt_scalef32_pk_bf16_fp8 (scale 1,
+                // exact) turns each pair of codes into the bf16 pair of one word.
+#pragma unroll
+                for (int k = 0; k < NW; ++k) {
+                    const uint32_t c01 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x05010400u);   // codes 0, 1
+                    const uint32_t c23 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x07030602u);   // codes 2, 3
+                    const uint32_t d01 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x05010400u);
+                    const uint32_t d23 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x07030602u);
+                    av[4 * k + 0] = make_uint2(fp8x2_to_bf16x2<false>(c01), fp8x2_to_bf16x2<false>(d01));
+                    av[4 * k + 1] = make_uint2(fp8x2_to_bf16x2<true>(c01), fp8x2_to_bf16x2<true>(d01));
+                    av[4 * k + 2] = make_uint2(fp8x2_to_bf16x2<false>(c23), fp8x2_to_bf16x2<false>(d23));
+                    av[4 * k + 3] = make_uint2(fp8x2_to_bf16x2<true>(c23), fp8x2_to_bf16x2<true>(d23));
+                }
+            } else {
+                // Value e is half e & 1 of word e >> 1: pair it across rows (0, 1) and (2, 3).
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    av[e] = make_uint2(__builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel),
+                                       __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel));
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], phi, acc[e]);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], plo, acc[e]);
         };
         auto load_k = [&](int j, int32_t blk, uint4 (&kb)[KL]) {
             const int64_t base = tile_base(j, blk);
@@ -421,7 +461,7 @@ paged_decode_split_kernel(DecodeArgs a) {
         auto load_v = [&](int j, int32_t blk, VLoad (&vb)[NI]) {
             const int64_t base = tile_base(j, blk);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const VLoad*>(vc + base + v_off + i * RPI * D);
+            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW>(vc + base + v_off + i * 4 * D);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -472,44 +512,37 @@ paged_decode_split_kernel(DecodeArgs a) {
             for (int it = 0; it < cn; it += DEPTH) {
 #pragma unroll
                 for (int st = 0; st < DEPTH; ++st) {
-                    qk_softmax(c0 + it + st, kbuf[st], lane_pick(kslo, kshi, it + st), lane_pick(vslo, vshi, it + st));
+                    uint2 phi, plo;
+                    qk_softmax(c0 + it + st, kbuf[st], lane_pick(kslo, kshi, it + st), lane_pick(vslo, vshi, it + st), phi, plo);
                     load_k(tile(it + st + DEPTH), blk(it + st + DEPTH), kbuf[st]);
-                    pv(c0 + it + st, vbuf[st]);
+                    pv(c0 + it + st, vbuf[st], phi, plo);
                     load_v(tile(it + st + DEPTH), blk(it + st + DEPTH), vbuf[st]);
                 }
             }
         }
 
-        // ---- segment totals: l per head (score layout), acc over row-groups ----
+        // ---- segment totals: l per head; lane l holds D/4 values of head l%16 ----
         l_lane = xsum32(xsum16(l_lane));           // lane (j, n): total of head n
+        if (mrow < G) {
+            const float inv = 1.f / (l_lane * kPScale);   // l >= 1: the tile that set the reference has weight 1
+            const float lse2 = m_lane + __builtin_amdgcn_logf(l_lane);
+            const int64_t sh = (int64_t)s * a.num_q_heads + h0 + mrow;
+            const int d0 = 4 * EPL * kq;           // acc[e][i] is value d0 + EPL i + e
+            if (direct) {
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = rowgroup_sum<LPR>(acc[h][e]);
+                    for (int e = 0; e < EPL; ++e) store_out(a.out, sh * D + d0 + EPL * i + e, acc[e][i] * inv, a.out_dtype);
+                if (kq == 0 && a.lse) a.lse[sh] = lse2 * kLn2;
+            } else {
+                float* o = a.ws_out + (sh * a.max_seg + slot) * D + d0;
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            if (h < G) {
-                const float L = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), h));
-                const float inv = 1.f / L;            // L >= 1: the tile that set m[h] has weight 1
-                const float lse2 = m[h] + __builtin_amdgcn_logf(L);
-                const int64_t sh = (int64_t)s * a.num_q_heads + h0 + h;
-                if (r == 0) {
-                    if (direct) {
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) store_out(a.out, sh * D + c * 8 + e, acc[h][e] * inv, a.out_dtype);
-                    } else {
-                        float* o = a.ws_out + (sh * a.max_seg + slot) * D + c * 8;
-                        *reinterpret_cast<float4*>(o) = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-                        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
-                    }
-                }
-                if (lane == 0) {
-                    if (direct) {
-                        if (a.lse) a.lse[sh] = lse2 * kLn2;
-                    } else {
-                        a.ws_lse[sh * a.max_seg + slot] = lse2;
-                    }
-                }
+                    for (int e = 0; e < EPL; e += 4)
+                        *reinterpret_cast<float4*>(o + EPL * i + e) =
+                            make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv);
+                if (kq == 0) a.ws_lse[sh * a.max_seg + slot] = lse2;
             }
         }
     };
