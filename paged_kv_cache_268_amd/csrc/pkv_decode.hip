@@ -196,12 +196,13 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
     return i;
 }
 
-// Tiles of one kv head of sequence s (16 tokens each), and the same count
-// padded to whole chunks when the chunk size is fixed.
-__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int s) {
-    const int n = min(max(a.context_lens[s], 0), a.max_context_len);
-    return (n + kTile - 1) / kTile;
+// Context length of sequence s as the kernels use it (clamped to
+// [0, max_context_len]); tiles of one kv head of it (16 tokens each), and the
+// same count padded to whole chunks when the chunk size is fixed.
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
+    return min(max(a.context_lens[s], 0), a.max_context_len);
 }
+__device__ __forceinline__ int len_tiles(int n) { return (n + kTile - 1) / kTile; }
 __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
     return fixed_chunk > 0 ? (nt + fixed_chunk - 1) / fixed_chunk * fixed_chunk : nt;
 }
@@ -231,12 +232,13 @@ paged_decode_split_kernel(DecodeArgs a) {
     using MfmaIn = typename MfmaType<BF16>::vec;
     using VLoad = VPiece<NW>;
     constexpr int DEPTH = 2;              // tiles in flight per wave
-    static_assert(128 % DEPTH == 0, "a block-id window of 128 tiles holds whole pipeline steps");
+    static_assert(128 % DEPTH == 0, "a window of 128 positions holds whole pipeline steps");
     // f16 weights go to PV times 2^7 (<= 2^15 with TAU = 8), clear of the f16
     // subnormal range; the output divides it out.
     constexpr float kPScale = BF16 ? 1.f : 128.f;
 
     __shared__ int s_pre[kMaxSeqs + 1];
+    __shared__ int s_len[kMaxSeqs];       // clamped context lengths, read once per workgroup
     __shared__ int s_wsum[kWaves];
 
     const int lane = threadIdx.x & 63;
@@ -248,7 +250,9 @@ paged_decode_split_kernel(DecodeArgs a) {
     int running = 0;
     for (int base = 0; base < B; base += kThreads) {
         const int s = base + (int)threadIdx.x;
-        const int v = s < B ? padded_tiles(seq_tiles(a, s), a.fixed_chunk) : 0;
+        const int n = s < B ? seq_len(a, s) : 0;
+        if (s < B) s_len[s] = n;
+        const int v = padded_tiles(len_tiles(n), a.fixed_chunk);
         int x = v;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -309,270 +313,314 @@ paged_decode_split_kernel(DecodeArgs a) {
     const int k_off = KV8 ? krow * D + kq * 16 : krow * D + kq * 8;
     const int v_off = kq * D + mrow * EPL;    // lane's V element offset inside a tile (+ i * 4 * D)
 
-    // One segment: tiles [j0, j1) of kv head g of sequence s.
-    auto run_segment = [&](int s, int g, int j0, int j1, int slot, bool direct) {
-        // Tokens this segment owns end here: at the context end or at the
-        // segment's last tile, whichever is first.
-        const int ctx = min(min(max(a.context_lens[s], 0), a.max_context_len), j1 * kTile);
-        const int h0 = g * G;
-        MfmaIn qb[KS];
+    // Softmax state of the current segment, per lane for head l%16 (equal in
+    // the 4 lanes of a head): m_lane the reference (-inf before the first
+    // tile, 0 for the padding heads >= G), l_lane the sum of this lane's
+    // weights, acc[e] rows 4 (l/16) + i of PV MFMA e, i.e. output values
+    // d = EPL (4 (l/16) + i) + e of head l%16.
+    floatx4 acc[EPL];
+    float m_lane = 0.f, l_lane = 0.f;
+    int seg_s = 0, seg_g = 0, seg_ctx = 0, seg_nt = 0, seg_slot = 0;
+    bool seg_direct = false;
+
+    auto tile_base = [&](int j, int g, int32_t blk) -> int64_t {
+        return (((int64_t)blk * Hkv + g) * BS + (j * kTile) % BS) * D;
+    };
+    // QK on the matrix core, then the online-softmax update.  The tile's
+    // weights come back in the B-operand layout of the PV MFMAs, split into
+    // 16-bit hi and lo parts, times the tile's V scale (8-bit V) or kPScale
+    // (the weight sum l keeps the unscaled weights).  8-bit K: codes widened
+    // to bf16 in registers, the tile's K scale folded into the score scale.
+    auto qk_softmax = [&](int j, const uint4 (&kb)[KL], const MfmaIn (&qb)[KS], float ksc, float vsc, uint2& phi,
+                          uint2& plo) {
+        const int t0 = j * kTile;
+        const bool full = t0 + kTile <= seg_ctx;
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KV8) {
+#pragma unroll
+            for (int u = 0; u < KL; ++u) {
+                uint4 lo, hi;
+                fp8x4_to_bf16x4(kb[u].x, lo.x, lo.y);
+                fp8x4_to_bf16x4(kb[u].y, lo.z, lo.w);
+                fp8x4_to_bf16x4(kb[u].z, hi.x, hi.y);
+                fp8x4_to_bf16x4(kb[u].w, hi.z, hi.w);
+                sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, lo), qb[2 * u], sc);
+                sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, hi), qb[2 * u + 1], sc);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
+        }
+        const float sk = KV8 ? sl2 * ksc : sl2;
+        float x[4];
+        bool need = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = sc[i] * sk;
+            if (!full && t0 + kq + 4 * i >= seg_ctx) x[i] = -INFINITY;
+            need |= x[i] > m_lane + kTau;
+        }
+        // Rare path: some score exceeds its head's reference by more than TAU.
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx = xmax16(mx);
+            mx = xmax32(mx);                    // lane (j, n): tile max of head n
+            if (mrow < G && mx > m_lane + kTau) {
+                const float alpha = __builtin_amdgcn_exp2f(m_lane - mx);   // 0 when m = -inf
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+                l_lane *= alpha;
+                m_lane = mx;
+            }
+        }
+        // Weights <= 2^TAU; a row past the context has x = -inf and weight 0.
+        const float pm = KV8 ? vsc : kPScale;
+        float pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(x[i] - m_lane);
+            l_lane += e;
+            pw[i] = e * pm;
+        }
+        split2<BF16>(pw[0], pw[1], phi.x, plo.x);
+        split2<BF16>(pw[2], pw[3], phi.y, plo.y);
+    };
+    // PV on the matrix core.  For each of the lane's EPL values e the A
+    // operand is (V[l/16][e], V[l/16 + 4][e], V[l/16 + 8][e], V[l/16 + 12][e])
+    // of the tile in 16-bit form; the weights' hi parts, then lo parts, are
+    // the B operand.
+    auto pv = [&](int j, const VLoad (&vb)[NI], uint2 phi, uint2 plo) {
+        const int t0 = j * kTile;
+        const bool full = t0 + kTile <= seg_ctx;
+        uint32_t w[NI][NW];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int k = 0; k < NW; ++k) w[i][k] = vb[i].w[k];
+        if (!full) {
+            // Unused slots may hold anything (NaN included): never let them into a sum.
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                if (t0 + kq + 4 * i >= seg_ctx)
+#pragma unroll
+                    for (int k = 0; k < NW; ++k) w[i][k] = 0u;
+        }
+        uint2 av[EPL];
+        if constexpr (KV8) {
+            // Codes 4k .. 4k + 3 of the four rows: interleave rows (0, 1) and
+            // (2, 3) byte by byte, then v_cvt_scalef32_pk_bf16_fp8 (scale 1,
+            // exact) turns each pair of codes into the bf16 pair of one word.
+#pragma unroll
+            for (int k = 0; k < NW; ++k) {
+                const uint32_t c01 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x05010400u);   // codes 0, 1
+                const uint32_t c23 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x07030602u);   // codes 2, 3
+                const uint32_t d01 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x05010400u);
+                const uint32_t d23 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x07030602u);
+                av[4 * k + 0] = make_uint2(fp8x2_to_bf16x2<false>(c01), fp8x2_to_bf16x2<false>(d01));
+                av[4 * k + 1] = make_uint2(fp8x2_to_bf16x2<true>(c01), fp8x2_to_bf16x2<true>(d01));
+                av[4 * k + 2] = make_uint2(fp8x2_to_bf16x2<false>(c23), fp8x2_to_bf16x2<false>(d23));
+                av[4 * k + 3] = make_uint2(fp8x2_to_bf16x2<true>(c23), fp8x2_to_bf16x2<true>(d23));
+            }
+        } else {
+            // Value e is half e & 1 of word e >> 1: pair it across rows (0, 1) and (2, 3).
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                av[e] = make_uint2(__builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel),
+                                   __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], phi, acc[e]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], plo, acc[e]);
+    };
+    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[KL]) {
+        const int64_t base = tile_base(j, g, blk);
+#pragma unroll
+        for (int u = 0; u < KL; ++u)
+            kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[NI]) {
+        const int64_t base = tile_base(j, g, blk);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW>(vc + base + v_off + i * 4 * D);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The q rows of kv group g of sequence s, as the QK B operand.
+    auto load_q = [&](int s, int g, MfmaIn (&qb)[KS]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (mrow < G) {
                 const int d0 = KV8 ? 16 * (4 * (ks / 2) + kq) + 8 * (ks % 2) : ks * 32 + kq * 8;
                 const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                                     ((int64_t)s * a.num_q_heads + h0 + mrow) * D + d0;
+                                     ((int64_t)s * a.num_q_heads + g * G + mrow) * D + d0;
                 w = *reinterpret_cast<const uint4*>(qp);
             }
             qb[ks] = __builtin_bit_cast(MfmaIn, w);
         }
-        // Softmax state, per lane for head l%16 (equal in the 4 lanes of a
-        // head): m_lane the reference (-inf before the first tile, 0 for the
-        // padding heads >= G), l_lane the sum of this lane's weights, acc[e]
-        // rows 4 (l/16) + i of PV MFMA e, i.e. output values
-        // d = EPL (4 (l/16) + i) + e of head l%16.
-        floatx4 acc[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-        float m_lane = mrow < G ? -INFINITY : 0.f;
-        float l_lane = 0.f;
-        const int32_t* table = a.block_tables + (int64_t)s * a.table_stride;
-
-        auto tile_base = [&](int j, int32_t blk) -> int64_t {
-            return (((int64_t)blk * Hkv + g) * BS + (j * kTile) % BS) * D;
-        };
-        // QK on the matrix core, then the online-softmax update.  The tile's
-        // weights come back in the B-operand layout of the PV MFMAs, split
-        // into 16-bit hi and lo parts, times the tile's V scale (8-bit V) or
-        // kPScale (the weight sum l keeps the unscaled weights).  8-bit K:
-        // codes widened to bf16 in registers, the tile's K scale folded into
-        // the score scale.
-        auto qk_softmax = [&](int j, const uint4 (&kb)[KL], float ksc, float vsc, uint2& phi, uint2& plo) {
-            const int t0 = j * kTile;
-            const bool full = t0 + kTile <= ctx;
-            floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (KV8) {
-#pragma unroll
-                for (int u = 0; u < KL; ++u) {
-                    uint4 lo, hi;
-                    fp8x4_to_bf16x4(kb[u].x, lo.x, lo.y);
-                    fp8x4_to_bf16x4(kb[u].y, lo.z, lo.w);
-                    fp8x4_to_bf16x4(kb[u].z, hi.x, hi.y);
-                    fp8x4_to_bf16x4(kb[u].w, hi.z, hi.w);
-                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, lo), qb[2 * u], sc);
-                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, hi), qb[2 * u + 1], sc);
-                }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
-            }
-            const float sk = KV8 ? sl2 * ksc : sl2;
-            float x[4];
-            bool need = false;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = sc[i] * sk;
-                if (!full && t0 + kq + 4 * i >= ctx) x[i] = -INFINITY;
-                need |= x[i] > m_lane + kTau;
-            }
-            // Rare path: some score exceeds its head's reference by more than TAU.
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                mx = xmax16(mx);
-                mx = xmax32(mx);                    // lane (j, n): tile max of head n
-                if (mrow < G && mx > m_lane + kTau) {
-                    const float alpha = __builtin_amdgcn_exp2f(m_lane - mx);   // 0 when m = -inf
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-                    l_lane *= alpha;
-                    m_lane = mx;
-                }
-            }
-            // Weights <= 2^TAU; a row past the context has x = -inf and weight 0.
-            const float pm = KV8 ? vsc : kPScale;
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = __builtin_amdgcn_exp2f(x[i] - m_lane);
-                l_lane += e;
-                p[i] = e * pm;
-            }
-            split2<BF16>(p[0], p[1], phi.x, plo.x);
-            split2<BF16>(p[2], p[3], phi.y, plo.y);
-        };
-        // PV on the matrix core.  For each of the lane's EPL values e the A
-        // operand is (V[l/16][e], V[l/16 + 4][e], V[l/16 + 8][e], V[l/16 + 12][e])
-        // of the tile in 16-bit form; the weights' hi parts, then lo parts,
-        // are the B operand.
-        auto pv = [&](int j, const VLoad (&vb)[NI], uint2 phi, uint2 plo) {
-            const int t0 = j * kTile;
-            const bool full = t0 + kTile <= ctx;
-            uint32_t w[NI][NW];
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-#pragma unroll
-                for (int k = 0; k < NW; ++k) w[i][k] = vb[i].w[k];
-            if (!full) {
-                // Unused slots may hold anything (NaN included): never let them into a sum.
-#pragma unroll
-                for (int i = 0; i < NI; ++i)
-                    if (t0 + kq + 4 * i >= ctx)
-#pragma unroll
-                        for (int k = 0; k < NW; ++k) w[i][k] = 0u;
-            }
-            uint2 av[EPL];
-            if constexpr (KV8) {
-                // Codes 4k .. 4k + 3 of the four rows: interleave rows (0, 1) and
-                // (2, 3) byte by byte, then v_cvt_scalef32_pk_bf16_fp8 (scale 1,
-                // exact) turns each pair of codes into the bf16 pair of one word.
-#pragma unroll
-                for (int k = 0; k < NW; ++k) {
-                    const uint32_t c01 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x05010400u);   // codes 0, 1
-                    const uint32_t c23 = __builtin_amdgcn_perm(w[1][k], w[0][k], 0x07030602u);   // codes 2, 3
-                    const uint32_t d01 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x05010400u);
-                    const uint32_t d23 = __builtin_amdgcn_perm(w[3][k], w[2][k], 0x07030602u);
-                    av[4 * k + 0] = make_uint2(fp8x2_to_bf16x2<false>(c01), fp8x2_to_bf16x2<false>(d01));
-                    av[4 * k + 1] = make_uint2(fp8x2_to_bf16x2<true>(c01), fp8x2_to_bf16x2<true>(d01));
-                    av[4 * k + 2] = make_uint2(fp8x2_to_bf16x2<false>(c23), fp8x2_to_bf16x2<false>(d23));
-                    av[4 * k + 3] = make_uint2(fp8x2_to_bf16x2<true>(c23), fp8x2_to_bf16x2<true>(d23));
-                }
-            } else {
-                // Value e is half e & 1 of word e >> 1: pair it across rows (0, 1) and (2, 3).
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    av[e] = make_uint2(__builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel),
-                                       __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel));
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], phi, acc[e]);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], plo, acc[e]);
-        };
-        auto load_k = [&](int j, int32_t blk, uint4 (&kb)[KL]) {
-            const int64_t base = tile_base(j, blk);
-#pragma unroll
-            for (int u = 0; u < KL; ++u)
-                kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        auto load_v = [&](int j, int32_t blk, VLoad (&vb)[NI]) {
-            const int64_t base = tile_base(j, blk);
-#pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW>(vc + base + v_off + i * 4 * D);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-
-        // DEPTH K and DEPTH V register buffers: the loads of tile j + DEPTH are
-        // issued as soon as tile j's K (after QK) or V (after PV) is consumed,
-        // so DEPTH tiles stay in flight per wave.  (Four tiles in flight for
-        // 8-bit K/V, the same bytes as two 16-bit tiles, measured slower: that
-        // kernel is limited by its per-tile vector work, not by latency.)
-        // Loads past the window's last tile re-read that tile (in bounds,
-        // served by the cache); a window whose tile count is not a multiple
-        // of DEPTH ends with tiles past the segment, which every row treats as
-        // outside the context (weight 0, V never used).  Block ids
-        // come 128 tiles at a time, two per lane, read back with v_readlane;
-        // with 8-bit K/V each lane also loads the K and V scales of its two
-        // blocks (vector loads: they stay in order with the tile loads).
-        for (int c0 = j0; c0 < j1; c0 += 128) {
-            const int cn = min(128, j1 - c0);
-            const int32_t blo = lane < cn ? table[((c0 + lane) * kTile) / BS] : 0;
-            const int32_t bhi = lane + 64 < cn ? table[((c0 + 64 + lane) * kTile) / BS] : 0;
-            float kslo = 1.f, kshi = 1.f, vslo = 1.f, vshi = 1.f;
-            if constexpr (KV8) {
-                if (lane < cn) {
-                    kslo = a.k_scale[(int64_t)blo * Hkv + g];
-                    vslo = a.v_scale[(int64_t)blo * Hkv + g];
-                }
-                if (lane + 64 < cn) {
-                    kshi = a.k_scale[(int64_t)bhi * Hkv + g];
-                    vshi = a.v_scale[(int64_t)bhi * Hkv + g];
-                }
-            }
-            auto blk = [&](int it) {
-                const int i = min(it, cn - 1);
-                return i < 64 ? __builtin_amdgcn_readlane(blo, i) : __builtin_amdgcn_readlane(bhi, i - 64);
-            };
-            auto lane_pick = [&](float lo, float hi, int it) {
-                const int i = min(it, cn - 1);
-                return __builtin_bit_cast(float, i < 64 ? __builtin_amdgcn_readlane(__builtin_bit_cast(int, lo), i)
-                                                        : __builtin_amdgcn_readlane(__builtin_bit_cast(int, hi), i - 64));
-            };
-            auto tile = [&](int it) { return c0 + min(it, cn - 1); };
-            uint4 kbuf[DEPTH][KL];
-            VLoad vbuf[DEPTH][NI];
-#pragma unroll
-            for (int st = 0; st < DEPTH; ++st) {
-                load_k(tile(st), blk(st), kbuf[st]);
-                load_v(tile(st), blk(st), vbuf[st]);
-            }
-            for (int it = 0; it < cn; it += DEPTH) {
-#pragma unroll
-                for (int st = 0; st < DEPTH; ++st) {
-                    uint2 phi, plo;
-                    qk_softmax(c0 + it + st, kbuf[st], lane_pick(kslo, kshi, it + st), lane_pick(vslo, vshi, it + st), phi, plo);
-                    load_k(tile(it + st + DEPTH), blk(it + st + DEPTH), kbuf[st]);
-                    pv(c0 + it + st, vbuf[st], phi, plo);
-                    load_v(tile(it + st + DEPTH), blk(it + st + DEPTH), vbuf[st]);
-                }
-            }
-        }
-
-        // ---- segment totals: l per head; lane l holds D/4 values of head l%16 ----
-        l_lane = xsum32(xsum16(l_lane));           // lane (j, n): total of head n
+    };
+    // End of a segment: l per head; lane l holds D/4 values of head l%16.
+    auto finish_segment = [&]() {
+        const float L = xsum32(xsum16(l_lane));   // lane (j, n): total of head n
         if (mrow < G) {
-            const float inv = 1.f / (l_lane * kPScale);   // l >= 1: the tile that set the reference has weight 1
-            const float lse2 = m_lane + __builtin_amdgcn_logf(l_lane);
-            const int64_t sh = (int64_t)s * a.num_q_heads + h0 + mrow;
+            const float inv = 1.f / (L * kPScale);   // L >= 1: the tile that set the reference has weight 1
+            const float lse2 = m_lane + __builtin_amdgcn_logf(L);
+            const int64_t sh = (int64_t)seg_s * a.num_q_heads + seg_g * G + mrow;
             const int d0 = 4 * EPL * kq;           // acc[e][i] is value d0 + EPL i + e
-            if (direct) {
+            if (seg_direct) {
+                // Values d0 .. d0 + 4 EPL - 1 of the row, contiguous: acc[e][i] at EPL i + e.
+                const int64_t o = sh * D + d0;
+                if (a.out_dtype == kOutF32) {
+                    float* op = reinterpret_cast<float*>(a.out) + o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) store_out(a.out, sh * D + d0 + EPL * i + e, acc[e][i] * inv, a.out_dtype);
+                        for (int e = 0; e < EPL; e += 4)
+                            *reinterpret_cast<float4*>(op + EPL * i + e) =
+                                make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv);
+                } else {
+                    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + o;
+                    const bool bf = a.out_dtype == kOutBF16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < EPL; e += 2) {
+                            const float v0 = acc[e][i] * inv, v1 = acc[e + 1][i] * inv;
+                            const uint32_t w = bf ? (uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16)
+                                                  : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                                                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+                            *reinterpret_cast<uint32_t*>(op + EPL * i + e) = w;
+                        }
+                }
                 if (kq == 0 && a.lse) a.lse[sh] = lse2 * kLn2;
             } else {
-                float* o = a.ws_out + (sh * a.max_seg + slot) * D + d0;
+                float* o = a.ws_out + (sh * a.max_seg + seg_slot) * D + d0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int e = 0; e < EPL; e += 4)
                         *reinterpret_cast<float4*>(o + EPL * i + e) =
                             make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv);
-                if (kq == 0) a.ws_lse[sh * a.max_seg + slot] = lse2;
+                if (kq == 0) a.ws_lse[sh * a.max_seg + seg_slot] = lse2;
             }
         }
     };
 
-    // ---- this wave's chunks: w, w + NW, w + 2 NW, ... ----
+    // ---- the wave's chunks: w, w + NW, w + 2 NW, ... ----
+    // A chunk's positions [lo, hi) of the flattened list run through one
+    // pipeline, DEPTH tiles in flight, across the segments inside it: a
+    // segment boundary only finishes one (s, g) and starts the next, the loads
+    // keep going.  Position p's tile comes from per-lane windows of 128
+    // positions (lane i: p = c0 + i and c0 + 64 + i): its sequence (~s when p
+    // is not a tile to process: past the chunk, or padding of a fixed chunk),
+    // kv head, tile index and block id, and with 8-bit K/V the block's K and
+    // V scales.  A new window (every 128 positions of a chunk) waits for its
+    // block ids once.  A position that is not processed still loads the
+    // chunk's last real tile, just read, so the load is a cache hit.
+    struct Win { int sv, g, j, blk; float ks, vs; };
+    auto win_info = [&](int p, int hi) -> Win {
+        const int pc = min(p, hi - 1);
+        int sl = 0, sh = B;                        // invariant: pre[sl] <= pc < pre[sh]
+        while (sh - sl > 1) {
+            const int mid = (sl + sh) >> 1;
+            if (s_pre[mid] <= pc) sl = mid; else sh = mid;
+        }
+        const int nt = len_tiles(s_len[sl]);       // >= 1: sequence sl owns position pc
+        const int pt = padded_tiles(nt, a.fixed_chunk);
+        const int rel = pc - s_pre[sl];
+        Win w;
+        w.g = rel / pt;
+        const int j = rel - w.g * pt;
+        w.j = min(j, nt - 1);
+        w.sv = (p < hi && j < nt) ? sl : ~sl;
+        w.blk = a.block_tables[(int64_t)sl * a.table_stride + (w.j * kTile) / BS];
+        w.ks = 1.f;
+        w.vs = 1.f;
+        if constexpr (KV8) {
+            w.ks = a.k_scale[(int64_t)w.blk * Hkv + w.g];
+            w.vs = a.v_scale[(int64_t)w.blk * Hkv + w.g];
+        }
+        return w;
+    };
     const int w_global = lwg * kWaves + wave;
     for (int ch = w_global; ch < NC; ch += a.num_waves) {
         const int lo = ch * C, hi = min(lo + C, T);
-        // Largest s with pre[s] <= lo (empty sequences before it share its prefix).
-        int sl = 0, sh_ = B;                       // invariant: pre[sl] <= lo < pre[sh_]
-        while (sh_ - sl > 1) {
-            const int mid = (sl + sh_) >> 1;
-            if (s_pre[mid] <= lo) sl = mid; else sh_ = mid;
-        }
-        int s = sl;
-        int t = lo;
-        while (t < hi) {
-            while (s_pre[s + 1] <= t) ++s;         // skip sequences with no tiles
-            const int nt = seq_tiles(a, s);
-            const int pt = padded_tiles(nt, a.fixed_chunk);
-            const int rel = t - s_pre[s];
-            const int g = rel / pt;
-            const int j0 = rel % pt;
-            const int seg_hi = min(hi, s_pre[s] + (g + 1) * pt);
-            const int j1 = min(seg_hi - s_pre[s] - g * pt, nt);
-            if (j0 < j1) {
-                const int first = s_pre[s] + g * pt;
-                run_segment(s, g, j0, j1, ch - first / C, (first + nt - 1) / C == first / C);
+        int c0 = lo;
+        Win wlo = win_info(c0 + lane, hi);
+        Win whi = win_info(c0 + 64 + lane, hi);
+        auto pick = [&](int vlo, int vhi, int x) -> int {
+            const int i = x - c0;                  // in [0, 128)
+            return i < 64 ? __builtin_amdgcn_readlane(vlo, i) : __builtin_amdgcn_readlane(vhi, i - 64);
+        };
+        auto pickf = [&](float vlo, float vhi, int x) -> float {
+            return __builtin_bit_cast(float, pick(__builtin_bit_cast(int, vlo), __builtin_bit_cast(int, vhi), x));
+        };
+        // Per pipeline slot: the K, V and q operands of the position it holds,
+        // and that position's (~)s, kv head, tile index and scales.
+        uint4 kbuf[DEPTH][KL];
+        VLoad vbuf[DEPTH][NI];
+        MfmaIn qs[DEPTH][KS];
+        int ps[DEPTH], pg[DEPTH], pj[DEPTH], pblk[DEPTH];
+        float pks[DEPTH], pvs[DEPTH];
+        // Slot st takes position x: its K, and its q rows when the slot's
+        // previous position (x - DEPTH) was another segment or before lo.
+        auto issue_k = [&](int st, int x) {
+            ps[st] = pick(wlo.sv, whi.sv, x);
+            pg[st] = pick(wlo.g, whi.g, x);
+            pj[st] = pick(wlo.j, whi.j, x);
+            pblk[st] = pick(wlo.blk, whi.blk, x);
+            if constexpr (KV8) {
+                pks[st] = pickf(wlo.ks, whi.ks, x);
+                pvs[st] = pickf(wlo.vs, whi.vs, x);
+            } else {
+                pks[st] = pvs[st] = 1.f;
             }
-            t = seg_hi;
+            load_k(pj[st], pg[st], pblk[st], kbuf[st]);
+            if (ps[st] >= 0 && (x < lo + DEPTH || pj[st] < DEPTH)) load_q(ps[st], pg[st], qs[st]);
+        };
+        auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st]); };
+#pragma unroll
+        for (int st = 0; st < DEPTH; ++st) {
+            issue_k(st, lo + st);
+            issue_v(st);
+        }
+        for (int p = lo; p < hi; p += DEPTH) {
+            if (p + DEPTH - c0 == 128) {
+                // The loads below run into the next window: read its block ids
+                // (the positions in flight keep theirs in the slots).
+                c0 += 128;
+                wlo = win_info(c0 + lane, hi);
+                whi = win_info(c0 + 64 + lane, hi);
+            }
+#pragma unroll
+            for (int st = 0; st < DEPTH; ++st) {
+                const int x = p + st;
+                const int sv = ps[st], g = pg[st], j = pj[st];
+                const bool live = sv >= 0;
+                if (live && (x == lo || j == 0)) {
+                    // A segment starts: (sv, g) from tile j on.
+                    seg_s = sv;
+                    seg_g = g;
+                    seg_ctx = s_len[sv];
+                    seg_nt = len_tiles(seg_ctx);
+                    const int first = s_pre[sv] + g * padded_tiles(seg_nt, a.fixed_chunk);
+                    seg_slot = ch - first / C;
+                    seg_direct = (first + seg_nt - 1) / C == first / C;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    m_lane = mrow < G ? -INFINITY : 0.f;
+                    l_lane = 0.f;
+                }
+                uint2 phi = make_uint2(0u, 0u), plo = make_uint2(0u, 0u);
+                if (live) qk_softmax(j, kbuf[st], qs[st], pks[st], pvs[st], phi, plo);
+                issue_k(st, x + DEPTH);
+                if (live) pv(j, vbuf[st], phi, plo);
+                issue_v(st);
+                if (live && (x == hi - 1 || j == seg_nt - 1)) finish_segment();
+            }
         }
     }
 }
