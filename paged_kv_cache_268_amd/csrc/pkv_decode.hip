@@ -150,19 +150,29 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
     }
 }
 
+// K/V tile loads.  Every K/V byte is read once per launch, so the loads are
+// non-temporal: the lines are not kept in the caches for reuse, which on
+// this access pattern (random 2-4 KiB pieces of the pool) measured about 10 %
+// faster for the 16-bit kernel than plain loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
 // A lane's piece of one V row: NW 32-bit words.
 template <int NW> struct VPiece { uint32_t w[NW]; };
 template <int NW>
 __device__ __forceinline__ VPiece<NW> load_piece(const void* p) {
     VPiece<NW> v;
     if constexpr (NW == 4) {
-        const uint4 t = *reinterpret_cast<const uint4*>(p);
+        const uint4 t = load_once16(p);
         v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
     } else if constexpr (NW == 2) {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
-        v.w[0] = t.x; v.w[1] = t.y;
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        v.w[0] = t[0]; v.w[1] = t[1];
     } else {
-        v.w[0] = *reinterpret_cast<const uint32_t*>(p);
+        v.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     }
     return v;
 }
@@ -439,7 +449,7 @@ paged_decode_split_kernel(DecodeArgs a) {
         const int64_t base = tile_base(j, g, blk);
 #pragma unroll
         for (int u = 0; u < KL; ++u)
-            kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
+            kb[u] = load_once16(kc + base + k_off + u * (KV8 ? 64 : 32));
         __builtin_amdgcn_sched_barrier(0);
     };
     auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[NI]) {
