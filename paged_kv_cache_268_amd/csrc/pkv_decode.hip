@@ -162,17 +162,19 @@ __device__ __forceinline__ uint4 load_once16(const void* p) {
 }
 // A lane's piece of one V row: NW 32-bit words.
 template <int NW> struct VPiece { uint32_t w[NW]; };
-template <int NW>
+template <int NW, bool ONCE>
 __device__ __forceinline__ VPiece<NW> load_piece(const void* p) {
     VPiece<NW> v;
     if constexpr (NW == 4) {
-        const uint4 t = load_once16(p);
+        const uint4 t = ONCE ? load_once16(p) : *reinterpret_cast<const uint4*>(p);
         v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
     } else if constexpr (NW == 2) {
-        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        const u32x2 t = ONCE ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                             : *reinterpret_cast<const u32x2*>(p);
         v.w[0] = t[0]; v.w[1] = t[1];
     } else {
-        v.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        v.w[0] = ONCE ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p))
+                      : *reinterpret_cast<const uint32_t*>(p);
     }
     return v;
 }
@@ -449,17 +451,27 @@ paged_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], plo, acc[e]);
     };
-    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[KL]) {
+    // keep: plain loads (the lines stay cached) instead of non-temporal ones.
+    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[KL], bool keep) {
         const int64_t base = tile_base(j, g, blk);
+        if (keep) {
 #pragma unroll
-        for (int u = 0; u < KL; ++u)
-            kb[u] = load_once16(kc + base + k_off + u * (KV8 ? 64 : 32));
+            for (int u = 0; u < KL; ++u) kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
+        } else {
+#pragma unroll
+            for (int u = 0; u < KL; ++u) kb[u] = load_once16(kc + base + k_off + u * (KV8 ? 64 : 32));
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[NI]) {
+    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[NI], bool keep) {
         const int64_t base = tile_base(j, g, blk);
+        if (keep) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW>(vc + base + v_off + i * 4 * D);
+            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW, false>(vc + base + v_off + i * 4 * D);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW, true>(vc + base + v_off + i * 4 * D);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     // The q rows of kv group g of sequence s, as the QK B operand.
@@ -533,7 +545,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     // kv head, tile index and block id, and with 8-bit K/V the block's K and
     // V scales.  A new window (every 128 positions of a chunk) waits for its
     // block ids once.  A position that is not processed still loads the
-    // chunk's last real tile, just read, so the load is a cache hit.
+    // chunk's last real tile (see issue_k: a cache hit).
     struct Win { int sv, g, j, blk; float ks, vs; };
     auto win_info = [&](int p, int hi) -> Win {
         const int pc = min(p, hi - 1);
@@ -578,6 +590,7 @@ paged_decode_split_kernel(DecodeArgs a) {
         VLoad vbuf[DEPTH][NI];
         MfmaIn qs[DEPTH][KS];
         int ps[DEPTH], pg[DEPTH], pj[DEPTH], pblk[DEPTH];
+        bool pkeep[DEPTH];
         float pks[DEPTH], pvs[DEPTH];
         // Slot st takes position x: its K, and its q rows when the slot's
         // previous position (x - DEPTH) was another segment or before lo.
@@ -592,10 +605,14 @@ paged_decode_split_kernel(DecodeArgs a) {
             } else {
                 pks[st] = pvs[st] = 1.f;
             }
-            load_k(pj[st], pg[st], pblk[st], kbuf[st]);
+            // The chunk's last real tile, and the positions past it that
+            // re-read it, use plain loads: that tile stays in the cache and
+            // the re-reads hit.
+            pkeep[st] = ps[st] < 0 || x == hi - 1;
+            load_k(pj[st], pg[st], pblk[st], kbuf[st], pkeep[st]);
             if (ps[st] >= 0 && (x < lo + DEPTH || pj[st] < DEPTH)) load_q(ps[st], pg[st], qs[st]);
         };
-        auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st]); };
+        auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st], pkeep[st]); };
 #pragma unroll
         for (int st = 0; st < DEPTH; ++st) {
             issue_k(st, lo + st);
