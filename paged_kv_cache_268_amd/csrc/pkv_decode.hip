@@ -656,72 +656,100 @@ paged_decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// Merge kernel: one 256-thread workgroup per (sequence, q head) whose (s, g)
-// spans more than one chunk.  With M = max_k lse_k and w_k = 2^(lse_k - M):
+// Merge kernel: one wave per (sequence, q head) whose (s, g) spans more than
+// one chunk, four per workgroup.  With M = max_k lse_k and w_k = 2^(lse_k - M):
 // out = sum_k w_k o_k / sum_k w_k and lse = M + log2(sum_k w_k) -- the
-// online-softmax identity applied to the segments.  Threads own 4
-// consecutive d values of one segment slot; the slots stride over the
-// segments and meet in LDS.
+// online-softmax identity applied to the segments.  Lane l owns D/64
+// consecutive d values of the output; lane k of a 64-segment batch computes
+// w_k, which the wave reads back lane by lane, so there is no LDS and no
+// barrier.  The kernel is a chain of dependent loads (length, header, lse,
+// rows), so the lse values and the first UNROLL segment rows are loaded
+// together with the length and header: every pair owns max_seg slots, so these
+// reads stay inside its own workspace rows whatever its segment count, and
+// rows past the count are never used.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_merge_kernel(MergeArgs a) {
-    constexpr int TPP = D / 4;                 // threads per segment row
-    constexpr int SLOTS = kThreads / TPP;      // segments handled at once
-    const int64_t sh = blockIdx.x;
+    constexpr int VPL = D / 64;                // output values per lane
+    constexpr int UNROLL = 4;                  // segment rows in flight per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t sh = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (sh >= (int64_t)a.num_seqs * a.num_q_heads) return;
     const int s = (int)(sh / a.num_q_heads);
     const int hq = (int)(sh % a.num_q_heads);
     const int G = a.num_q_heads / a.num_kv_heads;
     const int g = hq / G;
-    const int n = min(max(a.context_lens[s], 0), a.max_context_len);
+    const float* lse_p = a.ws_lse + sh * a.max_seg;
+    const float* out_p = a.ws_out + sh * a.max_seg * D + lane * VPL;
+
+    const int len = a.context_lens[s];
+    const int C = a.ws_hdr[1];
+    const int pre = a.ws_hdr[2 + s];
+    const float lse_first = lane < a.max_seg ? lse_p[lane] : -INFINITY;
+    float v0[UNROLL][VPL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) v0[u][e] = u < a.max_seg ? out_p[(int64_t)u * D + e] : 0.f;
+
+    const int n = min(max(len, 0), a.max_context_len);
     const int nt = (n + kTile - 1) / kTile;
     if (nt == 0) return;                       // written by the split kernel
-    const int C = a.ws_hdr[1];
     const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
-    const int first = a.ws_hdr[2 + s] + g * pt;
+    const int first = pre + g * pt;
     const int nseg = (first + nt - 1) / C - first / C + 1;
     if (nseg <= 1) return;                     // written directly
 
-    const float* lse_p = a.ws_lse + sh * a.max_seg;
-    const float* out_p = a.ws_out + sh * a.max_seg * D;
-    __shared__ float s_red[kThreads / 64];
-    __shared__ float s_acc[SLOTS][D];
-    __shared__ float s_w[SLOTS];
+    float M = lane < nseg ? lse_first : -INFINITY;
+    for (int k = lane + 64; k < nseg; k += 64) M = fmaxf(M, lse_p[k]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-    float mx = -INFINITY;
-    for (int k = threadIdx.x; k < nseg; k += kThreads) mx = fmaxf(mx, lse_p[k]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    float M = s_red[0];
+    float acc[VPL];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-
-    const int slot = threadIdx.x / TPP;
-    const int d4 = (threadIdx.x % TPP) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float wsum = 0.f;
-    for (int k = slot; k < nseg; k += SLOTS) {
-        const float w = __builtin_amdgcn_exp2f(lse_p[k] - M);
-        const float4 o = *reinterpret_cast<const float4*>(out_p + (int64_t)k * D + d4);
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
-        wsum += w;
-    }
-    s_acc[slot][d4 + 0] = acc.x;
-    s_acc[slot][d4 + 1] = acc.y;
-    s_acc[slot][d4 + 2] = acc.z;
-    s_acc[slot][d4 + 3] = acc.w;
-    if (threadIdx.x % TPP == 0) s_w[slot] = wsum;
-    __syncthreads();
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-        float o = 0.f, W = 0.f;
+    for (int e = 0; e < VPL; ++e) acc[e] = 0.f;
+    float W = 0.f;
+    for (int kb = 0; kb < nseg; kb += 64) {
+        const int cnt = min(64, nseg - kb);
+        const float lk = kb == 0 ? lse_first : (lane < cnt ? lse_p[kb + lane] : 0.f);
+        const float w = lane < cnt ? __builtin_amdgcn_exp2f(lk - M) : 0.f;
+        W += w;
+        const int wbits = __float_as_int(w);
+        const float* o = out_p + (int64_t)kb * D;
+        int j = 0;
+        if (kb == 0) {
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) { o += s_acc[k][d]; W += s_w[k]; }
-        store_out(a.out, sh * D + d, o / W, a.out_dtype);
-        if (a.lse && d == 0) a.lse[sh] = (M + __builtin_amdgcn_logf(W)) * kLn2;
+            for (int u = 0; u < UNROLL; ++u) {
+                if (u < cnt) {
+                    const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, u));
+#pragma unroll
+                    for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, v0[u][e], acc[e]);
+                }
+            }
+            j = min(UNROLL, cnt);
+        }
+        for (; j + UNROLL <= cnt; j += UNROLL) {
+            float v[UNROLL][VPL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int e = 0; e < VPL; ++e) v[u][e] = o[(int64_t)(j + u) * D + e];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, j + u));
+#pragma unroll
+                for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, v[u][e], acc[e]);
+            }
+        }
+        for (; j < cnt; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, j));
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, o[(int64_t)j * D + e], acc[e]);
+        }
     }
+    for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) store_out(a.out, sh * D + lane * VPL + e, acc[e] / W, a.out_dtype);
+    if (a.lse && lane == 0) a.lse[sh] = (M + __builtin_amdgcn_logf(W)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -788,8 +816,9 @@ hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int g
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
-    const unsigned n = (unsigned)((int64_t)a.num_seqs * a.num_q_heads);
-    if (n == 0) return hipSuccess;
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
+    if (pairs == 0) return hipSuccess;
+    const unsigned n = (unsigned)((pairs + kWaves - 1) / kWaves);
     if (head_dim == 128)
         hipLaunchKernelGGL(paged_decode_merge_kernel<128>, dim3(n), dim3(kThreads), 0, stream, a);
     else if (head_dim == 64)
