@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="decode configuration 1..5")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per split-K partition (0 = balanced split); default: the workload's own")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,6 +62,27 @@ def parse():
                     help="also run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) three times, "
                          "the known-size reference for HBM byte counters")
     return ap.parse_args()
+
+
+def unique_kv_bytes(tables, lens, bs, tok_bytes):
+    """K/V bytes of the distinct blocks the tables reach, each block counted by the
+    largest number of its slots any sequence uses."""
+    blk, used = [], []
+    for s in range(len(lens)):
+        n = int(lens[s])
+        nb = -(-n // bs)
+        if nb == 0:
+            continue
+        u = np.full(nb, bs, dtype=np.int64)
+        u[-1] = n - (nb - 1) * bs
+        blk.append(tables[s, :nb].astype(np.int64))
+        used.append(u)
+    if not blk:
+        return 0
+    blk, used = np.concatenate(blk), np.concatenate(used)
+    most = np.zeros(int(blk.max()) + 1, dtype=np.int64)
+    np.maximum.at(most, blk, used)
+    return int(most.sum()) * tok_bytes
 
 
 def kernel_sources_sha256():
@@ -323,7 +345,7 @@ def main():
     total_steps = K + Wu + N_BREAKDOWN
     grow_blocks = total_steps // 16 + 2
     wl = W.config(args.config, seed=args.seed, extra_table_entries=grow_blocks)
-    P = args.partition_size or wl.partition_size
+    P = wl.partition_size if args.partition_size is None else args.partition_size
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
     log(f"[bench] config {args.config} {wl.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} {wl.dtype} "
         f"sum(ctx)={int(wl.context_lens.sum())} max={wl.max_context_len} blocks={wl.num_blocks} "
@@ -385,6 +407,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log(f"[bench] timed {K} steps")
+    tables_end, lens_end = tables.cpu().numpy(), lens.cpu().numpy()
     for i in range(N_BREAKDOWN):
         step(e4=ev4[i])
     torch.cuda.synchronize()
@@ -393,11 +416,20 @@ def main():
     # K/V bytes each timed step's attention reads: context after that step's append.
     step_bytes = [int((ctx0 + Wu + i + 1).sum()) * Hkv * D * 2 * 2 for i in range(K)]
     kv_bytes = float(np.mean(step_bytes))
+    # Unique bytes: distinct (block, kv head) chunks the step reads, a block counted
+    # by the most tokens any sequence uses in it.  Equal to kv_bytes unless tables
+    # share blocks (shared prefixes).  Timed step i reads the state after its own
+    # append; appends go to private blocks, so unique bytes fall by one token per
+    # sequence for each step before the last timed one.
+    tok_bytes = Hkv * D * 2 * 2
+    uniq_end = unique_kv_bytes(tables_end, lens_end, bs, tok_bytes)
+    uniq_bytes = uniq_end - (K - 1) / 2 * B * tok_bytes
     t_part = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     t_app = [e[0].elapsed_time(e[1]) for e in ev4]
     t_merge = [e[2].elapsed_time(e[3]) for e in ev4]
     part_ms = float(np.mean(t_part))
-    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
+    achieved = uniq_bytes / (part_ms * 1e-3) / 1e9
+    achieved_logical = kv_bytes / (part_ms * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
 
     # Parity spot check of the last step's output against the oracle on two sequences.
@@ -425,6 +457,7 @@ def main():
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": int(kv_bytes),
+        "unique_kv_bytes_per_step": int(uniq_bytes),
         "kernel_ms": {
             "partition": round(part_ms, 4),
             "kv_append_event_pass": round(float(np.mean(t_app)), 4),
@@ -440,7 +473,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.config, K, Wu),
             "traffic_unit": "bytes per launch",
-            "algorithmic_bytes_per_launch": int(kv_bytes),
+            "algorithmic_bytes_per_launch": int(uniq_bytes),
+            "achieved_logical_bytes": round(achieved_logical, 2),
         },
         "cpu_baseline": None,
     }

@@ -63,6 +63,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr int kMinChunk = 8;           // balanced split: at least 8 tiles (128 tokens) per chunk
+constexpr int kMergeWidePairs = 1024;  // merge: a workgroup per pair up to this many pairs...
+constexpr int kMergeWideSegments = 32; // ...or for fixed partitions with more slots than this
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -656,99 +658,133 @@ paged_decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// Merge kernel: one wave per (sequence, q head) whose (s, g) spans more than
-// one chunk, four per workgroup.  With M = max_k lse_k and w_k = 2^(lse_k - M):
-// out = sum_k w_k o_k / sum_k w_k and lse = M + log2(sum_k w_k) -- the
-// online-softmax identity applied to the segments.  Lane l owns D/64
-// consecutive d values of the output; lane k of a 64-segment batch computes
-// w_k, which the wave reads back lane by lane, so there is no LDS and no
-// barrier.  The kernel is a chain of dependent loads (length, header, lse,
-// rows), so the lse values and the first UNROLL segment rows are loaded
-// together with the length and header: every pair owns max_seg slots, so these
-// reads stay inside its own workspace rows whatever its segment count, and
-// rows past the count are never used.
-template <int D>
+// Merge kernel: WPP waves per (sequence, q head) whose (s, g) spans more than
+// one chunk -- one wave (four pairs per workgroup) or a whole workgroup.  With
+// M = max_k lse_k and w_k = 2^(lse_k - M): out = sum_k w_k o_k / sum_k w_k and
+// lse = M + log2(sum_k w_k) -- the online-softmax identity applied to the
+// segments.  A wave load covers RPL segment rows (lane l reads 4 consecutive d
+// values of row l / (D/4)); the pair's waves take rows in turn and each lane
+// keeps UNROLL rows in flight, so a pair's first WPP RPL UNROLL rows arrive in
+// one round trip.  Every wave computes M itself from the lse values; rows with
+// the same d slice are summed by lane swaps, waves by LDS.  The kernel is a
+// chain of dependent loads (length, header, lse, rows), so each lane's first
+// UNROLL rows and lse values are loaded together with the length and header:
+// every pair owns max_seg slots, so these reads stay inside its own workspace
+// rows whatever its segment count, and rows past the count are never used.
+template <int D, int WPP>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_merge_kernel(MergeArgs a) {
-    constexpr int VPL = D / 64;                // output values per lane
-    constexpr int UNROLL = 4;                  // segment rows in flight per lane
+    constexpr int LPR = D / 4;                 // lanes per segment row (4 floats each)
+    constexpr int RPL = 64 / LPR;              // rows per wave load
+    constexpr int STEP = RPL * WPP;            // rows per load across the pair's waves
+    constexpr int UNROLL = 4;
+    constexpr int PAIRS = kWaves / WPP;        // pairs per workgroup
     const int lane = threadIdx.x & 63;
-    const int64_t sh = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (sh >= (int64_t)a.num_seqs * a.num_q_heads) return;
+    const int wave = threadIdx.x >> 6;
+    const int wp = wave % WPP;                 // this wave's index within its pair
+    const int64_t sh = (int64_t)blockIdx.x * PAIRS + wave / WPP;
+    if (sh >= (int64_t)a.num_seqs * a.num_q_heads) return;   // uniform over a pair's waves
     const int s = (int)(sh / a.num_q_heads);
     const int hq = (int)(sh % a.num_q_heads);
     const int G = a.num_q_heads / a.num_kv_heads;
     const int g = hq / G;
     const float* lse_p = a.ws_lse + sh * a.max_seg;
-    const float* out_p = a.ws_out + sh * a.max_seg * D + lane * VPL;
+    const int d4 = (lane % LPR) * 4;
+    const int r0 = wp * RPL + lane / LPR;      // this lane's first row
+    const float* out_p = a.ws_out + sh * a.max_seg * D + d4;
 
     const int len = a.context_lens[s];
     const int C = a.ws_hdr[1];
     const int pre = a.ws_hdr[2 + s];
-    const float lse_first = lane < a.max_seg ? lse_p[lane] : -INFINITY;
-    float v0[UNROLL][VPL];
+    const float lse_lane = lane < a.max_seg ? lse_p[lane] : -INFINITY;
+    float4 v0[UNROLL];
+    float l0[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) v0[u][e] = u < a.max_seg ? out_p[(int64_t)u * D + e] : 0.f;
+    for (int u = 0; u < UNROLL; ++u) {
+        const int k = r0 + u * STEP;
+        v0[u] = k < a.max_seg ? *reinterpret_cast<const float4*>(out_p + (int64_t)k * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        l0[u] = k < a.max_seg ? lse_p[k] : -INFINITY;
+    }
 
     const int n = min(max(len, 0), a.max_context_len);
     const int nt = (n + kTile - 1) / kTile;
-    if (nt == 0) return;                       // written by the split kernel
     const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
     const int first = pre + g * pt;
-    const int nseg = (first + nt - 1) / C - first / C + 1;
-    if (nseg <= 1) return;                     // written directly
+    // Empty pairs are written by the split kernel, one-segment pairs directly.
+    const int nseg = nt == 0 ? 0 : (first + nt - 1) / C - first / C + 1;
+    if (nseg <= 1) return;                     // uniform over a pair's waves
 
-    float M = lane < nseg ? lse_first : -INFINITY;
+    float M = lane < nseg ? lse_lane : -INFINITY;
     for (int k = lane + 64; k < nseg; k += 64) M = fmaxf(M, lse_p[k]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-    float acc[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) acc[e] = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float W = 0.f;
-    for (int kb = 0; kb < nseg; kb += 64) {
-        const int cnt = min(64, nseg - kb);
-        const float lk = kb == 0 ? lse_first : (lane < cnt ? lse_p[kb + lane] : 0.f);
-        const float w = lane < cnt ? __builtin_amdgcn_exp2f(lk - M) : 0.f;
-        W += w;
-        const int wbits = __float_as_int(w);
-        const float* o = out_p + (int64_t)kb * D;
-        int j = 0;
-        if (kb == 0) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (u < cnt) {
-                    const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, u));
-#pragma unroll
-                    for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, v0[u][e], acc[e]);
-                }
-            }
-            j = min(UNROLL, cnt);
-        }
-        for (; j + UNROLL <= cnt; j += UNROLL) {
-            float v[UNROLL][VPL];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) v[u][e] = o[(int64_t)(j + u) * D + e];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, j + u));
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, v[u][e], acc[e]);
-            }
-        }
-        for (; j < cnt; ++j) {
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(wbits, j));
-#pragma unroll
-            for (int e = 0; e < VPL; ++e) acc[e] = fmaf(wj, o[(int64_t)j * D + e], acc[e]);
+    for (int u = 0; u < UNROLL; ++u) {
+        if (r0 + u * STEP < nseg) {
+            const float w = __builtin_amdgcn_exp2f(l0[u] - M);
+            acc.x = fmaf(w, v0[u].x, acc.x);
+            acc.y = fmaf(w, v0[u].y, acc.y);
+            acc.z = fmaf(w, v0[u].z, acc.z);
+            acc.w = fmaf(w, v0[u].w, acc.w);
+            W += w;
         }
     }
-    for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off);
+    for (int kb = r0 + UNROLL * STEP; kb < nseg; kb += UNROLL * STEP) {
+        float4 v[UNROLL];
+        float l[UNROLL];
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) store_out(a.out, sh * D + lane * VPL + e, acc[e] / W, a.out_dtype);
+        for (int u = 0; u < UNROLL; ++u) {
+            const int k = kb + u * STEP;
+            v[u] = k < nseg ? *reinterpret_cast<const float4*>(out_p + (int64_t)k * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+            l[u] = k < nseg ? lse_p[k] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (kb + u * STEP < nseg) {
+                const float w = __builtin_amdgcn_exp2f(l[u] - M);
+                acc.x = fmaf(w, v[u].x, acc.x);
+                acc.y = fmaf(w, v[u].y, acc.y);
+                acc.z = fmaf(w, v[u].z, acc.z);
+                acc.w = fmaf(w, v[u].w, acc.w);
+                W += w;
+            }
+        }
+    }
+    // Rows of one wave load that share a d slice: lanes LPR apart.
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
+        W += __shfl_xor(W, off);
+    }
+    if constexpr (WPP > 1) {
+        // PAIRS == 1 here: every wave of the workgroup reaches this barrier.
+        __shared__ float4 s_acc[kWaves][LPR];
+        __shared__ float s_w[kWaves];
+        if (lane < LPR) s_acc[wave][lane] = acc;
+        if (lane == 0) s_w[wave] = W;
+        __syncthreads();
+        if (wave != 0) return;
+        if (lane < LPR) {
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) {
+                const float4 o = s_acc[w2][lane];
+                acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+            }
+        }
+#pragma unroll
+        for (int w2 = 1; w2 < kWaves; ++w2) W += s_w[w2];
+    }
+    if (lane >= LPR) return;
+    const int64_t o = sh * D + d4;
+    store_out(a.out, o + 0, acc.x / W, a.out_dtype);
+    store_out(a.out, o + 1, acc.y / W, a.out_dtype);
+    store_out(a.out, o + 2, acc.z / W, a.out_dtype);
+    store_out(a.out, o + 3, acc.w / W, a.out_dtype);
     if (a.lse && lane == 0) a.lse[sh] = (M + __builtin_amdgcn_logf(W)) * kLn2;
 }
 
@@ -818,13 +854,23 @@ hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int g
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
     if (pairs == 0) return hipSuccess;
-    const unsigned n = (unsigned)((pairs + kWaves - 1) / kWaves);
-    if (head_dim == 128)
-        hipLaunchKernelGGL(paged_decode_merge_kernel<128>, dim3(n), dim3(kThreads), 0, stream, a);
-    else if (head_dim == 64)
-        hipLaunchKernelGGL(paged_decode_merge_kernel<64>, dim3(n), dim3(kThreads), 0, stream, a);
-    else
+    // A workgroup per pair where segment lists may be long: the fixed split
+    // of a long context, or few pairs (where one long context among short ones
+    // spans many of the balanced split's chunks and the grid is small anyway).
+    // Otherwise one wave per pair: many pairs of a few segments each, for which
+    // a workgroup each would only add dispatch work.
+    const bool wide = pairs <= kMergeWidePairs || (a.fixed_chunk > 0 && a.max_seg > kMergeWideSegments);
+    const int per_block = wide ? 1 : kWaves;
+    const unsigned n = (unsigned)((pairs + per_block - 1) / per_block);
+    if (head_dim == 128) {
+        if (wide) hipLaunchKernelGGL((paged_decode_merge_kernel<128, kWaves>), dim3(n), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((paged_decode_merge_kernel<128, 1>), dim3(n), dim3(kThreads), 0, stream, a);
+    } else if (head_dim == 64) {
+        if (wide) hipLaunchKernelGGL((paged_decode_merge_kernel<64, kWaves>), dim3(n), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((paged_decode_merge_kernel<64, 1>), dim3(n), dim3(kThreads), 0, stream, a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

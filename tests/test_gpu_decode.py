@@ -226,6 +226,39 @@ def test_split_sizes_match_oracle(P, nw):
     compare(out, lse, ref_out, ref_lse, what=f"P={P} nw={nw}")
 
 
+@pytest.mark.parametrize("D,dtype,P", [(64, "f16", 16), (128, "bf16", 16), (64, "bf16", 48), (128, "f16", 32)])
+def test_long_segment_lists_merge(D, dtype, P):
+    """Fixed partitions of long contexts: up to 188 segments per (sequence, q head),
+    more than the merge kernel's first round of loads covers; lengths leave a
+    ragged last partition, a pair of a single segment and an empty one."""
+    wl = small(B=6, Hq=12, Hkv=3, D=D, dtype=dtype, ctx=(0, 5, 700, 1601, 2999, 3000), seed=11)
+    note(f"long segment lists D={D} {dtype} P={P}")
+    q, k, v = W.make_values(wl, DEV, poison=True)
+    tab, ctx = to_dev(wl)
+    ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
+    out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
+    compare(out, lse, ref_out, ref_lse, what=f"D={D} P={P}")
+    # The 16-bit output of the merge is the fp32 result rounded to nearest even.
+    code = pkv.PKV_BF16 if dtype == "bf16" else pkv.PKV_F16
+    out16, _ = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P, out_dtype=code, with_lse=False)
+    assert torch.equal(out16, out.to(q.dtype))
+
+
+def test_many_pairs_long_segment_lists_merge():
+    """More than 1024 (sequence, q head) pairs with up to 32 fixed partitions each:
+    the merge kernel's one-wave-per-pair form past its first round of loads."""
+    rng = np.random.default_rng(12)
+    ctx = rng.integers(1, 2049, 40)
+    ctx[:4] = (2048, 2047, 65, 64)
+    wl = W.make_workload(40, 32, 8, 128, 16, "bf16", ctx, 12, partition_size=64)
+    note("many pairs, P=64, up to 32 segments")
+    q, k, v = W.make_values(wl, DEV, poison=True)
+    tab, dctx = to_dev(wl)
+    out, lse = gpu_decode(wl, q, k, v, tab, dctx)
+    ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
+    compare(out, lse, ref_out, ref_lse, what="many pairs P=64")
+
+
 @pytest.mark.parametrize("P,nw", [(256, 0), (0, 8), (0, 16), (512, 4)])
 def test_segments_are_the_plan(P, nw):
     """Each segment's output in the workspace equals the oracle on its token range."""
