@@ -12,7 +12,7 @@
 // of a chunk, q head); wave w owns 16 queries.  The workgroup walks 32-key
 // tiles from position 0 to its last query's position.  Each K/V tile is read
 // once per workgroup (16-byte loads through the block table) into LDS, double
-// buffered: the next tile's loads are in flight while this one is consumed.
+// buffered, with the loads issued two tiles ahead (two register stages).
 // K sits row-major (rows padded by 16 bytes), V transposed ([d][key], rows
 // padded to 72 bytes).  Waves 2-3 load K (four 16-byte pieces per thread);
 // waves 0-1 load V as units of 4 consecutive keys x 8 d values and store, for
@@ -94,9 +94,9 @@ __device__ __forceinline__ int prefill_xcd_remap(int i, int n) {
 }  // namespace
 
 template <int D, int BS, bool BF16>
-// Four waves per SIMD (at most 128 VGPRs; 119 used at D = 128, no spills):
-// with the 35.8 KB of LDS per workgroup that is 4 workgroups per CU, and it
-// measured 13 % faster than the 3 workgroups the unconstrained 156 VGPRs allow.
+// Four waves per SIMD (at most 128 VGPRs; 128 used at D = 128, no spills):
+// with the 35.8 KB of LDS per workgroup that is 4 workgroups per CU, each with
+// two tiles' loads in flight.
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 paged_prefill_kernel(PrefillArgs a) {
     using V8 = typename PType<BF16>::v8;
@@ -182,6 +182,12 @@ paged_prefill_kernel(PrefillArgs a) {
     const bool qvalid = qi < m && q0 + qi < a.total_q;
     const int qpos = base_pos + qi;
     const float sl2 = a.scale * kPLog2e;
+    // Tiles [0, nomask_tiles) need no causal mask for this wave: all 16 of its
+    // queries are real and the tile's last key precedes its first query.
+    const int wq0 = qa + wave * 16;
+    const bool wave_full = wq0 + 16 <= m && q0 + wq0 + 16 <= a.total_q;
+    const int wave_pos0 = base_pos + wq0;
+    const int nomask_tiles = (wave_full && wave_pos0 >= 0) ? (wave_pos0 + 1) / kPKeys : 0;
 
     V8 qb[KS];
 #pragma unroll
@@ -197,43 +203,60 @@ paged_prefill_kernel(PrefillArgs a) {
     const uint4* kg = reinterpret_cast<const uint4*>(a.k_cache);
     const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache);
 
-    // 16-byte piece of token t (d chunk cd), or zeros past the context end.
     // Block ids of a tile (a 32-key tile spans one block of 32 or two of 16):
     // lane l loads entry (first + (l & 1)) as a vector load one iteration
     // before the tile's K/V loads need it, so the table read is off the
-    // critical path; read back with v_readlane.
+    // critical path; read back with v_readlane, so the two block bases are
+    // wave-uniform (scalar registers) and a lane's offset inside a block is
+    // the same for every tile (computed once below).  Keys at or past the
+    // context end are zeros, never loaded; only the last tile checks.
     const int last_blk = (n + BS - 1) / BS - 1;
     auto load_ids = [&](int kt) {
         return table[min((kt * kPKeys) / BS + (lane & 1), last_blk)];
     };
-    auto fetch = [&](const uint4* base, int t, int cd, int32_t b0, int32_t b1) {
-        uint4 z = make_uint4(0, 0, 0, 0);
-        if (t < n) {
-            const int32_t blk = (BS == kPKeys || (t % kPKeys) < BS) ? b0 : b1;
-            z = base[(((int64_t)blk * Hkv + g) * BS + t % BS) * CPR + cd];
-        }
-        return z;
-    };
     const bool k_half = wave >= 2;                 // uniform per wave
     const int ht = tid & (HT - 1);
-    // K half: piece ht + HT c is key (ht + HT c) / CPR, chunk (ht + HT c) % CPR.
+    // K half: piece ht + HT c is key (ht + HT c) / CPR, chunk (ht + HT c) % CPR;
+    // the keys of one c lie in one block (KEYS_PER_C divides the block size).
     // V half: unit ht + HT c is keys 4 ((ht + HT c) % 8) .. +3, chunk (ht + HT c) / 8.
+    constexpr int KEYS_PER_C = HT / CPR;
+    static_assert(HT % CPR == 0 && BS % KEYS_PER_C == 0, "a K piece group stays inside one block");
+    int koff[KPT], vkey[VPT], voff[VPT];           // offsets in 16-byte units inside a block
+#pragma unroll
+    for (int c = 0; c < KPT; ++c) {
+        const int piece = ht + HT * c;
+        koff[c] = ((piece / CPR) % BS) * CPR + piece % CPR;
+    }
+#pragma unroll
+    for (int c = 0; c < VPT; ++c) {
+        const int u = ht + HT * c;
+        vkey[c] = 4 * (u % 8);
+        voff[c] = (vkey[c] % BS) * CPR + u / 8;
+    }
+    const int64_t blk_stride = (int64_t)Hkv * BS * CPR, head_off = (int64_t)g * BS * CPR;
     auto gload = [&](int kt, int32_t ids, uint4 (&r)[SR]) {
         const int32_t b0 = __builtin_amdgcn_readlane(ids, 0), b1 = __builtin_amdgcn_readlane(ids, 1);
+        const int t0 = kt * kPKeys;
+        const bool full = t0 + kPKeys <= n;        // uniform: every key of the tile is cached
         if (k_half) {
+            const uint4* p0 = kg + b0 * blk_stride + head_off;
+            const uint4* p1 = kg + b1 * blk_stride + head_off;
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
-                const int piece = ht + HT * c;
-                r[c] = fetch(kg, kt * kPKeys + piece / CPR, piece % CPR, b0, b1);
+                const uint4* p = (BS == kPKeys || (c + 1) * KEYS_PER_C <= BS) ? p0 : p1;
+                const int key = (ht + HT * c) / CPR;
+                r[c] = (full || t0 + key < n) ? p[koff[c]] : make_uint4(0, 0, 0, 0);
             }
         } else {
+            const uint4* p0 = vg + b0 * blk_stride + head_off;
+            const uint4* p1 = vg + b1 * blk_stride + head_off;
 #pragma unroll
             for (int c = 0; c < VPT; ++c) {
                 const int u = ht + HT * c;
+                const uint4* p = ((BS == kPKeys || vkey[c] < BS) ? p0 : p1) + voff[c];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    r[4 * c + kk] = u < VU ? fetch(vg, kt * kPKeys + 4 * (u % 8) + kk, u / 8, b0, b1)
-                                           : make_uint4(0, 0, 0, 0);
+                    r[4 * c + kk] = (u < VU && (full || t0 + vkey[c] + kk < n)) ? p[kk * CPR] : make_uint4(0, 0, 0, 0);
             }
         }
     };
@@ -289,11 +312,21 @@ paged_prefill_kernel(PrefillArgs a) {
         const int t0 = kt * kPKeys + 4 * quad;
         float x[8];
         float mx = -INFINITY;
+        if (kt < nomask_tiles) {
+            // Every key of the tile is at or before every query of the wave.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x[r] = (qvalid && t0 + r <= qpos) ? c0[r] * sl2 : -INFINITY;
-            x[4 + r] = (qvalid && t0 + 16 + r <= qpos) ? c1[r] * sl2 : -INFINITY;
-            mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
+            for (int r = 0; r < 4; ++r) {
+                x[r] = c0[r] * sl2;
+                x[4 + r] = c1[r] * sl2;
+                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[r] = (qvalid && t0 + r <= qpos) ? c0[r] * sl2 : -INFINITY;
+                x[4 + r] = (qvalid && t0 + 16 + r <= qpos) ? c1[r] * sl2 : -INFINITY;
+                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
+            }
         }
         mx = pmax32(pmax16(mx));                       // column max of this tile
         const bool need = mx > m_l + kPTau;            // uniform over the column's 4 lanes
@@ -327,23 +360,33 @@ paged_prefill_kernel(PrefillArgs a) {
         }
     };
 
-    uint4 stage[SR];
-    int32_t ids_next = 0;                          // block ids of the tile after the one in flight
+    // Two register stages: the global loads of tile kt + 2 are issued while
+    // tile kt is consumed, and stored to LDS one iteration later, so each
+    // tile's loads have a whole iteration to arrive.  LDS stays double
+    // buffered: the barrier that ends an iteration separates the reads of one
+    // buffer from the next store into it.
+    uint4 st_a[SR], st_b[SR];
+    int32_t ids_next = 0;                          // block ids of the next tile to load
     if (NT > 0) {
-        gload(0, load_ids(0), stage);
-        lstore(0, stage);
+        gload(0, load_ids(0), st_a);
+        lstore(0, st_a);
     }
-    if (NT > 1) ids_next = load_ids(1);
+    if (NT > 1) gload(1, load_ids(1), st_a);       // tile 1 in flight in st_a
+    if (NT > 2) ids_next = load_ids(2);
     __syncthreads();
-    for (int kt = 0; kt < NT; ++kt) {
-        const int b = kt & 1;
-        if (kt + 1 < NT) {
-            gload(kt + 1, ids_next, stage);
-            if (kt + 2 < NT) ids_next = load_ids(kt + 2);
+    // cur holds tile kt + 1's loads in flight; nxt is free.
+    auto step = [&](int kt, uint4 (&cur)[SR], uint4 (&nxt)[SR]) {
+        if (kt + 2 < NT) {
+            gload(kt + 2, ids_next, nxt);
+            if (kt + 3 < NT) ids_next = load_ids(kt + 3);
         }
-        compute(b, kt);
-        if (kt + 1 < NT) lstore(b ^ 1, stage);
+        compute(kt & 1, kt);
+        if (kt + 1 < NT) lstore((kt + 1) & 1, cur);
         __syncthreads();
+    };
+    for (int kt = 0; kt < NT; kt += 2) {
+        step(kt, st_a, st_b);
+        if (kt + 1 < NT) step(kt + 1, st_b, st_a);
     }
 
     // ---- finalize: column totals, normalised output, lse ----
