@@ -364,6 +364,23 @@ def test_random_small_shapes(seed):
     compare(out, lse, ref_out, ref_lse, what=f"random {seed}")
 
 
+@pytest.mark.parametrize("P", [0, 32])
+def test_maximum_batch(P):
+    """4096 sequences, the most one call takes: the in-LDS tile prefix over sequences runs
+    16 rounds of 256 (every other test fits one round); short ragged contexts, empty ones
+    included."""
+    rng = np.random.default_rng(40)
+    ctx = rng.integers(0, 61, 4096)
+    ctx[[0, 255, 256, 4095]] = (0, 60, 1, 33)
+    wl = W.make_workload(4096, 4, 2, 64, 16, "f16", ctx, 40, partition_size=P)
+    note(f"maximum batch B=4096 P={P}")
+    q, k, v = W.make_values(wl, DEV, poison=True)
+    tab, dctx = to_dev(wl)
+    out, lse = gpu_decode(wl, q, k, v, tab, dctx)
+    ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
+    compare(out, lse, ref_out, ref_lse, what=f"B=4096 P={P}")
+
+
 def test_table_stride_wider_than_needed():
     wl = small(seed=11, extra_table_entries=40)
     note("table stride > used width")

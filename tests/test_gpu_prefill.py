@@ -102,6 +102,23 @@ def test_prefill_benchmark_shape_sampled():
     note(f"  {len(rows)} sampled rows, max abs err {err:.3g}")
 
 
+def test_prefill_maximum_batch():
+    """4096 sequences, the most one call takes: the in-LDS prefix of query tiles over
+    sequences runs 16 rounds of 256; short chunks and prefixes, empty chunks included."""
+    rng = np.random.default_rng(41)
+    pre = rng.integers(0, 40, 4096).tolist()
+    chk = rng.integers(0, 9, 4096).tolist()
+    chk[0], chk[4095] = 0, 70
+    wl, cu = W.make_prefill_workload(4, 2, 64, 16, "bf16", pre, chk, seed=41)
+    note(f"prefill maximum batch B=4096 total_q={int(cu[-1])}")
+    _, k, v = W.make_values(wl, DEV, poison=True)
+    q = W.make_prefill_q(wl, cu, DEV)
+    ro, rl = oracle.paged_prefill(W.bits16(q), W.bits16(k), W.bits16(v), wl.block_tables, wl.context_lens, cu,
+                                  wl.scale, num_kv_heads=2, block_size=16, dtype=oracle.BF16)
+    out, lse = run_gpu(wl, cu, q, k, v)
+    check(out, lse, ro, rl, "B=4096")
+
+
 def test_prefill_empty_chunks_and_out_of_contract_rows():
     wl, cu = W.make_prefill_workload(8, 2, 64, 16, "bf16", [10, 0, 40], [0, 20, 0], seed=5)
     _, k, v = W.make_values(wl, DEV, poison=True)

@@ -231,6 +231,7 @@ def test_split_sizes_and_workspace():
     ("kv_dtype", pkv.PKV_F32, pkv.PKV_EUNSUPPORTED),
     ("out_dtype", pkv.PKV_F16, pkv.PKV_EUNSUPPORTED),     # q is bf16
     ("table_stride", 3, pkv.PKV_EINVAL),                  # < ceil(1000 / 16)
+    ("num_seqs", 4097, pkv.PKV_EUNSUPPORTED),             # the tile prefix holds 4096 sequences
 ])
 def test_descriptor_errors(field, value, code):
     d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 0, num_waves=64)
