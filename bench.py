@@ -287,12 +287,14 @@ def prefill_leg(steps, warmup, dev):
     }
 
 
-def cpu_baseline(wl, q, k, v, budget_s):
-    """The oracle on the workload's sequences in order, cycling, until the budget is spent."""
+def cpu_baseline(wl, q, k, v, budget_s, nthreads=None):
+    """The oracle on the workload's sequences in order, cycling, until the budget is spent,
+    on nthreads OpenMP threads (default: all the host lets it use)."""
     import torch
     import oracle
     from paged_kv_cache_268_amd import workloads as W
-    nthreads = oracle.max_threads()
+    if nthreads is None:
+        nthreads = oracle.max_threads()
     done_seqs, done_bytes, elapsed = 0, 0, 0.0
     batch = max(1, nthreads // max(1, wl.num_kv_heads))
     i = 0
@@ -504,6 +506,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)
+        one = cpu_baseline(wl, q, k, v, max(1.0, args.cpu_seconds / 5), nthreads=1)
+        res["cpu_baseline"]["single_core"] = {key: one[key] for key in ("value", "unit", "tokens_per_s", "sample")}
     pool.close()
     print(json.dumps(res), flush=True)
 
