@@ -44,11 +44,13 @@ def log(msg):
 
 
 def parse():
+    from paged_kv_cache_268_amd.workloads import CONFIG_NAMES
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, help="decode configuration 1..5")
+    ap.add_argument("--config", type=int, default=3,
+                    help="decode workload 1..5: " + ", ".join(f"{k} = {v}" for k, v in sorted(CONFIG_NAMES.items())))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-K partition (0 = balanced split); default: the workload's own")
     ap.add_argument("--seed", type=int, default=None)
@@ -349,7 +351,7 @@ def main():
     wl = W.config(args.config, seed=args.seed, extra_table_entries=grow_blocks)
     P = wl.partition_size if args.partition_size is None else args.partition_size
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
-    log(f"[bench] config {args.config} {wl.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} {wl.dtype} "
+    log(f"[bench] {wl.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} {wl.dtype} "
         f"sum(ctx)={int(wl.context_lens.sum())} max={wl.max_context_len} blocks={wl.num_blocks} "
         f"meta-sha256={wl.metadata_sha256()[:16]}")
 
@@ -451,7 +453,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) q/K/V, seeded context lengths and shuffled physical blocks)",
         "config": {
-            "workload": f"config {args.config}: {wl.name}",
+            "workload": wl.name,
             "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
             "context_lens": f"sum {int(ctx0.sum())} at start, +1 per step, max {wl.max_context_len}",
             "partition_size": P_used, "accumulate": "fp32", "kv_dtype": wl.dtype,

@@ -69,20 +69,20 @@ def _gpu():
 # Parity on the five configurations
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_parity_config(cid):
+@pytest.mark.parametrize("cid", [1, 2, 3, 4], ids=lambda c: W.CONFIG_NAMES[c])
+def test_parity_decode_workload(cid):
     wl = W.config(cid)
-    note(f"config {cid} {wl.name}: B={wl.num_seqs} ctx sum={int(wl.context_lens.sum())} "
+    note(f"{wl.name}: B={wl.num_seqs} ctx sum={int(wl.context_lens.sum())} "
          f"P={wl.partition_size} blocks={wl.num_blocks}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
-    # The configuration's own split (config 4: fixed 512-token partitions), the
-    # balanced split, and fixed 512-token partitions for all.
+    # The workload's own split (fixed 512-token partitions for the long skewed
+    # one), the balanced split, and fixed 512-token partitions for all.
     for P in sorted({wl.partition_size, 0, 512}):
         out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
-        err = compare(out, lse, ref_out, ref_lse, what=f"config {cid} P={P}")
-        note(f"config {cid} P={P}: max abs err {err:.3g}")
+        err = compare(out, lse, ref_out, ref_lse, what=f"{wl.name} P={P}")
+        note(f"{wl.name} P={P}: max abs err {err:.3g}")
 
 
 def _compact(wl, seqs):
@@ -99,9 +99,9 @@ def _compact(wl, seqs):
     return used, tab, ctx
 
 
-def test_parity_config5_sampled():
+def test_parity_shared_prefix_mix_sampled():
     wl = W.config(5)
-    note(f"config 5 {wl.name}: B={wl.num_seqs} ctx sum={int(wl.context_lens.sum())} blocks={wl.num_blocks}")
+    note(f"{wl.name}: B={wl.num_seqs} ctx sum={int(wl.context_lens.sum())} blocks={wl.num_blocks}")
     q, k, v = W.make_values(wl, DEV, poison=True)
     tab, ctx = to_dev(wl)
     out, lse = gpu_decode(wl, q, k, v, tab, ctx)
@@ -116,10 +116,10 @@ def test_parity_config5_sampled():
     qb = W.bits16(q[seqs])
     ref_out, ref_lse = oracle.paged_decode(qb, kb, vb, ctab, cctx, wl.scale, num_kv_heads=wl.num_kv_heads,
                                            block_size=wl.block_size, dtype=oracle.BF16)
-    err = compare(out[seqs], lse[seqs], ref_out, ref_lse, what="config 5 sample")
-    compare(out512[seqs], lse512[seqs], ref_out, ref_lse, what="config 5 sample P=512")
+    err = compare(out[seqs], lse[seqs], ref_out, ref_lse, what=f"{wl.name} sample")
+    compare(out512[seqs], lse512[seqs], ref_out, ref_lse, what=f"{wl.name} sample P=512")
     assert np.all(np.isfinite(out.cpu().numpy())) and np.all(np.isfinite(out512.cpu().numpy()))
-    note(f"config 5 sample of {len(seqs)}: max abs err {err:.3g}")
+    note(f"{wl.name} sample of {len(seqs)}: max abs err {err:.3g}")
 
 
 # ---------------------------------------------------------------------------

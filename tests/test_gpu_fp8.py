@@ -62,10 +62,10 @@ def compare(out, lse, ro, rl, what):
     return err
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4], ids=lambda c: W.CONFIG_NAMES[c])
 def test_fp8_decode_parity(cid):
     wl = W.config(cid)
-    note(f"8-bit decode, config {cid} {wl.name}: B={wl.num_seqs} blocks={wl.num_blocks}")
+    note(f"8-bit decode, {wl.name}: B={wl.num_seqs} blocks={wl.num_blocks}")
     q = bf16_q(wl, 1000 + cid)
     kc, vc, ks, vs = W.make_fp8_cache(wl, DEV, poison=True)
     tab = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(DEV)
@@ -75,7 +75,7 @@ def test_fp8_decode_parity(cid):
         lse = torch.full((wl.num_seqs, wl.num_q_heads), float("nan"), device=DEV)
         out = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, wl.max_context_len, partition_size=P, lse=lse)
         torch.cuda.synchronize()
-        err = compare(out, lse, ro, rl, f"config {cid} P={P}")
+        err = compare(out, lse, ro, rl, f"{wl.name} P={P}")
         note(f"  P={P}: max abs err {err:.3g}")
     # bf16 output: the fp32 result rounded once
     outb = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, wl.max_context_len, out_dtype=pkv.PKV_BF16)
