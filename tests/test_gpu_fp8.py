@@ -84,6 +84,27 @@ def test_fp8_decode_parity(cid):
     assert np.all(np.abs(ob - ro) <= TOL + np.abs(ro) * 2.0 ** -8)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(6, 3, 64, 32), (32, 8, 128, 32), (20, 4, 64, 16), (3, 1, 128, 32),
+                                         (16, 2, 128, 32)])
+def test_fp8_decode_shapes(Hq, Hkv, D, bs):
+    """The 8-bit instances the decode workloads do not reach: block 32, head dim 64 with a kv
+    group, groups padded to 2, 4 and 8 lanes; lengths around block edges, empty and long."""
+    ctx = [0, 1, bs - 1, bs, bs + 1, 500, 1500, 37]
+    wl = W.make_workload(len(ctx), Hq, Hkv, D, bs, "bf16", ctx, seed=90 + Hq + bs, pool_factor=1.5)
+    note(f"8-bit decode Hq={Hq} Hkv={Hkv} D={D} bs={bs}")
+    q = bf16_q(wl, 91)
+    kc, vc, ks, vs = W.make_fp8_cache(wl, DEV, poison=True)
+    tab = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(DEV)
+    ctx_d = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(DEV)
+    ro, rl = ref_fp8(wl, q, kc, vc, ks, vs)
+    for P in (0, 2 * bs):
+        lse = torch.full((wl.num_seqs, wl.num_q_heads), float("nan"), device=DEV)
+        out = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx_d, wl.scale, wl.max_context_len, partition_size=P, lse=lse)
+        torch.cuda.synchronize()
+        err = compare(out, lse, ro, rl, f"Hq={Hq} Hkv={Hkv} D={D} bs={bs} P={P}")
+        note(f"  P={P}: max abs err {err:.3g}")
+
+
 def test_fp8_poison_and_empty_bit_exact():
     """NaN codes in unused slots change nothing; empty contexts give 0 / -inf."""
     wl = W.make_workload(5, 8, 2, 128, 16, "bf16", [0, 1, 33, 200, 0], seed=77, pool_factor=1.5)
