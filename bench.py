@@ -415,6 +415,16 @@ def main():
     for i in range(N_BREAKDOWN):
         step(e4=ev4[i])
     torch.cuda.synchronize()
+    # Cross-check of the per-launch event timing: back-to-back split-kernel launches
+    # on unchanged inputs between two events, divided by their number.
+    N_B2B = 20
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(N_B2B):
+        pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    b2b_ms = b0.elapsed_time(b1) / N_B2B
 
     ms_step = (t1 - t0) * 1e3 / K
     # K/V bytes each timed step's attention reads: context after that step's append.
@@ -467,6 +477,7 @@ def main():
             "kv_append_event_pass": round(float(np.mean(t_app)), 4),
             "merge_event_pass": round(float(np.mean(t_merge)), 4),
             "partition_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
+            "partition_back_to_back": round(b2b_ms, 4),
         },
         "roofline": {
             "bound": "hbm",
