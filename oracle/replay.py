@@ -35,9 +35,11 @@ What is replayed, from the definitions:
     another holder stays where it is.  In a block list a host block c is written
     -2 - c.  A sequence holding host blocks is parked: it cannot be appended to
     and it publishes length 0 (table row all -1) until it is restored;
-  * the decode split: every (sequence s, kv head g, 16-token tile j) in one
-    sequence-major list -- (s, g)'s tiles start at first(s, g) =
-    Hkv * sum_{s'<s} pt_s' + g * pt_s -- cut into chunks of C tiles.  With a
+  * the decode split: every (sequence s, head group q, 16-token tile j) in one
+    sequence-major list, a group being the H kv heads one wave takes together
+    (H = 2 for 8-bit K/V with an even kv head count, else 1) -- the tiles of
+    kv head g start at first(s, g) = (Hkv / H) * sum_{s'<s} pt_s' + (g // H) * pt_s
+    -- cut into chunks of C tiles.  With a
     fixed partition size P, C = P / 16 and pt_s = ceil(nt_s / C) * C (so a
     chunk is the partition [p*P, min((p+1)*P, n)) of one (s, g)); balanced,
     pt_s = nt_s and C = max(8, ceil(T / W)) for W waves and T tiles in all.
@@ -315,9 +317,10 @@ TILE = 16
 MIN_CHUNK = 8
 
 
-def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, num_waves: int = 1):
+def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, num_waves: int = 1,
+         heads_per_wave: int = 1):
     """Segments (seq, kv_head, slot, tok_lo, tok_hi) of the decode split, in order."""
-    if partition_size < 0 or num_waves < 1:
+    if partition_size < 0 or num_waves < 1 or heads_per_wave < 1 or num_kv_heads % heads_per_wave:
         raise ValueError("bad split parameters")
     lens = [max(0, int(n)) for n in context_lens]
     nt = [ceil_div(n, TILE) for n in lens]
@@ -330,7 +333,7 @@ def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, nu
     acc = 0
     for s in range(len(lens)):
         firsts.append(acc)
-        acc += num_kv_heads * pt[s]
+        acc += (num_kv_heads // heads_per_wave) * pt[s]
     total = acc
     if partition_size == 0:
         C = max(MIN_CHUNK, ceil_div(total, num_waves))
@@ -339,7 +342,7 @@ def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, nu
         for g in range(num_kv_heads):
             if nt[s] == 0:
                 continue
-            first = firsts[s] + g * pt[s]
+            first = firsts[s] + (g // heads_per_wave) * pt[s]
             c0, c1 = first // C, (first + nt[s] - 1) // C
             for ch in range(c0, c1 + 1):
                 j0 = max(ch * C - first, 0)

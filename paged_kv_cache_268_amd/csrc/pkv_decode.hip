@@ -221,9 +221,16 @@ __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
     return fixed_chunk > 0 ? (nt + fixed_chunk - 1) / fixed_chunk * fixed_chunk : nt;
 }
 
-// The split.  All (sequence s, kv head g, tile j) are laid out in one list,
-// sequence-major: (s, g)'s tiles start at first(s, g) = pre[s] + g * pt_s,
-// pre[s] = Hkv * sum_{s' < s} pt_s'.  The list is cut into chunks of C tiles;
+// The split.  A wave takes HW kv heads of each tile: HW = 2 for 8-bit K/V
+// with an even kv head count (the two heads' (block, kv head) pieces are
+// adjacent, so a tile's K and V reads are 4 KiB contiguous at D = 128 instead
+// of 2 KiB), else 1.  All (sequence s, head group q, tile j) are laid out in
+// one list, sequence-major: the tiles of kv head g start at first(s, g) =
+// pre[s] + (g / HW) * pt_s, pre[s] = (Hkv / HW) * sum_{s' < s} pt_s'.  With
+// HW = 2 the B operand holds both heads' q groups (2G columns), the two K
+// tiles go through it in two MFMA chains and each lane keeps the scores of
+// its own column's head; PV runs one chain per head with the other head's
+// columns' weights zero.  The list is cut into chunks of C tiles;
 // wave w of the NW waves in the grid takes chunks w, w + NW, ...  Balanced
 // mode (partition_size 0): pt_s = tiles of s, C = max(kMinChunk, ceil(T / NW))
 // so every wave gets an equal share whatever the lengths.  Fixed mode:
@@ -236,8 +243,8 @@ __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
 // fit, <= 256 VGPRs); the 8-bit ones are held to 168 VGPRs so three fit,
 // which measured about 5 % faster (half the bytes per tile, so more waves
 // keep as many bytes in flight).
-template <int D, int BS, int GP, bool BF16, bool KV8>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1)))
+template <int D, int BS, int GP, bool BF16, bool KV8, int HW>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV8 ? (HW == 2 ? 2 : 3) : 1)))
 paged_decode_split_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;            // MFMA k-steps per tile
     constexpr int KL = KV8 ? D / 64 : KS; // K load instructions per tile (16 bytes per lane each)
@@ -247,6 +254,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     static_assert(GP <= 16, "kv group of at most 16 q heads");
     static_assert(!KV8 || BF16, "8-bit K/V pair with a bf16 query");
     static_assert(NW == 1 || NW == 2 || NW == 4, "V piece of 4, 8 or 16 bytes");
+    static_assert(HW == 1 || HW == 2, "one or two kv heads per wave");
     using MfmaIn = typename MfmaType<BF16>::vec;
     using VLoad = VPiece<NW>;
     constexpr int DEPTH = 2;              // tiles in flight per wave
@@ -263,6 +271,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     // Wave index as a uniform (scalar) value, so loops stay scalar.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int B = a.num_seqs, Hkv = a.num_kv_heads;
+    const int HG = Hkv / HW;              // list entries per (sequence, tile): kv heads taken HW at a time
 
     // ---- prefix of padded tiles over sequences (every workgroup, in LDS) ----
     int running = 0;
@@ -285,11 +294,11 @@ paged_decode_split_kernel(DecodeArgs a) {
             woff += w < wave ? s_wsum[w] : 0;
             tot += s_wsum[w];
         }
-        if (s < B) s_pre[s] = (running + woff + x - v) * Hkv;
+        if (s < B) s_pre[s] = (running + woff + x - v) * HG;
         running += tot;
         __syncthreads();
     }
-    if (threadIdx.x == 0) s_pre[B] = running * Hkv;
+    if (threadIdx.x == 0) s_pre[B] = running * HG;
     __syncthreads();
     const int T = s_pre[B];
     const int C = a.fixed_chunk > 0 ? a.fixed_chunk : max(kMinChunk, (T + a.num_waves - 1) / a.num_waves);
@@ -311,6 +320,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     }
 
     const int G = a.num_q_heads / Hkv;
+    const int GC = HW * G;                // B-operand columns in use: the q heads of the wave's kv heads
     // MFMA operand roles (v_mfma_f32_16x16x32): A = 16 tokens x 32 d of K,
     // B = 32 d x 16 heads of q (heads >= G are zero), C = scores[token][head].
     // Lane l supplies A row l%16 and B column l%16, d-chunk 8*(l/16) of each
@@ -349,27 +359,43 @@ paged_decode_split_kernel(DecodeArgs a) {
     // 16-bit hi and lo parts, times the tile's V scale (8-bit V) or kPScale
     // (the weight sum l keeps the unscaled weights).  8-bit K: codes widened
     // to bf16 in registers, the tile's K scale folded into the score scale.
-    auto qk_softmax = [&](int j, const uint4 (&kb)[KL], const MfmaIn (&qb)[KS], float ksc, float vsc, uint2& phi,
-                          uint2& plo) {
+    // With two kv heads per wave (HW == 2) both heads' K tiles go through the
+    // same B operand (columns [0, G) are the first head's q heads, [G, 2G) the
+    // second's) and each lane keeps the score of its own column's head.
+    const bool second = HW == 2 && mrow >= G;   // this lane's column is a q head of the second kv head
+    auto qk_softmax = [&](int j, const uint4 (&kb)[HW * KL], const MfmaIn (&qb)[KS], float ksc, float vsc,
+                          float ksc1, float vsc1, uint2& phi, uint2& plo) {
         const int t0 = j * kTile;
         const bool full = t0 + kTile <= seg_ctx;
-        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KV8) {
+        floatx4 sch[HW];
 #pragma unroll
-            for (int u = 0; u < KL; ++u) {
-                uint4 lo, hi;
-                fp8x4_to_bf16x4(kb[u].x, lo.x, lo.y);
-                fp8x4_to_bf16x4(kb[u].y, lo.z, lo.w);
-                fp8x4_to_bf16x4(kb[u].z, hi.x, hi.y);
-                fp8x4_to_bf16x4(kb[u].w, hi.z, hi.w);
-                sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, lo), qb[2 * u], sc);
-                sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, hi), qb[2 * u + 1], sc);
+        for (int h = 0; h < HW; ++h) {
+            floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (KV8) {
+#pragma unroll
+                for (int u = 0; u < KL; ++u) {
+                    const uint4 kw = kb[h * KL + u];
+                    uint4 lo, hi;
+                    fp8x4_to_bf16x4(kw.x, lo.x, lo.y);
+                    fp8x4_to_bf16x4(kw.y, lo.z, lo.w);
+                    fp8x4_to_bf16x4(kw.z, hi.x, hi.y);
+                    fp8x4_to_bf16x4(kw.w, hi.z, hi.w);
+                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, lo), qb[2 * u], sc);
+                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, hi), qb[2 * u + 1], sc);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[h * KL + ks]), qb[ks], sc);
             }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = mfma_16x16x32<BF16>(__builtin_bit_cast(MfmaIn, kb[ks]), qb[ks], sc);
+            sch[h] = sc;
         }
-        const float sk = KV8 ? sl2 * ksc : sl2;
+        floatx4 sc = sch[0];
+        if constexpr (HW == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = second ? sch[HW - 1][i] : sc[i];
+        }
+        const float sk = KV8 ? sl2 * (second ? ksc1 : ksc) : sl2;
         float x[4];
         bool need = false;
 #pragma unroll
@@ -383,7 +409,7 @@ paged_decode_split_kernel(DecodeArgs a) {
             float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
             mx = xmax16(mx);
             mx = xmax32(mx);                    // lane (j, n): tile max of head n
-            if (mrow < G && mx > m_lane + kTau) {
+            if (mrow < GC && mx > m_lane + kTau) {
                 const float alpha = __builtin_amdgcn_exp2f(m_lane - mx);   // 0 when m = -inf
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
@@ -392,7 +418,7 @@ paged_decode_split_kernel(DecodeArgs a) {
             }
         }
         // Weights <= 2^TAU; a row past the context has x = -inf and weight 0.
-        const float pm = KV8 ? vsc : kPScale;
+        const float pm = KV8 ? (second ? vsc1 : vsc) : kPScale;
         float pw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -407,14 +433,19 @@ paged_decode_split_kernel(DecodeArgs a) {
     // operand is (V[l/16][e], V[l/16 + 4][e], V[l/16 + 8][e], V[l/16 + 12][e])
     // of the tile in 16-bit form; the weights' hi parts, then lo parts, are
     // the B operand.
-    auto pv = [&](int j, const VLoad (&vb)[NI], uint2 phi, uint2 plo) {
+    auto pv = [&](int j, const VLoad (&vbh)[HW * NI], uint2 phi, uint2 plo) {
         const int t0 = j * kTile;
         const bool full = t0 + kTile <= seg_ctx;
+#pragma unroll
+        for (int h = 0; h < HW; ++h) {
+        // B operand for head h: this lane's weights if its column is a q head of h, else 0.
+        const bool mine = HW == 1 || (h == 1) == second;
+        const uint2 ph = mine ? phi : make_uint2(0u, 0u), pl = mine ? plo : make_uint2(0u, 0u);
         uint32_t w[NI][NW];
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int k = 0; k < NW; ++k) w[i][k] = vb[i].w[k];
+            for (int k = 0; k < NW; ++k) w[i][k] = vbh[h * NI + i].w[k];
         if (!full) {
             // Unused slots may hold anything (NaN included): never let them into a sum.
 #pragma unroll
@@ -449,30 +480,41 @@ paged_decode_split_kernel(DecodeArgs a) {
             }
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], phi, acc[e]);
+        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], ph, acc[e]);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], plo, acc[e]);
+        for (int e = 0; e < EPL; ++e) acc[e] = mfma_16x16x16<BF16>(av[e], pl, acc[e]);
+        }
     };
     // keep: plain loads (the lines stay cached) instead of non-temporal ones.
-    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[KL], bool keep) {
-        const int64_t base = tile_base(j, g, blk);
-        if (keep) {
+    // g is the list's head group: kv heads g * HW .. g * HW + HW - 1, whose
+    // (block, kv head) pieces are adjacent in memory (BS * D values apart).
+    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[HW * KL], bool keep) {
+        const int64_t base = tile_base(j, g * HW, blk);
 #pragma unroll
-            for (int u = 0; u < KL; ++u) kb[u] = *reinterpret_cast<const uint4*>(kc + base + k_off + u * (KV8 ? 64 : 32));
-        } else {
+        for (int h = 0; h < HW; ++h) {
+            const int64_t hb = base + (int64_t)h * BS * D + k_off;
+            if (keep) {
 #pragma unroll
-            for (int u = 0; u < KL; ++u) kb[u] = load_once16(kc + base + k_off + u * (KV8 ? 64 : 32));
+                for (int u = 0; u < KL; ++u) kb[h * KL + u] = *reinterpret_cast<const uint4*>(kc + hb + u * (KV8 ? 64 : 32));
+            } else {
+#pragma unroll
+                for (int u = 0; u < KL; ++u) kb[h * KL + u] = load_once16(kc + hb + u * (KV8 ? 64 : 32));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[NI], bool keep) {
-        const int64_t base = tile_base(j, g, blk);
-        if (keep) {
+    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[HW * NI], bool keep) {
+        const int64_t base = tile_base(j, g * HW, blk);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW, false>(vc + base + v_off + i * 4 * D);
-        } else {
+        for (int h = 0; h < HW; ++h) {
+            const int64_t hb = base + (int64_t)h * BS * D + v_off;
+            if (keep) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i) vb[i] = load_piece<NW, true>(vc + base + v_off + i * 4 * D);
+                for (int i = 0; i < NI; ++i) vb[h * NI + i] = load_piece<NW, false>(vc + hb + i * 4 * D);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) vb[h * NI + i] = load_piece<NW, true>(vc + hb + i * 4 * D);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -481,10 +523,10 @@ paged_decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 w = make_uint4(0, 0, 0, 0);
-            if (mrow < G) {
+            if (mrow < GC) {
                 const int d0 = KV8 ? 16 * (4 * (ks / 2) + kq) + 8 * (ks % 2) : ks * 32 + kq * 8;
                 const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                                     ((int64_t)s * a.num_q_heads + g * G + mrow) * D + d0;
+                                     ((int64_t)s * a.num_q_heads + g * GC + mrow) * D + d0;
                 w = *reinterpret_cast<const uint4*>(qp);
             }
             qb[ks] = __builtin_bit_cast(MfmaIn, w);
@@ -493,10 +535,10 @@ paged_decode_split_kernel(DecodeArgs a) {
     // End of a segment: l per head; lane l holds D/4 values of head l%16.
     auto finish_segment = [&]() {
         const float L = xsum32(xsum16(l_lane));   // lane (j, n): total of head n
-        if (mrow < G) {
+        if (mrow < GC) {
             const float inv = 1.f / (L * kPScale);   // L >= 1: the tile that set the reference has weight 1
             const float lse2 = m_lane + __builtin_amdgcn_logf(L);
-            const int64_t sh = (int64_t)seg_s * a.num_q_heads + seg_g * G + mrow;
+            const int64_t sh = (int64_t)seg_s * a.num_q_heads + seg_g * GC + mrow;
             const int d0 = 4 * EPL * kq;           // acc[e][i] is value d0 + EPL i + e
             if (seg_direct) {
                 // Values d0 .. d0 + 4 EPL - 1 of the row, contiguous: acc[e][i] at EPL i + e.
@@ -548,7 +590,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     // V scales.  A new window (every 128 positions of a chunk) waits for its
     // block ids once.  A position that is not processed still loads the
     // chunk's last real tile (see issue_k: a cache hit).
-    struct Win { int sv, g, j, blk; float ks, vs; };
+    struct Win { int sv, g, j, blk; float ks, vs, ks1, vs1; };
     auto win_info = [&](int p, int hi) -> Win {
         const int pc = min(p, hi - 1);
         int sl = 0, sh = B;                        // invariant: pre[sl] <= pc < pre[sh]
@@ -565,11 +607,15 @@ paged_decode_split_kernel(DecodeArgs a) {
         w.j = min(j, nt - 1);
         w.sv = (p < hi && j < nt) ? sl : ~sl;
         w.blk = a.block_tables[(int64_t)sl * a.table_stride + (w.j * kTile) / BS];
-        w.ks = 1.f;
-        w.vs = 1.f;
+        w.ks = w.vs = w.ks1 = w.vs1 = 1.f;
         if constexpr (KV8) {
-            w.ks = a.k_scale[(int64_t)w.blk * Hkv + w.g];
-            w.vs = a.v_scale[(int64_t)w.blk * Hkv + w.g];
+            const int64_t si = (int64_t)w.blk * Hkv + w.g * HW;   // scales of the group's first kv head
+            w.ks = a.k_scale[si];
+            w.vs = a.v_scale[si];
+            if constexpr (HW == 2) {
+                w.ks1 = a.k_scale[si + 1];
+                w.vs1 = a.v_scale[si + 1];
+            }
         }
         return w;
     };
@@ -588,12 +634,12 @@ paged_decode_split_kernel(DecodeArgs a) {
         };
         // Per pipeline slot: the K, V and q operands of the position it holds,
         // and that position's (~)s, kv head, tile index and scales.
-        uint4 kbuf[DEPTH][KL];
-        VLoad vbuf[DEPTH][NI];
+        uint4 kbuf[DEPTH][HW * KL];
+        VLoad vbuf[DEPTH][HW * NI];
         MfmaIn qs[DEPTH][KS];
         int ps[DEPTH], pg[DEPTH], pj[DEPTH], pblk[DEPTH];
         bool pkeep[DEPTH];
-        float pks[DEPTH], pvs[DEPTH];
+        float pks[DEPTH], pvs[DEPTH], pks1[DEPTH], pvs1[DEPTH];
         // Slot st takes position x: its K, and its q rows when the slot's
         // previous position (x - DEPTH) was another segment or before lo.
         auto issue_k = [&](int st, int x) {
@@ -601,9 +647,14 @@ paged_decode_split_kernel(DecodeArgs a) {
             pg[st] = pick(wlo.g, whi.g, x);
             pj[st] = pick(wlo.j, whi.j, x);
             pblk[st] = pick(wlo.blk, whi.blk, x);
+            pks1[st] = pvs1[st] = 1.f;
             if constexpr (KV8) {
                 pks[st] = pickf(wlo.ks, whi.ks, x);
                 pvs[st] = pickf(wlo.vs, whi.vs, x);
+                if constexpr (HW == 2) {
+                    pks1[st] = pickf(wlo.ks1, whi.ks1, x);
+                    pvs1[st] = pickf(wlo.vs1, whi.vs1, x);
+                }
             } else {
                 pks[st] = pvs[st] = 1.f;
             }
@@ -644,11 +695,11 @@ paged_decode_split_kernel(DecodeArgs a) {
                     seg_direct = (first + seg_nt - 1) / C == first / C;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    m_lane = mrow < G ? -INFINITY : 0.f;
+                    m_lane = mrow < GC ? -INFINITY : 0.f;
                     l_lane = 0.f;
                 }
                 uint2 phi = make_uint2(0u, 0u), plo = make_uint2(0u, 0u);
-                if (live) qk_softmax(j, kbuf[st], qs[st], pks[st], pvs[st], phi, plo);
+                if (live) qk_softmax(j, kbuf[st], qs[st], pks[st], pvs[st], pks1[st], pvs1[st], phi, plo);
                 issue_k(st, x + DEPTH);
                 if (live) pv(j, vbuf[st], phi, plo);
                 issue_v(st);
@@ -709,7 +760,7 @@ paged_decode_merge_kernel(MergeArgs a) {
     const int n = min(max(len, 0), a.max_context_len);
     const int nt = (n + kTile - 1) / kTile;
     const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
-    const int first = pre + g * pt;
+    const int first = pre + (g / a.heads_per_wave) * pt;
     // Empty pairs are written by the split kernel, one-segment pairs directly.
     const int nseg = nt == 0 ? 0 : (first + nt - 1) / C - first / C + 1;
     if (nseg <= 1) return;                     // uniform over a pair's waves
@@ -792,9 +843,9 @@ paged_decode_merge_kernel(MergeArgs a) {
 // Launchers.
 // ---------------------------------------------------------------------------
 
-template <int D, int BS, int GP, bool BF16, bool KV8>
+template <int D, int BS, int GP, bool BF16, bool KV8, int HW>
 static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStream_t stream) {
-    auto kern = paged_decode_split_kernel<D, BS, GP, BF16, KV8>;
+    auto kern = paged_decode_split_kernel<D, BS, GP, BF16, KV8, HW>;
     if (waves_per_cu) {
         int blocks = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kThreads, 0);
@@ -806,30 +857,40 @@ static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStre
     return hipGetLastError();
 }
 
-template <int D, int BS, bool BF16, bool KV8>
+template <int D, int BS, bool BF16, bool KV8, int HW>
 static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st) {
-    switch (gp) {
-        case 1: return split_dispatch<D, BS, 1, BF16, KV8>(a, wpc, st);
-        case 2: return split_dispatch<D, BS, 2, BF16, KV8>(a, wpc, st);
-        case 4: return split_dispatch<D, BS, 4, BF16, KV8>(a, wpc, st);
-        case 8: return split_dispatch<D, BS, 8, BF16, KV8>(a, wpc, st);
+    if constexpr (HW == 1) {
+        switch (gp) {
+            case 1: return split_dispatch<D, BS, 1, BF16, KV8, 1>(a, wpc, st);
+            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 1>(a, wpc, st);
+            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 1>(a, wpc, st);
+            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 1>(a, wpc, st);
+        }
+    } else {
+        switch (gp) {          // columns of two kv heads' q groups: 2 G
+            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 2>(a, wpc, st);
+            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 2>(a, wpc, st);
+            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 2>(a, wpc, st);
+            case 16: return split_dispatch<D, BS, 16, BF16, KV8, 2>(a, wpc, st);
+        }
     }
     return hipErrorInvalidValue;
 }
 
-template <int D, bool BF16, bool KV8>
+template <int D, bool BF16, bool KV8, int HW>
 static hipError_t split_b(const DecodeArgs* a, int bs, int gp, int* wpc, hipStream_t st) {
-    if (bs == 16) return split_g<D, 16, BF16, KV8>(a, gp, wpc, st);
-    if (bs == 32) return split_g<D, 32, BF16, KV8>(a, gp, wpc, st);
+    if (bs == 16) return split_g<D, 16, BF16, KV8, HW>(a, gp, wpc, st);
+    if (bs == 32) return split_g<D, 32, BF16, KV8, HW>(a, gp, wpc, st);
     return hipErrorInvalidValue;
 }
 
 template <int D>
 static hipError_t split_t(const DecodeArgs* a, int bs, int gp, KvKind kind, int* wpc, hipStream_t st) {
     switch (kind) {
-        case KvKind::F16: return split_b<D, false, false>(a, bs, gp, wpc, st);
-        case KvKind::BF16: return split_b<D, true, false>(a, bs, gp, wpc, st);
-        case KvKind::FP8_BF16Q: return split_b<D, true, true>(a, bs, gp, wpc, st);
+        case KvKind::F16: return split_b<D, false, false, 1>(a, bs, gp, wpc, st);
+        case KvKind::BF16: return split_b<D, true, false, 1>(a, bs, gp, wpc, st);
+        case KvKind::FP8_BF16Q: return split_b<D, true, true, 1>(a, bs, gp, wpc, st);
+        case KvKind::FP8_BF16Q_PAIR: return split_b<D, true, true, 2>(a, bs, gp, wpc, st);
     }
     return hipErrorInvalidValue;
 }
@@ -847,13 +908,16 @@ hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKin
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream) {
     if (a.num_waves < kWaves || a.num_waves % kWaves) return hipErrorInvalidValue;
-    if (kind == KvKind::FP8_BF16Q && (!a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
+    const bool pair = kind == KvKind::FP8_BF16Q_PAIR;
+    if ((kind == KvKind::FP8_BF16Q || pair) && (!a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
+    if (a.heads_per_wave != (pair ? 2 : 1) || a.num_kv_heads % a.heads_per_wave) return hipErrorInvalidValue;
     return split_any(&a, head_dim, block_size, group_pad, kind, nullptr, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
     const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
     if (pairs == 0) return hipSuccess;
+    if (a.heads_per_wave < 1 || a.heads_per_wave > 2 || a.num_kv_heads % a.heads_per_wave) return hipErrorInvalidValue;
     // A workgroup per pair where segment lists may be long: the fixed split
     // of a long context, or few pairs (where one long context among short ones
     // spans many of the balanced split's chunks and the grid is small anyway).

@@ -884,6 +884,7 @@ struct Plan {
     int32_t max_seg = 0;
     int32_t num_waves = 0;                  // resolved grid size (0 until resolved)
     int32_t group_pad = 0;
+    int32_t heads_per_wave = 1;             // kv heads one wave takes per tile (2: 8-bit K/V, even Hkv)
     pkv::KvKind kind = pkv::KvKind::F16;
     int32_t out_kind = pkv::kOutF32;
     size_t hdr_bytes = 0, out_bytes = 0, ws_bytes = 0;
@@ -935,8 +936,13 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
     const int64_t per_seq = P > 0 ? (int64_t)pl->max_seg * pl->fixed_chunk : max_tiles;
     if ((int64_t)d->num_seqs * d->num_kv_heads * per_seq >= (int64_t)1 << 30)
         return fail(PKV_EUNSUPPORTED, "too many tiles in one call (num_seqs x kv heads x tiles >= 2^30)");
-    pl->group_pad = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    pl->kind = d->kv_dtype == PKV_FP8_E4M3 ? pkv::KvKind::FP8_BF16Q
+    // 8-bit K/V with an even kv head count: a wave takes two adjacent kv heads
+    // of each tile (4 KiB contiguous per tile at D = 128 instead of 2 KiB).
+    const bool pair = d->kv_dtype == PKV_FP8_E4M3 && d->num_kv_heads % 2 == 0;
+    pl->heads_per_wave = pair ? 2 : 1;
+    const int cols = G * pl->heads_per_wave;  // MFMA B-operand columns in use
+    pl->group_pad = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
+    pl->kind = d->kv_dtype == PKV_FP8_E4M3 ? (pair ? pkv::KvKind::FP8_BF16Q_PAIR : pkv::KvKind::FP8_BF16Q)
              : d->kv_dtype == PKV_BF16    ? pkv::KvKind::BF16
                                           : pkv::KvKind::F16;
     const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_seg;
@@ -952,14 +958,15 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
 int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
     int64_t nw = d->num_waves;
     if (nw == 0) {
-        static int cache[2][2][4][3][64];          // [D][bs][gp][kv kind][device] -> waves per CU
+        static int cache[2][2][5][4][64];          // [D][bs][gp][kv kind][device] -> waves per CU
         static int cus[64];
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
         if (dev < 0 || dev >= 64) return fail(PKV_EUNSUPPORTED, "device index %d", dev);
         const int di = d->head_dim == 128 ? 1 : 0, bi = d->block_size == 32 ? 1 : 0;
-        const int gi = pl->group_pad == 1 ? 0 : pl->group_pad == 2 ? 1 : pl->group_pad == 4 ? 2 : 3;
+        const int gi = pl->group_pad == 1 ? 0 : pl->group_pad == 2 ? 1 : pl->group_pad == 4 ? 2
+                     : pl->group_pad == 8 ? 3 : 4;
         int& wpc = cache[di][bi][gi][(int)pl->kind][dev];
         if (wpc == 0) {
             e = pkv::split_waves_per_cu(d->head_dim, d->block_size, pl->group_pad, pl->kind, &wpc);
@@ -972,7 +979,7 @@ int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
         nw = (int64_t)std::max(wpc, 4) * cus[dev];
     }
     if (pl->fixed_chunk > 0) {
-        const int64_t chunks = (int64_t)d->num_seqs * d->num_kv_heads * pl->max_seg;
+        const int64_t chunks = (int64_t)d->num_seqs * (d->num_kv_heads / pl->heads_per_wave) * pl->max_seg;
         nw = std::min(nw, std::max<int64_t>(chunks, 1));
     }
     nw = std::min<int64_t>((nw + 3) / 4 * 4, (int64_t)1 << 28);
@@ -981,23 +988,25 @@ int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
 }
 
 // The split the kernel makes, replayed on the host for given lengths: calls
-// f(seq, kv_head, slot, tok_lo, tok_hi) for every segment in order.
+// f(seq, kv_head, slot, tok_lo, tok_hi) for every segment in order.  The list
+// holds (sequence, head group, tile), a group being the heads_per_wave kv heads
+// one wave takes together; every head of a group starts at the group's tile.
 template <class F>
 int enumerate_segments(const pkv_attn_desc* d, const Plan& pl, const int32_t* ctx_host, F&& f) {
-    const int B = d->num_seqs, Hkv = d->num_kv_heads;
+    const int B = d->num_seqs, Hkv = d->num_kv_heads, hw = pl.heads_per_wave;
     std::vector<int64_t> pre(B + 1, 0);
     std::vector<int32_t> nt(B), pt(B);
     for (int s = 0; s < B; ++s) {
         const int32_t n = std::min(std::max(ctx_host[s], 0), d->max_context_len);
         nt[s] = (int32_t)ceil_div(n, kTile);
         pt[s] = pl.fixed_chunk > 0 ? (int32_t)(ceil_div(nt[s], pl.fixed_chunk) * pl.fixed_chunk) : nt[s];
-        pre[s + 1] = pre[s] + (int64_t)pt[s] * Hkv;
+        pre[s + 1] = pre[s] + (int64_t)pt[s] * (Hkv / hw);
     }
     const int64_t T = pre[B];
     const int64_t C = pl.fixed_chunk > 0 ? pl.fixed_chunk : std::max<int64_t>(kMinChunk, ceil_div(T, pl.num_waves));
     for (int s = 0; s < B; ++s) {
         for (int g = 0; g < Hkv && nt[s] > 0; ++g) {
-            const int64_t first = pre[s] + (int64_t)g * pt[s];
+            const int64_t first = pre[s] + (int64_t)(g / hw) * pt[s];
             const int64_t c0 = first / C, c1 = (first + nt[s] - 1) / C;
             for (int64_t ch = c0; ch <= c1; ++ch) {
                 const int64_t j0 = std::max<int64_t>(ch * C - first, 0);
@@ -1057,7 +1066,7 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     Plan pl;
     int rc = resolve(d, &pl);
     if (rc) return rc;
-    const bool kv8 = pl.kind == pkv::KvKind::FP8_BF16Q;
+    const bool kv8 = pl.kind == pkv::KvKind::FP8_BF16Q || pl.kind == pkv::KvKind::FP8_BF16Q_PAIR;
     if (kv8 != fp8_call)
         return fail(PKV_EINVAL, kv8 ? "kv_dtype PKV_FP8_E4M3 goes through the _fp8 entry points (they take the scales)"
                                     : "the _fp8 entry points need kv_dtype PKV_FP8_E4M3");
@@ -1092,6 +1101,7 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     a.max_seg = pl.max_seg;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
+    a.heads_per_wave = pl.heads_per_wave;
     hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.kind, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "split kernel launch");
     return PKV_OK;
@@ -1136,6 +1146,7 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     a.max_seg = pl.max_seg;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
+    a.heads_per_wave = pl.heads_per_wave;
     hipError_t e = pkv::launch_merge(a, d->head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "merge kernel launch");
     return PKV_OK;

@@ -14,7 +14,9 @@ constexpr int kMaxSeqs = 4096;   // sequences per decode call (prefix of tile co
 constexpr int kTileTokens = 16;  // tokens per tile of the split
 
 // K/V storage and query type of a decode call.
-enum class KvKind { F16, BF16, FP8_BF16Q };   // FP8_BF16Q: OCP E4M3 K/V with scales, bf16 q
+// FP8_BF16Q: OCP E4M3 K/V with scales, bf16 q; FP8_BF16Q_PAIR: the same with two
+// adjacent kv heads per wave (even kv head counts).
+enum class KvKind { F16, BF16, FP8_BF16Q, FP8_BF16Q_PAIR };
 
 struct DecodeArgs {
     const void* q;
@@ -39,6 +41,7 @@ struct DecodeArgs {
     int32_t max_seg;         // segment slots per (sequence, q head) in the workspace
     int32_t max_context_len;
     int32_t out_dtype;       // kOut*
+    int32_t heads_per_wave;  // kv heads a wave takes per tile: 1, or 2 for FP8_BF16Q_PAIR
 };
 
 struct MergeArgs {
@@ -55,6 +58,7 @@ struct MergeArgs {
     int32_t max_seg;
     int32_t max_context_len;
     int32_t out_dtype;
+    int32_t heads_per_wave;  // as the split kernel's: a kv head g sits in list group g / heads_per_wave
 };
 
 

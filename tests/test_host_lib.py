@@ -176,17 +176,24 @@ def test_bad_pool_arguments():
 # Decode descriptor, plan, workspace, errors (host only)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("P,bs,nw", [(512, 16, 64), (256, 32, 4), (48, 16, 1000), (0, 16, 64), (0, 32, 3072),
-                                       (0, 16, 4), (0, 16, 100000)])
-def test_plan_matches_replay_bit_exact(P, bs, nw):
+@pytest.mark.parametrize("P,bs,nw,kv8", [(512, 16, 64, False), (256, 32, 4, False), (48, 16, 1000, False),
+                                          (0, 16, 64, False), (0, 32, 3072, False), (0, 16, 4, False),
+                                          (0, 16, 100000, False), (0, 16, 64, True), (512, 16, 64, True),
+                                          (0, 32, 3072, True), (48, 16, 4, True)])
+def test_plan_matches_replay_bit_exact(P, bs, nw, kv8):
+    """The library's split equals the replay's; 8-bit K/V with an even kv head
+    count takes the kv heads two per wave (list over head pairs)."""
     rng = np.random.default_rng(0)
     ctx = rng.integers(0, 5000, 37).astype(np.int32)
     ctx[3] = 0
     ctx[5] = 512
     ctx[6] = 1
     d = pkv.attn_desc(37, 32, 8, 128, bs, 10000, 400, int(ctx.max()), P, num_waves=nw)
+    if kv8:
+        d.kv_dtype, d.q_dtype = pkv.PKV_FP8_E4M3, pkv.PKV_BF16
     got = pkv.plan(d, ctx)
-    want = np.array(R.plan(ctx.tolist(), 8, P, pkv.grid_waves(d)), dtype=np.int32).reshape(-1, 5)
+    want = np.array(R.plan(ctx.tolist(), 8, P, pkv.grid_waves(d), heads_per_wave=2 if kv8 else 1),
+                    dtype=np.int32).reshape(-1, 5)
     assert np.array_equal(got, want)
     # Every token of every (seq, kv head) is covered exactly once, in order.
     for s in range(37):
