@@ -105,6 +105,59 @@ def test_fp8_decode_shapes(Hq, Hkv, D, bs):
         note(f"  P={P}: max abs err {err:.3g}")
 
 
+@pytest.mark.parametrize("P,nw", [(0, 8), (0, 16), (256, 4)])
+def test_fp8_pair_segments_are_the_plan(P, nw):
+    """With two kv heads per wave, each segment in the workspace equals the oracle on its token
+    range, at the slot the host plan gives for its own kv head (both heads of a pair share a
+    tile list entry and so a slot), and nothing else is written."""
+    lens = [5, 700, 1024, 1500, 0, 33]
+    wl = W.make_workload(len(lens), 32, 8, 128, 16, "bf16", lens, seed=93, pool_factor=1.5)
+    note(f"8-bit pair workspace segments vs oracle sub-ranges, P={P} nw={nw}")
+    q = bf16_q(wl, 94)
+    kc, vc, ks, vs = W.make_fp8_cache(wl, DEV, poison=True)
+    tab = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(DEV)
+    ctx = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(DEV)
+    desc = pkv.desc_for(q, kc, tab, wl.max_context_len, P, num_waves=nw)
+    ws = pkv.alloc_workspace(desc, DEV)
+    _, seg_out, seg_lse = pkv.workspace_views(desc, ws)
+    seg_out.fill_(float("nan"))
+    seg_lse.fill_(float("nan"))
+    out = torch.zeros(q.shape, device=DEV)
+    lse = torch.zeros(q.shape[:2], device=DEV)
+    pkv.decode_partials_fp8(desc, q, kc, vc, ks, vs, tab, ctx, wl.scale, out, lse, ws)
+    torch.cuda.synchronize()
+    seg_out, seg_lse = seg_out.cpu().numpy(), seg_lse.cpu().numpy()
+    items = pkv.plan(desc, wl.context_lens)
+    want = R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc), heads_per_wave=2)
+    assert np.array_equal(items, np.array(want, dtype=np.int32).reshape(-1, 5))
+    G = wl.num_q_heads // wl.num_kv_heads
+    nseg = {}
+    for s_, g, _, _, _ in items.tolist():
+        nseg[(s_, g)] = nseg.get((s_, g), 0) + 1
+    ro, rl = ref_fp8(wl, q, kc, vc, ks, vs)
+    used = np.zeros(seg_lse.shape, dtype=bool)
+    for s_, g, kslot, lo, hi in items.tolist():
+        heads = slice(g * G, (g + 1) * G)
+        if nseg[(s_, g)] == 1:                                 # written straight to out
+            compare(out[s_, heads][None], lse[s_, heads][None], ro[s_, heads][None], rl[s_, heads][None],
+                    "direct")
+            continue
+        los = np.zeros(wl.num_seqs, np.int32)
+        his = np.zeros(wl.num_seqs, np.int32)
+        los[s_], his[s_] = lo, hi
+        so, sl = oracle.paged_decode(W.bits16(q), u8(kc), u8(vc), wl.block_tables, wl.context_lens, wl.scale,
+                                     num_kv_heads=wl.num_kv_heads, block_size=wl.block_size, dtype=oracle.BF16,
+                                     kv_dtype=oracle.FP8, k_scale=ks.cpu().numpy(), v_scale=vs.cpu().numpy(),
+                                     tok_lo=los, tok_hi=his)
+        assert np.abs(seg_out[s_, heads, kslot] - so[s_, heads]).max() <= TOL
+        assert np.abs(seg_lse[s_, heads, kslot] / np.log2(np.e) - sl[s_, heads]).max() <= TOL
+        used[s_, heads, kslot] = True
+    assert np.all(np.isnan(seg_lse[~used]))                    # nothing else was written
+    pkv.merge(desc, ctx, out, lse, ws)
+    torch.cuda.synchronize()
+    compare(out, lse, ro, rl, "merged")
+
+
 def test_fp8_poison_and_empty_bit_exact():
     """NaN codes in unused slots change nothing; empty contexts give 0 / -inf."""
     wl = W.make_workload(5, 8, 2, 128, 16, "bf16", [0, 1, 33, 200, 0], seed=77, pool_factor=1.5)
