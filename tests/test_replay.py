@@ -142,6 +142,35 @@ def test_plan_balanced_worked_example():
                      (3, 0, 0, 0, 7), (3, 1, 0, 0, 7)]
 
 
+def test_plan_two_heads_per_wave_worked_example():
+    # Two kv heads taken together: the list holds one entry per (sequence,
+    # pair, tile), 3 + 13 = 16 tiles; 2 waves -> C = 8.  Sequence 1 starts at
+    # tile 3: its tiles 0..4 fall in chunk 0, 5..12 in chunk 1, for both heads.
+    items = R.plan([40, 200], num_kv_heads=2, partition_size=0, num_waves=2, heads_per_wave=2)
+    assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200),
+                     (1, 1, 0, 0, 80), (1, 1, 1, 80, 200)]
+    # One head per wave on the same input: 32 tiles, C = 16, and head 1 of
+    # sequence 1 starts at tile 19, so the two heads are cut differently.
+    items = R.plan([40, 200], num_kv_heads=2, partition_size=0, num_waves=2)
+    assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 160), (1, 0, 1, 160, 200),
+                     (1, 1, 0, 0, 200)]
+
+
+@pytest.mark.parametrize("P,nw", [(0, 1), (0, 7), (0, 64), (0, 5000), (256, 3), (512, 100)])
+def test_plan_pairs_equal_half_the_heads(P, nw):
+    # With two heads per wave the list over Hkv heads is the one-head list over
+    # Hkv / 2 heads, and each of its segments belongs to both heads of a pair.
+    rng = random.Random(nw + P)
+    lens = [rng.randrange(3000) for _ in range(37)] + [0, 1, 16, 17, 128, 129]
+    for hkv in (2, 4, 8):
+        pair = R.plan(lens, hkv, P, nw, heads_per_wave=2)
+        half = R.plan(lens, hkv // 2, P, nw)
+        want = [(s, 2 * g + h, k, lo, hi) for (s, g, k, lo, hi) in half for h in (0, 1)]
+        assert sorted(pair) == sorted(want)
+    with pytest.raises(ValueError):
+        R.plan(lens, 3, P, nw, heads_per_wave=2)
+
+
 # ---------------------------------------------------------------- host tier
 
 GOLDEN_TIER = os.path.join(os.path.dirname(__file__), "golden", "tiered_evict_to_cpu.json")
