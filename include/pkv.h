@@ -263,9 +263,12 @@ int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t tabl
  *   v_cache      : device [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype
  *   block_tables : device int32, row s at block_tables + s * table_stride
  *   context_lens : device int32 [num_seqs], each in [0, max_context_len]
- *   out          : device [num_seqs][num_q_heads][head_dim], out_dtype
+ *   out          : device [num_seqs][num_q_heads][head_dim], out_dtype; 16-byte
+ *                  aligned for PKV_F32, 8-byte aligned for 16-bit outputs
  *   lse          : device float [num_seqs][num_q_heads] or NULL: natural-log
- *                  sum of exp(scores); -inf for an empty context
+ *                  sum of exp(scores); -inf for an empty context; 4-byte aligned
+ * q, k_cache and v_cache are 16-byte aligned; tables and lengths 4-byte.  A
+ * misaligned pointer is refused with PKV_EINVAL before anything is enqueued.
  *
  * For q head h the kv head is h / (num_q_heads / num_kv_heads) (contiguous
  * GQA groups).  out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) V[t] over
@@ -338,8 +341,8 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
 
 /* ------------------------------------------------------------------------
  * Decode over an 8-bit K/V cache (kv_dtype PKV_FP8_E4M3, q_dtype PKV_BF16).
- * Reduced-precision storage of cached K/V ("LLM+Agent 全栈推理底座" 5.2 keeps
- * historical KV at reduced precision) in the OCP E4M3 format with one fp32
+ * Reduced-precision storage of cached K/V ("从零开始构建LLM推理引擎：模型执行器深度解析"
+ * 5.2, KV缓存管理技巧: historical KV kept at reduced precision) in the OCP E4M3 format with one fp32
  * scale per (block, kv head):
  *   k_cache, v_cache : device uint8 [num_blocks][num_kv_heads][block_size][head_dim]
  *   k_scale, v_scale : device float [num_blocks][num_kv_heads]

@@ -39,7 +39,8 @@
  * infinities), and every (block, kv head) of K and of V carries one fp32
  * scale: the value a code stands for is its E4M3 value times the scale of its
  * block and kv head.  This is the KV-compression idea of
- * "LLM+Agent 全栈推理底座" 5.2 (historical KV kept at reduced precision) carried
+ * "从零开始构建LLM推理引擎：模型执行器深度解析" 5.2, KV缓存管理技巧 (historical
+ * KV kept at reduced precision) carried
  * to an 8-bit format with per-block scales; the pages fix neither the format
  * nor the scale granularity.
  *

@@ -223,12 +223,23 @@ class PoolReplay:
         for b in blocks:
             self._unref(b)
 
+    def _copies(self, tails: Sequence[int]) -> int:
+        """Blocks copy-on-write takes for the listed shared tails (one entry per listed
+        sequence that writes into its shared, partly filled tail block).  The sequences
+        copy in list order while the tail has another holder and each copy drops one
+        reference, so k listed holders of a tail held r times take min(k, r - 1) copies."""
+        n = 0
+        for b in set(tails):
+            n += min(tails.count(b), self.ref[b] - 1)
+        return n
+
     # -- append one token to each listed sequence (all-or-nothing) --------
     def append(self, seq_ids: Sequence[int]) -> List[AppendItem]:
         ids = [int(s) for s in seq_ids]
         if len(set(ids)) != len(ids):
             raise PoolError("EINVAL", "duplicate sequence id")
         need = 0
+        tails = []
         for s in ids:
             if s not in self.seqs:
                 raise PoolError("EINVAL", "unknown sequence")
@@ -240,7 +251,8 @@ class PoolReplay:
                     raise PoolError("EINVAL", "sequence reached max_blocks_per_seq")
                 need += 1
             elif self.ref[blocks[-1]] > 1:
-                need += 1
+                tails.append(blocks[-1])
+        need += self._copies(tails)
         if need > len(self.free):
             raise PoolError("ENOMEM", "pool exhausted")
         items = []
@@ -272,6 +284,7 @@ class PoolReplay:
         if len(ids) != len(cnt) or len(set(ids)) != len(ids) or any(c < 0 for c in cnt):
             raise PoolError("EINVAL", "bad sequence list or counts")
         need = 0
+        tails = []
         for s, c in zip(ids, cnt):
             if s not in self.seqs:
                 raise PoolError("EINVAL", "unknown sequence")
@@ -284,7 +297,8 @@ class PoolReplay:
                 raise PoolError("EINVAL", "sequence would exceed max_blocks_per_seq")
             need += blocks_needed(t + c, self.bs) - blocks_needed(t, self.bs)
             if t % self.bs and self.ref[blocks[-1]] > 1:
-                need += 1
+                tails.append(blocks[-1])
+        need += self._copies(tails)
         if need > len(self.free):
             raise PoolError("ENOMEM", "pool exhausted")
         items = []

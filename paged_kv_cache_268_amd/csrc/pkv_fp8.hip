@@ -1,6 +1,6 @@
 // pkv_fp8.hip -- 16-bit K/V blocks -> OCP E4M3 blocks with one fp32 scale per
 // (block, kv head), for the 8-bit cache (reduced-precision storage of cached
-// K/V, "LLM+Agent 全栈推理底座" 5.2).
+// K/V, "从零开始构建LLM推理引擎：模型执行器深度解析" 5.2, KV缓存管理技巧).
 //
 // One wave per (item, kv head), four per workgroup: the largest magnitude over
 // the block's first `used` rows of K and of V, scale = amax / 448 (1 when every

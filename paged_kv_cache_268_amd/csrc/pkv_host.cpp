@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -370,10 +371,29 @@ static pkv::AppendItem take_slot(pkv_pool* p, int32_t s) {
     return it;
 }
 
+// Blocks that copy-on-write takes in one call, given the shared (reference
+// count > 1), partly filled tail block of every listed sequence that writes
+// into its tail.  Sequences copy in list order while the tail still has
+// another holder, and each copy drops one reference, so k listed holders of a
+// tail held r times take min(k, r - 1) copies: when every holder is listed,
+// the last one writes in place.
+static int64_t cow_blocks(const pkv_pool* p, std::vector<int32_t>& tails) {
+    std::sort(tails.begin(), tails.end());
+    int64_t n = 0;
+    for (size_t i = 0; i < tails.size();) {
+        size_t j = i;
+        while (j < tails.size() && tails[j] == tails[i]) ++j;
+        n += std::min<int64_t>((int64_t)(j - i), (int64_t)p->ref[tails[i]] - 1);
+        i = j;
+    }
+    return n;
+}
+
 static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::AppendItem* items, bool* any_copy) {
     if (n < 0 || (n > 0 && !seq_ids)) return fail(PKV_EINVAL, "kv_reserve: bad n or seq_ids");
     const int32_t bs = p->d.block_size;
     std::vector<uint8_t> mark(p->d.max_seqs, 0);
+    std::vector<int32_t> shared_tails;
     int64_t need = 0;
     for (int32_t i = 0; i < n; ++i) {
         const int32_t s = seq_ids[i];
@@ -387,9 +407,10 @@ static int reserve_impl(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv::App
                 return fail(PKV_EINVAL, "kv_reserve: sequence %d is full (%d blocks)", s, p->d.max_blocks_per_seq);
             ++need;
         } else if (p->ref[p->blocks[s].back()] > 1) {
-            ++need;
+            shared_tails.push_back(p->blocks[s].back());
         }
     }
+    need += cow_blocks(p, shared_tails);
     if (need > p->num_free)
         return fail(PKV_ENOMEM, "kv_reserve: need %lld blocks, %d free", (long long)need, p->num_free);
     bool copy = false;
@@ -498,6 +519,7 @@ int kv_append_tokens(pkv_pool* p, int32_t n, const int32_t* seq_ids, const int32
     if (kv8 && !p->k_scale) return fail(PKV_EINVAL, "kv_append_tokens: 8-bit pool without scales (kv_block_pool_set_fp8_scales)");
     const int32_t bs = p->d.block_size;
     std::vector<uint8_t> mark(p->d.max_seqs, 0);
+    std::vector<int32_t> shared_tails;
     int64_t need = 0, total = 0, cows = 0;
     for (int32_t i = 0; i < n; ++i) {
         const int32_t s = seq_ids[i], c = counts[i];
@@ -512,11 +534,12 @@ int kv_append_tokens(pkv_pool* p, int32_t n, const int32_t* seq_ids, const int32
             return fail(PKV_EINVAL, "kv_append_tokens: sequence %d would exceed %d blocks", s, p->d.max_blocks_per_seq);
         need += ceil_div(t + c, bs) - ceil_div(t, bs);
         if (t % bs && p->ref[p->blocks[s].back()] > 1) {
-            ++need;
-            ++cows;
+            shared_tails.push_back(p->blocks[s].back());
+            ++cows;                              // upper bound: sizes the staging buffer
         }
         total += c;
     }
+    need += cow_blocks(p, shared_tails);
     if (need > p->num_free)
         return fail(PKV_ENOMEM, "kv_append_tokens: need %lld blocks, %d free", (long long)need, p->num_free);
     if (total == 0) return PKV_OK;
@@ -958,8 +981,12 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
 int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
     int64_t nw = d->num_waves;
     if (nw == 0) {
-        static int cache[2][2][5][4][64];          // [D][bs][gp][kv kind][device] -> waves per CU
-        static int cus[64];
+        // Occupancy and CU count per (instance, device), looked up once.  The
+        // values are properties of the device and the code object, so threads
+        // that race here store the same numbers; the entries are atomics so
+        // that concurrent calls (on distinct pools or workspaces) are safe.
+        static std::atomic<int> cache[2][2][5][4][64];   // [D][bs][gp][kv kind][device] -> waves per CU
+        static std::atomic<int> cus[64];
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -967,16 +994,20 @@ int resolve_waves(const pkv_attn_desc* d, Plan* pl) {
         const int di = d->head_dim == 128 ? 1 : 0, bi = d->block_size == 32 ? 1 : 0;
         const int gi = pl->group_pad == 1 ? 0 : pl->group_pad == 2 ? 1 : pl->group_pad == 4 ? 2
                      : pl->group_pad == 8 ? 3 : 4;
-        int& wpc = cache[di][bi][gi][(int)pl->kind][dev];
+        std::atomic<int>& slot = cache[di][bi][gi][(int)pl->kind][dev];
+        int wpc = slot.load(std::memory_order_relaxed);
         if (wpc == 0) {
             e = pkv::split_waves_per_cu(d->head_dim, d->block_size, pl->group_pad, pl->kind, &wpc);
             if (e != hipSuccess) return fail_hip(e, "occupancy query");
+            slot.store(wpc, std::memory_order_relaxed);
         }
-        if (cus[dev] == 0) {
-            e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        int ncu = cus[dev].load(std::memory_order_relaxed);
+        if (ncu == 0) {
+            e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+            cus[dev].store(ncu, std::memory_order_relaxed);
         }
-        nw = (int64_t)std::max(wpc, 4) * cus[dev];
+        nw = (int64_t)std::max(wpc, 4) * ncu;
     }
     if (pl->fixed_chunk > 0) {
         const int64_t chunks = (int64_t)d->num_seqs * (d->num_kv_heads / pl->heads_per_wave) * pl->max_seg;
@@ -1020,15 +1051,21 @@ int enumerate_segments(const pkv_attn_desc* d, const Plan& pl, const int32_t* ct
     return PKV_OK;
 }
 
+// Decode pointers.  Outputs: the kernels store rows of fp32 out with 16-byte
+// vector stores and 16-bit out with 4-byte stores, so out must be 16-byte
+// (fp32) or 8-byte (16-bit) aligned; lse (nullable) 4-byte aligned.
 int check_ptrs(const Plan& pl, const void* q, const void* k, const void* v, const int32_t* tables,
-               const int32_t* lens, const void* out, const void* ws, size_t ws_bytes, bool need_inputs) {
+               const int32_t* lens, const void* out, const float* lse, const void* ws, size_t ws_bytes,
+               bool need_inputs) {
     if (need_inputs) {
         if (!q || !k || !v || !tables || !lens) return fail(PKV_EINVAL, "null input pointer");
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(tables, 4) || !aligned(lens, 4))
             return fail(PKV_EINVAL, "q, k_cache, v_cache must be 16-byte aligned");
     }
     if (!out) return fail(PKV_EINVAL, "null out");
-    if (!aligned(out, pl.out_kind == pkv::kOutF32 ? 4 : 2)) return fail(PKV_EINVAL, "out misaligned");
+    if (!aligned(out, pl.out_kind == pkv::kOutF32 ? 16 : 8))
+        return fail(PKV_EINVAL, "out must be %d-byte aligned", pl.out_kind == pkv::kOutF32 ? 16 : 8);
+    if (lse && !aligned(lse, 4)) return fail(PKV_EINVAL, "lse must be 4-byte aligned");
     if (!ws || ws_bytes < pl.ws_bytes)
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, pl.ws_bytes);
     if (!aligned(ws, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
@@ -1073,7 +1110,7 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     if (kv8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
         return fail(PKV_EINVAL, "8-bit K/V: null or misaligned k_scale / v_scale");
     if (d->num_seqs == 0) return PKV_OK;
-    rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, workspace, workspace_bytes, true);
+    rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes, true);
     if (rc) return rc;
     rc = resolve_waves(d, &pl);
     if (rc) return rc;
@@ -1129,7 +1166,7 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     if (rc) return rc;
     if (d->num_seqs == 0 || pl.max_seg <= 1) return PKV_OK;
     if (!context_lens || !aligned(context_lens, 4)) return fail(PKV_EINVAL, "null context_lens");
-    rc = check_ptrs(pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, workspace, workspace_bytes, false);
+    rc = check_ptrs(pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, lse, workspace, workspace_bytes, false);
     if (rc) return rc;
     const char* ws = reinterpret_cast<const char*>(workspace);
     pkv::MergeArgs a{};

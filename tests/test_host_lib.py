@@ -277,6 +277,55 @@ def test_misaligned_inputs_are_refused():
     assert rc == pkv.PKV_EINVAL
 
 
+@pytest.mark.parametrize("out_dtype,offset,code", [
+    (pkv.PKV_F32, 4, pkv.PKV_EINVAL),       # fp32 out: 16-byte vector stores
+    (pkv.PKV_F32, 8, pkv.PKV_EINVAL),
+    (pkv.PKV_F32, 16, None),
+    (pkv.PKV_BF16, 2, pkv.PKV_EINVAL),      # 16-bit out: 8-byte alignment
+    (pkv.PKV_BF16, 4, pkv.PKV_EINVAL),
+    (pkv.PKV_BF16, 8, None),
+])
+def test_out_alignment(out_dtype, offset, code):
+    """The decode stores its output rows with 16-byte (fp32) or 4-byte (16-bit) vector stores;
+    out must be 16- or 8-byte aligned, lse 4-byte aligned."""
+    d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 100, 0, out_dtype=out_dtype, num_waves=64)
+    lib = pkv.load()
+    ok = ctypes.c_void_p(1 << 20)
+    out = ctypes.c_void_p((1 << 21) + offset)
+    for fn in (lib.paged_attn_decode, lib.paged_attn_decode_partials):
+        rc = fn(ctypes.byref(d), ok, ok, ok, ok, ok, ctypes.c_float(1.0), out, None, ok, 1 << 30, None)
+        if code is not None:
+            assert rc == code, pkv.last_error()
+            assert "out" in pkv.last_error()
+    rc = lib.paged_attn_merge(ctypes.byref(d), ok, out, None, ok, 1 << 30, None)
+    if code is not None:
+        assert rc == code
+    lse_bad = ctypes.c_void_p((1 << 22) + 2)
+    rc = lib.paged_attn_decode(ctypes.byref(d), ok, ok, ok, ok, ok, ctypes.c_float(1.0), ok, lse_bad, ok, 1 << 30,
+                               None)
+    assert rc == pkv.PKV_EINVAL and "lse" in pkv.last_error()
+
+
+def test_reserve_shared_tail_with_one_free_block():
+    """Two forked sequences share a partly filled tail; one free block is enough to append
+    to both in one call (the first copies, the second then holds the tail alone and writes
+    in place).  The library and the replay agree bit for bit, ENOMEM is not raised."""
+    lp, ref = _pool_pair(3, 16, 3, 2, [0, 1, 2])
+    a = lp.add(); ref.add_seq()
+    for _ in range(2):
+        lp.reserve([a]); ref.append([a])
+    b = lp.fork(a); ref.fork(a)
+    c = lp.add(); ref.add_seq()
+    lp.reserve([c]); ref.append([c])
+    assert lp.stats()[0] == 1 and lp.stats(0)[2] == 2
+    items = lp.reserve([a, b])
+    want = ref.append([a, b])
+    assert items.tolist() == [list(w) for w in want]
+    assert items.tolist() == [[a, 2 * 16 + 2, 0, 2, 0, 2, 3], [b, 2, 0, -1, -1, 0, 3]]
+    _same_state(lp, ref, 3)
+    lp.close()
+
+
 def test_validate_tables():
     tab = np.array([[3, 1, -1], [0, -1, -1]], dtype=np.int32)
     pkv.validate_tables(tab, [20, 16], num_blocks=4, block_size=16)

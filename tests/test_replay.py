@@ -80,6 +80,58 @@ def test_fork_copy_on_write():
     assert pool.free[-1] == 1 and pool.ref[3] == 1
 
 
+def test_shared_tail_listed_holders_charge_min_k_r_minus_1():
+    """Two forked sequences share a partly filled tail and are appended in one call with a
+    single free block: the first copies (the tail then has one holder left), the second
+    writes in place, so one block suffices (worked by hand)."""
+    pool = R.PoolReplay(3, 4, max_seqs=3, max_blocks_per_seq=2, alloc_order=[0, 1, 2])
+    a = pool.add_seq()
+    pool.append([a])
+    pool.append([a])                             # a: block 0, 2 tokens
+    b = pool.fork(a)                             # block 0 held twice
+    c = pool.add_seq()
+    pool.append([c])                             # c: block 1; free list [2]
+    assert pool.num_free() == 1 and pool.ref[0] == 2
+    ia, ib = pool.append([a, b])
+    assert tuple(ia) == (a, 2 * 4 + 2, 0, 2, 0, 2, 3)   # a copies block 0's 2 rows into block 2
+    assert tuple(ib) == (b, 0 * 4 + 2, 0, -1, -1, 0, 3)  # b is the last holder: in place
+    assert pool.num_free() == 0 and pool.ref[0] == 1 and pool.ref[2] == 1
+    # the same through append_tokens (one token each)
+    pool2 = R.PoolReplay(3, 4, max_seqs=3, max_blocks_per_seq=2, alloc_order=[0, 1, 2])
+    a = pool2.add_seq()
+    pool2.append_tokens([a], [2])
+    b = pool2.fork(a)
+    c = pool2.add_seq()
+    pool2.append([c])
+    items = pool2.append_tokens([a, b], [1, 1])
+    assert [tuple(i) for i in items] == [(a, 10, 0, 2, 0, 2, 3), (b, 2, 0, -1, -1, 0, 3)]
+
+
+def test_shared_tail_three_holders():
+    """A tail held by three sequences: listing two of them takes two copies, listing all
+    three also takes two (the last one writes in place); one block short is ENOMEM."""
+    for listed, copies in ((2, 2), (3, 2)):
+        pool = R.PoolReplay(4, 4, max_seqs=4, max_blocks_per_seq=2, alloc_order=[0, 1, 2, 3])
+        a = pool.add_seq()
+        pool.append([a])                         # block 0, 1 token
+        b, c = pool.fork(a), pool.fork(a)        # held three times; free [3, 2, 1]
+        ids = [a, b, c][:listed]
+        d = pool.add_seq()
+        pool.append([d])                         # block 1 to d; free [3, 2]
+        assert pool.num_free() == copies
+        items = pool.append(ids)
+        assert sum(1 for it in items if it[4] >= 0) == copies
+        assert pool.num_free() == 0
+        pool3 = R.PoolReplay(4, 4, max_seqs=5, max_blocks_per_seq=2, alloc_order=[0, 1, 2, 3])
+        a = pool3.add_seq()
+        pool3.append([a])
+        b, c = pool3.fork(a), pool3.fork(a)
+        d, e = pool3.add_seq(), pool3.add_seq()
+        pool3.append([d, e])                     # free [3]: one block short
+        with pytest.raises(R.PoolError):
+            pool3.append([a, b, c][:listed])
+
+
 def test_free_returns_blocks_lifo():
     pool = R.PoolReplay(4, 2, max_seqs=2, max_blocks_per_seq=4, alloc_order=[0, 1, 2, 3])
     a = pool.add_seq()
