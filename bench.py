@@ -101,8 +101,15 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(config_id, steps, warmup):
-    """HBM bytes per decode launch from the counter summary, or None if it does not apply."""
+def measured_traffic(config_id, algorithmic_bytes):
+    """HBM bytes per decode launch, or None if the counter summary does not apply.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE per launch (scaled by the counters' reading of
+    a copy of known size) and the algorithmic bytes of the same launches.  It applies while
+    the kernel sources hash to the value recorded with it and it was taken on the same
+    workload; the step counts may differ (contexts grow by one token per step), so the
+    measured traffic per algorithmic byte is carried over to this run's algorithmic bytes.
+    """
     try:
         with open(TRAFFIC_SUMMARY) as f:
             fields = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
@@ -111,12 +118,25 @@ def measured_traffic(config_id, steps, warmup):
     fields = {k.strip(): v.strip() for k, v in fields.items()}
     if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
-    if fields.get("workload_args") != f"--config {config_id} --steps {steps} --warmup {warmup}":
+    if fields.get("workload_args", "").split()[:2] != ["--config", str(config_id)]:
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+        ratio = int(fields["traffic_bytes_per_launch"]) / int(fields["algorithmic_bytes_per_launch"])
+    except (KeyError, ValueError, ZeroDivisionError):
         return None
+    return int(round(ratio * algorithmic_bytes))
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, per direction
@@ -234,8 +254,9 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
     o16 = pkv.decode(q, k, v, tables, lens, wl.scale, max_ctx).float()
     torch.cuda.synchronize()
     err = float((o8 - o16).abs().max())
+    kept = {"out": o8.cpu(), "k_scale": ks.cpu().numpy(), "v_scale": vs.cpu().numpy()}
     del kc, vc, ks, vs, ws
-    return {
+    return kept, {
         "kernel": "paged_decode_split_kernel (E4M3 K/V)",
         "kv_dtype": "e4m3 + fp32 scale per (block, kv head)",
         "split_ms": round(part, 4), "split_plus_merge_ms": round(whole, 4),
@@ -245,6 +266,7 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
         "tokens_per_s_decode_only": round(wl.num_seqs / (whole * 1e-3), 1),
         "speedup_vs_16bit_split": None,
         "max_abs_diff_vs_16bit_path": round(err, 5),
+        "vs_16bit_oracle": None,
     }
 
 
@@ -289,12 +311,72 @@ def prefill_leg(steps, warmup, dev):
     }
 
 
-def cpu_baseline(wl, q, k, v, budget_s, nthreads=None):
-    """The oracle on the workload's sequences in order, cycling, until the budget is spent,
-    on nthreads OpenMP threads (default: all the host lets it use)."""
+def oracle_on(wl, q, k, v, tables, lens, seqs, nthreads):
+    """The oracle on the listed sequences of the given state (host tables and lengths), over
+    only the blocks they use: (out [n][Hq][D], lse [n][Hq]) in fp64."""
     import torch
     import oracle
     from paged_kv_cache_268_amd import workloads as W
+    rows = tables[seqs]
+    ctx = lens[seqs]
+    used = sorted({int(b) for j in range(len(seqs)) for b in rows[j, :-(-int(ctx[j]) // wl.block_size)]})
+    remap = {b: n for n, b in enumerate(used)}
+    tab = np.full_like(rows, -1)
+    for j in range(len(seqs)):
+        nb = -(-int(ctx[j]) // wl.block_size)
+        tab[j, :nb] = [remap[int(b)] for b in rows[j, :nb]]
+    idx = torch.tensor(used, device=k.device)
+    kb, vb = W.bits16(k.index_select(0, idx)), W.bits16(v.index_select(0, idx))
+    qb = W.bits16(q[seqs])
+    return oracle.paged_decode(qb, kb, vb, tab, ctx, wl.scale, num_kv_heads=wl.num_kv_heads,
+                               block_size=wl.block_size, dtype=oracle.BF16 if wl.dtype == "bf16" else oracle.F16,
+                               nthreads=nthreads)
+
+
+PARITY_TOL = 2e-3
+
+
+def parity_check(wl, q, k, v, tables, lens, out_step, fp8_kept, nthreads):
+    """The last step's output (the timed path, q's dtype) on four sequences against the oracle,
+    within 2e-3 + half an ulp of the output type; and, if the 8-bit leg ran, its fp32 output on
+    the same sequences against the same 16-bit oracle within 2e-3 + the bound derived from the
+    quantiser's half-step error (oracle/fp8_bound.py)."""
+    B = wl.num_seqs
+    seqs = sorted({0, 1, B // 2, B - 1})
+    ref, lse = oracle_on(wl, q, k, v, tables, lens, seqs, nthreads)
+    got = out_step[seqs].float().numpy().astype(np.float64)
+    half_ulp = 2.0 ** -8 if wl.dtype == "bf16" else 2.0 ** -11
+    err = np.abs(got - ref)
+    res = {
+        "parity_sequences": seqs,
+        "parity_max_abs_err": float(err.max()),
+        "parity_tol": f"{PARITY_TOL} + |oracle| * {half_ulp} (the output's rounding to {wl.dtype})",
+        "parity_ok": bool(np.all(np.isfinite(got)) and np.all(err <= PARITY_TOL + np.abs(ref) * half_ulp)),
+        "fp8_vs_16bit_oracle": None,
+    }
+    if fp8_kept is not None:
+        from oracle import fp8_bound as FB
+        bound = FB.decode_bound(q[seqs].double().cpu().numpy(), k, v, fp8_kept["k_scale"], fp8_kept["v_scale"],
+                                tables[seqs], lens[seqs], wl.scale, wl.num_kv_heads, ref, lse)
+        e8 = np.abs(fp8_kept["out"][seqs].numpy().astype(np.float64) - ref)
+        tol8 = PARITY_TOL + bound
+        res["fp8_vs_16bit_oracle"] = {
+            "sequences": seqs,
+            "max_abs_err": round(float(e8.max()), 5),
+            "bound": "2e-3 + 7 S_d + Q_d per element (oracle/fp8_bound.py)",
+            "bound_median": round(float(np.median(tol8)), 5),
+            "bound_max": round(float(tol8.max()), 5),
+            "largest_share_of_bound": round(float(np.max(e8 / tol8)), 4),
+            "within_bound": bool(np.all(e8 <= tol8)),
+        }
+    return res
+
+
+def cpu_baseline(wl, q, k, v, tables, lens, budget_s, nthreads=None):
+    """The oracle on the workload's sequences (the state after the timed steps: host tables and
+    lengths) in order, cycling, until the budget is spent, on nthreads OpenMP threads (default:
+    all the host lets it use)."""
+    import oracle
     if nthreads is None:
         nthreads = oracle.max_threads()
     done_seqs, done_bytes, elapsed = 0, 0, 0.0
@@ -303,29 +385,17 @@ def cpu_baseline(wl, q, k, v, budget_s, nthreads=None):
     while elapsed < budget_s:
         seqs = [(i + j) % wl.num_seqs for j in range(batch)]
         i += batch
-        rows = wl.block_tables[seqs]
-        ctx = wl.context_lens[seqs]
-        used = sorted({int(b) for j, s in enumerate(seqs) for b in rows[j, :-(-int(ctx[j]) // wl.block_size)]})
-        remap = {b: n for n, b in enumerate(used)}
-        tab = np.full_like(rows, -1)
-        for j in range(len(seqs)):
-            nb = -(-int(ctx[j]) // wl.block_size)
-            tab[j, :nb] = [remap[int(b)] for b in rows[j, :nb]]
-        idx = torch.tensor(used, device=k.device)
-        kb, vb = W.bits16(k.index_select(0, idx)), W.bits16(v.index_select(0, idx))
-        qb = W.bits16(q[seqs])
         t0 = time.perf_counter()
-        oracle.paged_decode(qb, kb, vb, tab, ctx, wl.scale, num_kv_heads=wl.num_kv_heads,
-                            block_size=wl.block_size, dtype=oracle.BF16 if wl.dtype == "bf16" else oracle.F16,
-                            nthreads=nthreads)
+        oracle_on(wl, q, k, v, tables, lens, seqs, nthreads)
         elapsed += time.perf_counter() - t0
         done_seqs += len(seqs)
-        done_bytes += int(ctx.astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+        done_bytes += int(lens[seqs].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "tokens_per_s": round(done_seqs / elapsed, 2),
         "cores": nthreads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{done_seqs} sequence decodes cycling over the workload's {wl.num_seqs} sequences "
                   f"({done_seqs / wl.num_seqs:.2f} passes, {done_bytes / 1e9:.3f} GB of K/V), "
@@ -415,6 +485,10 @@ def main():
     for i in range(N_BREAKDOWN):
         step(e4=ev4[i])
     torch.cuda.synchronize()
+    # The state the last step decoded, and that step's output (checked against the oracle in
+    # the CPU-baseline leg).
+    tables_last, lens_last = tables.cpu().numpy(), lens.cpu().numpy()
+    out_last = out.cpu()
     # Cross-check of the per-launch event timing: back-to-back split-kernel launches
     # on unchanged inputs between two events, divided by their number.
     N_B2B = 20
@@ -445,9 +519,6 @@ def main():
     achieved = uniq_bytes / (part_ms * 1e-3) / 1e9
     achieved_logical = kv_bytes / (part_ms * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_step * 1e-3) / 1e9
-
-    # Parity spot check of the last step's output against the oracle on two sequences.
-    torch.cuda.synchronize()
 
     res = {
         "metric": "paged-attn decode effective KV GB/s (% of 8 TB/s HBM peak) + tokens/s",
@@ -486,12 +557,13 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.config, K, Wu),
+            "traffic": measured_traffic(args.config, uniq_bytes),
             "traffic_unit": "bytes per launch",
             "algorithmic_bytes_per_launch": int(uniq_bytes),
             "achieved_logical_bytes": round(achieved_logical, 2),
         },
         "cpu_baseline": None,
+        "parity_max_abs_err": None,
     }
     if args.calibrate_copy:
         n = (1 << 30) // 4
@@ -504,25 +576,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] calibration copy: 3 x (read 1 GiB + write 1 GiB)")
+    fp8_kept = None
     if not args.no_fp8 and wl.dtype != "bf16":
         log("[bench] 8-bit K/V leg skipped: the E4M3 decode takes a bf16 query, this workload is " + wl.dtype)
     elif not args.no_fp8:
         log("[bench] 8-bit K/V: quantise the pool, time the 8-bit decode")
-        res["fp8_kv"] = fp8_leg(wl, q, k, v, tables, lens, max_ctx, K, Wu, dev)
+        fp8_kept, res["fp8_kv"] = fp8_leg(wl, q, k, v, tables, lens, max_ctx, K, Wu, dev)
         res["fp8_kv"]["speedup_vs_16bit_split"] = round(part_ms / res["fp8_kv"]["split_ms"], 3)
     if not args.no_prefill:
         log("[bench] chunked prefill leg")
         res["prefill"] = prefill_leg(20, 3, dev)
+    parity_ok = True
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] the last step's output against the oracle on four sequences")
+        par = parity_check(wl, q, k, v, tables_last, lens_last, out_last, fp8_kept, oracle.max_threads())
+        parity_ok = par["parity_ok"] and (par["fp8_vs_16bit_oracle"] is None
+                                          or par["fp8_vs_16bit_oracle"]["within_bound"])
+        res["parity_max_abs_err"] = round(par.pop("parity_max_abs_err"), 6)
+        if par["fp8_vs_16bit_oracle"] is not None and "fp8_kv" in res:
+            res["fp8_kv"]["vs_16bit_oracle"] = par.pop("fp8_vs_16bit_oracle")
+        else:
+            par.pop("fp8_vs_16bit_oracle")
+        res.update(par)
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, tables_last, lens_last, args.cpu_seconds)
+        one = cpu_baseline(wl, q, k, v, tables_last, lens_last, max(1.0, args.cpu_seconds / 5), nthreads=1)
+        res["cpu_baseline"]["single_core"] = {key: one[key] for key in ("value", "unit", "tokens_per_s", "sample")}
+    # Last: the host-tier round trip moves blocks, after which the pool no longer holds the
+    # state the timed steps decoded.
     if not args.no_tier:
         log("[bench] host tier: offload past the GPU window, restore, decode check")
         res["host_tier"] = host_tier_leg(pool, wl, q, k, v, tables, lens, max_ctx, args.gpu_window, dev)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)
-        one = cpu_baseline(wl, q, k, v, max(1.0, args.cpu_seconds / 5), nthreads=1)
-        res["cpu_baseline"]["single_core"] = {key: one[key] for key in ("value", "unit", "tokens_per_s", "sample")}
     pool.close()
     print(json.dumps(res), flush=True)
+    if not parity_ok:
+        log("[bench] PARITY FAILED: the timed output differs from the oracle beyond the tolerance")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -51,3 +51,24 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_carried_over_only_for_same_sources_and_workload(tmp_path, monkeypatch):
+    """roofline.traffic: the committed counters' traffic per algorithmic byte, applied to this
+    run's algorithmic bytes, only while the kernel sources hash to the recorded value and the
+    summary was taken on the same workload (any step counts)."""
+    import bench
+    f = tmp_path / "summary.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(f))
+    body = ("# comment: with a colon\n"
+            "workload_args: --config 3 --steps 50 --warmup 10\n"
+            f"kernel_sources_sha256: {bench.kernel_sources_sha256()}\n"
+            "traffic_bytes_per_launch: 1010\n"
+            "algorithmic_bytes_per_launch: 1000\n")
+    f.write_text(body)
+    assert bench.measured_traffic(3, 2_000_000) == 2_020_000
+    assert bench.measured_traffic(5, 2_000_000) is None
+    f.write_text(body.replace(bench.kernel_sources_sha256(), "0" * 64))
+    assert bench.measured_traffic(3, 2_000_000) is None
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.txt"))
+    assert bench.measured_traffic(3, 2_000_000) is None

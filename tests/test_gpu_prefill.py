@@ -102,6 +102,30 @@ def test_prefill_benchmark_shape_sampled():
     note(f"  {len(rows)} sampled rows, max abs err {err:.3g}")
 
 
+def test_prefill_benchmark_shape_whole_sequences():
+    """The benchmark's batch at full size; every row (all 512 chunk rows, all 32 q heads) of four
+    whole sequences against the oracle: the shortest and the longest cached prefix and two
+    others."""
+    wl, cu = W.llama3_8b_prefill()
+    _, k, v = W.make_values(wl, DEV, poison=True)
+    q = W.make_prefill_q(wl, cu, DEV)
+    out, lse = run_gpu(wl, cu, q, k, v)
+    m = np.diff(cu)
+    prefix = wl.context_lens - m
+    rng = np.random.default_rng(17)
+    rest = [s for s in range(wl.num_seqs) if s not in (int(prefix.argmin()), int(prefix.argmax()))]
+    seqs = sorted({int(prefix.argmin()), int(prefix.argmax())} | set(rng.choice(rest, 2, replace=False).tolist()))
+    note(f"prefill {wl.name}: whole sequences {seqs}, prefixes {prefix[seqs].tolist()}")
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    sub_cu = np.concatenate([[0], np.cumsum(m[seqs])]).astype(np.int32)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ro, rl = oracle.paged_prefill(W.bits16(q[ridx]), W.bits16(k), W.bits16(v), wl.block_tables[seqs],
+                                  wl.context_lens[seqs], sub_cu, wl.scale, num_kv_heads=wl.num_kv_heads,
+                                  block_size=wl.block_size, dtype=oracle.BF16)
+    err = check(out[ridx], lse[ridx], ro, rl, "whole sequences")
+    note(f"  {len(rows)} rows x {wl.num_q_heads} heads, max abs err {err:.3g}")
+
+
 def test_prefill_maximum_batch():
     """4096 sequences, the most one call takes: the in-LDS prefix of query tiles over
     sequences runs 16 rounds of 256; short chunks and prefixes, empty chunks included."""
