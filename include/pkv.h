@@ -312,12 +312,19 @@ int32_t paged_attn_partition_size(const pkv_attn_desc* desc);
  * query on the current device), or a negative status. */
 int32_t paged_attn_grid_waves(const pkv_attn_desc* desc);
 
-/* Bytes of device workspace paged_attn_decode needs.  Layout, each part
- * 256-byte aligned, with S = segment slots (fixed: ceil(max_context_len / P);
- * balanced: ceil(ceil(max_context_len / 16) / 8) + 1):
+/* Bytes of device workspace paged_attn_decode needs (0 on a bad descriptor).
+ * With num_waves = 0 the size depends on the current device (the grid is
+ * sized by an occupancy query).  Layout, each part 256-byte aligned, with
+ * GC = (num_q_heads / num_kv_heads) * HW q heads per row (HW = 2 for an
+ * 8-bit cache with an even kv head count, else 1), pairs = num_seqs *
+ * num_kv_heads / HW, and rows = pairs + (fixed: pairs * ceil(max_context_len
+ * / P); balanced: the grid's waves):
  *   int32 hdr[3 + num_seqs]   (tiles, chunk size, tile prefix [num_seqs + 1])
- *   float seg_out[num_seqs][num_q_heads][S][head_dim]   (normalised outputs)
- *   float seg_lse[num_seqs][num_q_heads][S]             (log2-domain lse) */
+ *   float seg_out[rows][GC][head_dim]   (normalised segment outputs)
+ *   float seg_lse[rows][GC]             (log2-domain lse)
+ * Segment k of pair p (sequence s, kv heads p % (num_kv_heads / HW) * HW ..)
+ * sits in row (its chunk index) + p, the chunk index being the one
+ * paged_attn_plan's slot k counts from. */
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* desc);
 
 /* The whole decode: the split pass, then (if a (sequence, kv head) may span

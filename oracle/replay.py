@@ -363,3 +363,34 @@ def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, nu
                 j1 = min((ch + 1) * C - first, nt[s])
                 items.append((s, g, ch - c0, j0 * TILE, min(j1 * TILE, n)))
     return items
+
+
+def segment_rows(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, num_waves: int = 1,
+                 heads_per_wave: int = 1):
+    """Workspace row of every segment of the split, {(seq, kv_head, slot): row}: segment slot k of
+    the pair p = (sequence s, head group g // heads_per_wave), p = s * (num_kv_heads //
+    heads_per_wave) + g // heads_per_wave, is chunk first // C + k of the flattened tile list and
+    sits in row (that chunk) + p.  The kv heads of one group share their rows."""
+    lens = [max(0, int(n)) for n in context_lens]
+    nt = [ceil_div(n, TILE) for n in lens]
+    hg = num_kv_heads // heads_per_wave
+    if partition_size > 0:
+        C = partition_size // TILE
+        pt = [ceil_div(x, C) * C for x in nt]
+    else:
+        pt = list(nt)
+    total = hg * sum(pt)
+    if partition_size == 0:
+        C = max(MIN_CHUNK, ceil_div(total, num_waves))
+    rows = {}
+    acc = 0
+    for s in range(len(lens)):
+        for g in range(num_kv_heads):
+            if nt[s] == 0:
+                continue
+            first = acc + (g // heads_per_wave) * pt[s]
+            c0, c1 = first // C, (first + nt[s] - 1) // C
+            for k in range(c1 - c0 + 1):
+                rows[(s, g, k)] = c0 + k + s * hg + g // heads_per_wave
+        acc += hg * pt[s]
+    return rows

@@ -348,7 +348,8 @@ paged_decode_split_kernel(DecodeArgs a) {
     // d = EPL (4 (l/16) + i) + e of head l%16.
     floatx4 acc[EPL];
     float m_lane = 0.f, l_lane = 0.f;
-    int seg_s = 0, seg_g = 0, seg_ctx = 0, seg_nt = 0, seg_slot = 0;
+    int seg_s = 0, seg_g = 0, seg_ctx = 0, seg_nt = 0;
+    int64_t seg_row = 0;                  // workspace row of the segment: chunk index + pair index
     bool seg_direct = false;
 
     auto tile_base = [&](int j, int g, int32_t blk) -> int64_t {
@@ -567,14 +568,14 @@ paged_decode_split_kernel(DecodeArgs a) {
                 }
                 if (kq == 0 && a.lse) a.lse[sh] = lse2 * kLn2;
             } else {
-                float* o = a.ws_out + (sh * a.max_seg + seg_slot) * D + d0;
+                float* o = a.ws_out + (seg_row * GC + mrow) * D + d0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int e = 0; e < EPL; e += 4)
                         *reinterpret_cast<float4*>(o + EPL * i + e) =
                             make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv);
-                if (kq == 0) a.ws_lse[sh * a.max_seg + seg_slot] = lse2;
+                if (kq == 0) a.ws_lse[seg_row * GC + mrow] = lse2;
             }
         }
     };
@@ -691,7 +692,10 @@ paged_decode_split_kernel(DecodeArgs a) {
                     seg_ctx = s_len[sv];
                     seg_nt = len_tiles(seg_ctx);
                     const int first = s_pre[sv] + g * padded_tiles(seg_nt, a.fixed_chunk);
-                    seg_slot = ch - first / C;
+                    // Segment k of pair p (sequence sv, head group g) is chunk first / C + k:
+                    // rows chunk + p are distinct over all segments (a pair's chunks come after
+                    // those of the pairs before it) and fewer than chunks + pairs.
+                    seg_row = (int64_t)ch + (int64_t)sv * HG + g;
                     seg_direct = (first + seg_nt - 1) / C == first / C;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -713,15 +717,14 @@ paged_decode_split_kernel(DecodeArgs a) {
 // one chunk -- one wave (four pairs per workgroup) or a whole workgroup.  With
 // M = max_k lse_k and w_k = 2^(lse_k - M): out = sum_k w_k o_k / sum_k w_k and
 // lse = M + log2(sum_k w_k) -- the online-softmax identity applied to the
-// segments.  A wave load covers RPL segment rows (lane l reads 4 consecutive d
-// values of row l / (D/4)); the pair's waves take rows in turn and each lane
-// keeps UNROLL rows in flight, so a pair's first WPP RPL UNROLL rows arrive in
-// one round trip.  Every wave computes M itself from the lse values; rows with
-// the same d slice are summed by lane swaps, waves by LDS.  The kernel is a
-// chain of dependent loads (length, header, lse, rows), so each lane's first
-// UNROLL rows and lse values are loaded together with the length and header:
-// every pair owns max_seg slots, so these reads stay inside its own workspace
-// rows whatever its segment count, and rows past the count are never used.
+// segments.  Segment k of the pair p (sequence s, head group g / HW) sits in
+// workspace row first / C + k + p, column hq - (g / HW) GC of its GC q heads.
+// A wave load covers RPL segment rows (lane l reads 4 consecutive d values of
+// row l / (D/4)); the pair's waves take rows in turn and each lane keeps
+// UNROLL rows in flight, so a pair's first WPP RPL UNROLL rows arrive in one
+// round trip once the length and the header (chunk size, tile prefix) have
+// given the first row.  Every wave computes M itself from the lse values;
+// rows with the same d slice are summed by lane swaps, waves by LDS.
 template <int D, int WPP>
 __global__ void __launch_bounds__(kThreads)
 paged_decode_merge_kernel(MergeArgs a) {
@@ -738,35 +741,38 @@ paged_decode_merge_kernel(MergeArgs a) {
     const int s = (int)(sh / a.num_q_heads);
     const int hq = (int)(sh % a.num_q_heads);
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int g = hq / G;
-    const float* lse_p = a.ws_lse + sh * a.max_seg;
+    const int HW = a.heads_per_wave;
+    const int GC = HW * G;                     // q heads per workspace row
+    const int gp = hq / GC;                    // head group of the list
     const int d4 = (lane % LPR) * 4;
     const int r0 = wp * RPL + lane / LPR;      // this lane's first row
-    const float* out_p = a.ws_out + sh * a.max_seg * D + d4;
 
     const int len = a.context_lens[s];
     const int C = a.ws_hdr[1];
     const int pre = a.ws_hdr[2 + s];
-    const float lse_lane = lane < a.max_seg ? lse_p[lane] : -INFINITY;
+    const int n = min(max(len, 0), a.max_context_len);
+    const int nt = (n + kTile - 1) / kTile;
+    const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
+    const int first = pre + gp * pt;
+    // Empty pairs are written by the split kernel, one-segment pairs directly.
+    const int nseg = nt == 0 ? 0 : (first + nt - 1) / C - first / C + 1;
+    if (nseg <= 1) return;                     // uniform over a pair's waves
+    const int64_t row0 = (int64_t)(first / C) + (int64_t)s * (a.num_kv_heads / HW) + gp;
+    const int hcol = hq - gp * GC;
+    const float* lse_p = a.ws_lse + row0 * GC + hcol;             // row k at lse_p[k GC]
+    const float* out_p = a.ws_out + (row0 * GC + hcol) * D + d4;  // row k at out_p[k GC D]
+    const int64_t rs = (int64_t)GC * D;
+
     float4 v0[UNROLL];
     float l0[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int k = r0 + u * STEP;
-        v0[u] = k < a.max_seg ? *reinterpret_cast<const float4*>(out_p + (int64_t)k * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-        l0[u] = k < a.max_seg ? lse_p[k] : -INFINITY;
+        v0[u] = k < nseg ? *reinterpret_cast<const float4*>(out_p + k * rs) : make_float4(0.f, 0.f, 0.f, 0.f);
+        l0[u] = k < nseg ? lse_p[(int64_t)k * GC] : -INFINITY;
     }
-
-    const int n = min(max(len, 0), a.max_context_len);
-    const int nt = (n + kTile - 1) / kTile;
-    const int pt = a.fixed_chunk > 0 ? (nt + a.fixed_chunk - 1) / a.fixed_chunk * a.fixed_chunk : nt;
-    const int first = pre + (g / a.heads_per_wave) * pt;
-    // Empty pairs are written by the split kernel, one-segment pairs directly.
-    const int nseg = nt == 0 ? 0 : (first + nt - 1) / C - first / C + 1;
-    if (nseg <= 1) return;                     // uniform over a pair's waves
-
-    float M = lane < nseg ? lse_lane : -INFINITY;
-    for (int k = lane + 64; k < nseg; k += 64) M = fmaxf(M, lse_p[k]);
+    float M = -INFINITY;
+    for (int k = lane; k < nseg; k += 64) M = fmaxf(M, lse_p[(int64_t)k * GC]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -788,8 +794,8 @@ paged_decode_merge_kernel(MergeArgs a) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int k = kb + u * STEP;
-            v[u] = k < nseg ? *reinterpret_cast<const float4*>(out_p + (int64_t)k * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-            l[u] = k < nseg ? lse_p[k] : -INFINITY;
+            v[u] = k < nseg ? *reinterpret_cast<const float4*>(out_p + k * rs) : make_float4(0.f, 0.f, 0.f, 0.f);
+            l[u] = k < nseg ? lse_p[(int64_t)k * GC] : -INFINITY;
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {

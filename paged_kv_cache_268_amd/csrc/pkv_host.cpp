@@ -904,7 +904,8 @@ constexpr int32_t kMinChunk = 8;            // must equal the kernel's balanced-
 struct Plan {
     int32_t part_size = 0;                  // 0 = balanced split
     int32_t fixed_chunk = 0;                // part_size / 16
-    int32_t max_seg = 0;
+    int32_t max_seg = 0;                    // upper bound of segments per (sequence, kv head)
+    int32_t seg_rows = 0;                   // workspace rows (after size_workspace)
     int32_t num_waves = 0;                  // resolved grid size (0 until resolved)
     int32_t group_pad = 0;
     int32_t heads_per_wave = 1;             // kv heads one wave takes per tile (2: 8-bit K/V, even Hkv)
@@ -968,10 +969,23 @@ int resolve(const pkv_attn_desc* d, Plan* pl) {
     pl->kind = d->kv_dtype == PKV_FP8_E4M3 ? (pair ? pkv::KvKind::FP8_BF16Q_PAIR : pkv::KvKind::FP8_BF16Q)
              : d->kv_dtype == PKV_BF16    ? pkv::KvKind::BF16
                                           : pkv::KvKind::F16;
-    const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl->max_seg;
+    return PKV_OK;
+}
+
+// Workspace layout for a resolved split (num_waves known): a segment k of
+// the pair p = (sequence, head group) is written to row (its chunk index) + p.
+// Balanced mode has at most num_waves chunks (C >= ceil(T / num_waves)),
+// fixed mode at most max_seg per pair; so rows = that bound + pairs.
+int size_workspace(const pkv_attn_desc* d, Plan* pl) {
+    const int64_t pairs = (int64_t)d->num_seqs * (d->num_kv_heads / pl->heads_per_wave);
+    const int64_t chunks = pl->fixed_chunk > 0 ? pairs * pl->max_seg : (int64_t)pl->num_waves;
+    const int64_t rows = std::max<int64_t>(chunks + pairs, 1);
+    if (rows >= ((int64_t)1 << 31)) return fail(PKV_EUNSUPPORTED, "workspace rows %lld exceed int32", (long long)rows);
+    const int64_t cols = (int64_t)(d->num_q_heads / d->num_kv_heads) * pl->heads_per_wave;   // q heads per row
+    pl->seg_rows = (int32_t)rows;
     pl->hdr_bytes = up256(sizeof(int32_t) * (3 + (size_t)d->num_seqs));
-    pl->out_bytes = up256(rows * d->head_dim * sizeof(float));
-    pl->ws_bytes = pl->hdr_bytes + pl->out_bytes + up256(rows * sizeof(float));
+    pl->out_bytes = up256((size_t)rows * cols * d->head_dim * sizeof(float));
+    pl->ws_bytes = pl->hdr_bytes + pl->out_bytes + up256((size_t)rows * cols * sizeof(float));
     return PKV_OK;
 }
 
@@ -1093,6 +1107,9 @@ int32_t paged_attn_grid_waves(const pkv_attn_desc* d) {
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
     Plan pl;
     if (resolve(d, &pl)) return 0;
+    // Only the balanced split's size depends on the grid.
+    if (pl.fixed_chunk == 0 && resolve_waves(d, &pl)) return 0;
+    if (size_workspace(d, &pl)) return 0;
     return pl.ws_bytes;
 }
 
@@ -1110,9 +1127,11 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     if (kv8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
         return fail(PKV_EINVAL, "8-bit K/V: null or misaligned k_scale / v_scale");
     if (d->num_seqs == 0) return PKV_OK;
-    rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes, true);
-    if (rc) return rc;
     rc = resolve_waves(d, &pl);
+    if (rc) return rc;
+    rc = size_workspace(d, &pl);
+    if (rc) return rc;
+    rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes, true);
     if (rc) return rc;
     char* ws = reinterpret_cast<char*>(workspace);
     pkv::DecodeArgs a{};
@@ -1135,7 +1154,7 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     a.table_stride = d->table_stride;
     a.fixed_chunk = pl.fixed_chunk;
     a.num_waves = pl.num_waves;
-    a.max_seg = pl.max_seg;
+    a.seg_rows = pl.seg_rows;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
     a.heads_per_wave = pl.heads_per_wave;
@@ -1166,6 +1185,10 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     if (rc) return rc;
     if (d->num_seqs == 0 || pl.max_seg <= 1) return PKV_OK;
     if (!context_lens || !aligned(context_lens, 4)) return fail(PKV_EINVAL, "null context_lens");
+    rc = resolve_waves(d, &pl);
+    if (rc) return rc;
+    rc = size_workspace(d, &pl);
+    if (rc) return rc;
     rc = check_ptrs(pl, nullptr, nullptr, nullptr, nullptr, nullptr, out, lse, workspace, workspace_bytes, false);
     if (rc) return rc;
     const char* ws = reinterpret_cast<const char*>(workspace);
@@ -1181,6 +1204,7 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     a.num_kv_heads = d->num_kv_heads;
     a.fixed_chunk = pl.fixed_chunk;
     a.max_seg = pl.max_seg;
+    a.seg_rows = pl.seg_rows;
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
     a.heads_per_wave = pl.heads_per_wave;

@@ -29,8 +29,8 @@ struct DecodeArgs {
     void* out;
     float* lse;              // natural log, nullable
     int32_t* ws_hdr;         // [2 + B + 1]: T, C, prefix of padded tiles (x Hkv) over sequences
-    float* ws_out;           // [B][Hq][max_seg][D] normalised segment outputs
-    float* ws_lse;           // [B][Hq][max_seg], log2 domain
+    float* ws_out;           // [rows][GC][D] normalised segment outputs, GC = q heads of a wave's kv heads
+    float* ws_lse;           // [rows][GC], log2 domain; segment k of pair p = (s, head group) in row c + p
     float scale;
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -38,7 +38,7 @@ struct DecodeArgs {
     int32_t table_stride;
     int32_t fixed_chunk;     // tiles per chunk (partition_size / 16); 0 = balanced split
     int32_t num_waves;       // waves in the grid (multiple of 4)
-    int32_t max_seg;         // segment slots per (sequence, q head) in the workspace
+    int32_t seg_rows;        // rows of ws_out / ws_lse
     int32_t max_context_len;
     int32_t out_dtype;       // kOut*
     int32_t heads_per_wave;  // kv heads a wave takes per tile: 1, or 2 for FP8_BF16Q_PAIR
@@ -55,7 +55,8 @@ struct MergeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t fixed_chunk;
-    int32_t max_seg;
+    int32_t max_seg;         // upper bound of segments per (sequence, kv head) (launch shape only)
+    int32_t seg_rows;        // rows of ws_out / ws_lse
     int32_t max_context_len;
     int32_t out_dtype;
     int32_t heads_per_wave;  // as the split kernel's: a kv head g sits in list group g / heads_per_wave

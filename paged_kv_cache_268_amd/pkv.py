@@ -187,17 +187,22 @@ def workspace_bytes(desc: AttnDesc) -> int:
 
 
 def workspace_views(desc: AttnDesc, ws):
-    """(hdr int32, seg_out float [B][Hq][S][D], seg_lse float [B][Hq][S]) views of a uint8 workspace tensor,
-    following the layout include/pkv.h documents for paged_attn_workspace_bytes."""
+    """(hdr int32, seg_out float [rows][GC][D], seg_lse float [rows][GC]) views of a uint8 workspace
+    tensor, following the layout include/pkv.h documents for paged_attn_workspace_bytes."""
     import torch
-    B, Hq, D = desc.num_seqs, desc.num_q_heads, desc.head_dim
+    B, Hq, Hkv, D = desc.num_seqs, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
     P, mc = desc.partition_size, desc.max_context_len
-    S = max(1, -(-mc // P)) if P > 0 else -(-(-(-mc // 16)) // 8) + 1
+    hw = 2 if desc.kv_dtype == PKV_FP8_E4M3 and Hkv % 2 == 0 else 1
+    GC = Hq // Hkv * hw
+    pairs = B * (Hkv // hw)
+    chunks = pairs * max(1, -(-mc // P)) if P > 0 else grid_waves(desc)
+    rows = max(chunks + pairs, 1)
     up = lambda x: (x + 255) // 256 * 256
-    hb, ob = up(4 * (3 + B)), up(B * Hq * S * D * 4)
+    hb, ob = up(4 * (3 + B)), up(rows * GC * D * 4)
+    assert hb + ob + up(rows * GC * 4) == workspace_bytes(desc)
     hdr = ws[:4 * (3 + B)].view(torch.int32)
-    seg_out = ws[hb:hb + B * Hq * S * D * 4].view(torch.float32).view(B, Hq, S, D)
-    seg_lse = ws[hb + ob:hb + ob + B * Hq * S * 4].view(torch.float32).view(B, Hq, S)
+    seg_out = ws[hb:hb + rows * GC * D * 4].view(torch.float32).view(rows, GC, D)
+    seg_lse = ws[hb + ob:hb + ob + rows * GC * 4].view(torch.float32).view(rows, GC)
     return hdr, seg_out, seg_lse
 
 

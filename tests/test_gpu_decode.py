@@ -227,7 +227,8 @@ def test_many_pairs_long_segment_lists_merge():
 
 @pytest.mark.parametrize("P,nw", [(256, 0), (0, 8), (0, 16), (512, 4)])
 def test_segments_are_the_plan(P, nw):
-    """Each segment's output in the workspace equals the oracle on its token range."""
+    """Each segment's output in the workspace (the row of its chunk and pair) equals the oracle on
+    its token range, and nothing else is written."""
     wl = small(seed=7, ctx=(5, 700, 1024, 1500, 0, 33), B=6)
     note(f"workspace segments vs oracle sub-ranges, P={P} nw={nw}")
     q, k, v = W.make_values(wl, DEV, poison=True)
@@ -246,6 +247,7 @@ def test_segments_are_the_plan(P, nw):
     want = np.array(R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc)), dtype=np.int32)
     assert np.array_equal(items, want.reshape(-1, 5))
     G = wl.num_q_heads // wl.num_kv_heads
+    rows = R.segment_rows(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc))
     nseg = {}
     for s_, g, kslot, lo, hi in items.tolist():
         nseg[(s_, g)] = nseg.get((s_, g), 0) + 1
@@ -253,6 +255,7 @@ def test_segments_are_the_plan(P, nw):
     used = np.zeros(seg_lse.shape, dtype=bool)
     for s_, g, kslot, lo, hi in items.tolist():
         heads = slice(g * G, (g + 1) * G)
+        row = rows[(s_, g, kslot)]
         if nseg[(s_, g)] == 1:                                 # written straight to out
             compare(out[s_, heads][None], lse[s_, heads][None], ref_full[s_, heads][None],
                     ref_full_lse[s_, heads][None], what="direct")
@@ -260,9 +263,9 @@ def test_segments_are_the_plan(P, nw):
         los = np.zeros(wl.num_seqs, np.int32); his = np.zeros(wl.num_seqs, np.int32)
         los[s_], his[s_] = lo, hi
         ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v, tok_lo=los, tok_hi=his)
-        assert np.abs(seg_out[s_, heads, kslot] - ref_out[s_, heads]).max() <= TOL
-        assert np.abs(seg_lse[s_, heads, kslot] / math.log2(math.e) - ref_lse[s_, heads]).max() <= TOL
-        used[s_, heads, kslot] = True
+        assert np.abs(seg_out[row] - ref_out[s_, heads]).max() <= TOL
+        assert np.abs(seg_lse[row] / math.log2(math.e) - ref_lse[s_, heads]).max() <= TOL
+        used[row] = True
     assert np.all(np.isnan(seg_lse[~used]))                    # nothing else was written
     pkv.merge(desc, ctx, out, lse, ws)
     torch.cuda.synchronize()

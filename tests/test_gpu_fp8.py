@@ -161,8 +161,8 @@ def test_fp8_decode_shapes(Hq, Hkv, D, bs):
 @pytest.mark.parametrize("P,nw", [(0, 8), (0, 16), (256, 4)])
 def test_fp8_pair_segments_are_the_plan(P, nw):
     """With two kv heads per wave, each segment in the workspace equals the oracle on its token
-    range, at the slot the host plan gives for its own kv head (both heads of a pair share a
-    tile list entry and so a slot), and nothing else is written."""
+    range, in the workspace row of its slot (both heads of a pair share a tile list entry, a
+    slot and a row, each in its own columns), and nothing else is written."""
     lens = [5, 700, 1024, 1500, 0, 33]
     wl = W.make_workload(len(lens), 32, 8, 128, 16, "bf16", lens, seed=93, pool_factor=1.5)
     note(f"8-bit pair workspace segments vs oracle sub-ranges, P={P} nw={nw}")
@@ -184,6 +184,7 @@ def test_fp8_pair_segments_are_the_plan(P, nw):
     want = R.plan(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc), heads_per_wave=2)
     assert np.array_equal(items, np.array(want, dtype=np.int32).reshape(-1, 5))
     G = wl.num_q_heads // wl.num_kv_heads
+    rows = R.segment_rows(wl.context_lens.tolist(), wl.num_kv_heads, P, pkv.grid_waves(desc), heads_per_wave=2)
     nseg = {}
     for s_, g, _, _, _ in items.tolist():
         nseg[(s_, g)] = nseg.get((s_, g), 0) + 1
@@ -191,6 +192,7 @@ def test_fp8_pair_segments_are_the_plan(P, nw):
     used = np.zeros(seg_lse.shape, dtype=bool)
     for s_, g, kslot, lo, hi in items.tolist():
         heads = slice(g * G, (g + 1) * G)
+        row, cols = rows[(s_, g, kslot)], slice((g % 2) * G, (g % 2 + 1) * G)   # a row holds both heads' q heads
         if nseg[(s_, g)] == 1:                                 # written straight to out
             compare(out[s_, heads][None], lse[s_, heads][None], ro[s_, heads][None], rl[s_, heads][None],
                     "direct")
@@ -202,9 +204,9 @@ def test_fp8_pair_segments_are_the_plan(P, nw):
                                      num_kv_heads=wl.num_kv_heads, block_size=wl.block_size, dtype=oracle.BF16,
                                      kv_dtype=oracle.FP8, k_scale=ks.cpu().numpy(), v_scale=vs.cpu().numpy(),
                                      tok_lo=los, tok_hi=his)
-        assert np.abs(seg_out[s_, heads, kslot] - so[s_, heads]).max() <= TOL
-        assert np.abs(seg_lse[s_, heads, kslot] / np.log2(np.e) - sl[s_, heads]).max() <= TOL
-        used[s_, heads, kslot] = True
+        assert np.abs(seg_out[row, cols] - so[s_, heads]).max() <= TOL
+        assert np.abs(seg_lse[row, cols] / np.log2(np.e) - sl[s_, heads]).max() <= TOL
+        used[row, cols] = True
     assert np.all(np.isnan(seg_lse[~used]))                    # nothing else was written
     pkv.merge(desc, ctx, out, lse, ws)
     torch.cuda.synchronize()

@@ -213,11 +213,17 @@ def test_split_sizes_and_workspace():
     d = pkv.attn_desc(4, 4, 4, 64, 16, 64, 16, 256, 0, pkv.PKV_F16, num_waves=8)
     assert pkv.partition_size(d) == 0 and pkv.grid_waves(d) == 8
     up = lambda x: (x + 255) // 256 * 256
-    S = -(-(256 // 16) // 8) + 1
-    assert pkv.workspace_bytes(d) == up(4 * 7) + up(4 * 4 * S * 64 * 4) + up(4 * 4 * S * 4)
+    # balanced: rows = waves (at most one chunk each) + pairs; one q head per row (MHA)
+    rows = 8 + 4 * 4
+    assert pkv.workspace_bytes(d) == up(4 * 7) + up(rows * 1 * 64 * 4) + up(rows * 1 * 4)
+    # fixed 512-token partitions: rows = pairs * ceil(8192 / 512) + pairs; the group's 4 q heads per row
     d = pkv.attn_desc(64, 32, 8, 128, 16, 30000, 512, 8192, 512, num_waves=0)
-    S = 8192 // 512
-    assert pkv.workspace_bytes(d) == up(4 * 67) + up(64 * 32 * S * 128 * 4) + up(64 * 32 * S * 4)
+    rows = 64 * 8 * (8192 // 512) + 64 * 8
+    assert pkv.workspace_bytes(d) == up(4 * 67) + up(rows * 4 * 128 * 4) + up(rows * 4 * 4)
+    # 8-bit K/V, even kv heads: a row holds both kv heads' q heads, half the pairs
+    d = pkv.attn_desc(3, 16, 4, 128, 16, 64, 64, 1000, 0, kv_dtype=pkv.PKV_FP8_E4M3, num_waves=64)
+    rows = 64 + 3 * 2
+    assert pkv.workspace_bytes(d) == up(4 * 6) + up(rows * 8 * 128 * 4) + up(rows * 8 * 4)
     # a fixed split never gets more waves than chunks
     d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 512, num_waves=4000)
     assert pkv.grid_waves(d) == 2 * 4 * 2
@@ -435,3 +441,4 @@ def test_append_tokens_errors_leave_the_pool_unchanged():
     assert lib.kv_append_tokens(pool2.handle, 2, ids.ctypes.data, counts0.ctypes.data, None, None, None, None,
                                 None) == pkv.PKV_OK
     pool.close(); pool2.close()
+

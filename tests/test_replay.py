@@ -401,3 +401,41 @@ def test_append_tokens_all_or_nothing():
     items = pool.append_tokens([s, t], [5, 3])
     assert [it[0] for it in items] == [s] * 5 + [t] * 3
     assert pool.seqs[s][1] == 5 and pool.seqs[t][1] == 3
+
+
+def test_segment_rows_worked_examples():
+    """Balanced: lengths 5, 700, 40, two kv heads, 4 waves: 1 + 44 + 3 tiles per kv head, T = 96,
+    C = max(8, 24) = 24.  Pair (1, 1) starts at list position 46 and spans chunks 1, 2, 3; its
+    pair index is 3, so its rows are 4, 5, 6.  Fixed P = 128 (C = 8 tiles): lengths 300, 40 pad to
+    24 and 8 tiles; pair (0, 1) starts at 24 (chunks 3, 4, 5, pair 1: rows 4, 5, 6), pair (1, 1) at
+    56 (chunk 7, pair 3: row 10)."""
+    assert R.segment_rows([5, 700, 40], 2, 0, 4) == {
+        (0, 0, 0): 0, (0, 1, 0): 1, (1, 0, 0): 2, (1, 0, 1): 3, (1, 1, 0): 4, (1, 1, 1): 5, (1, 1, 2): 6,
+        (2, 0, 0): 7, (2, 1, 0): 8}
+    assert R.segment_rows([300, 40], 2, 128, 4) == {
+        (0, 0, 0): 0, (0, 0, 1): 1, (0, 0, 2): 2, (0, 1, 0): 4, (0, 1, 1): 5, (0, 1, 2): 6,
+        (1, 0, 0): 8, (1, 1, 0): 10}
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_segment_rows_distinct_and_bounded(seed):
+    """Every segment of the plan has a row; rows of distinct pairs or slots differ, the kv heads of
+    one group share theirs, and all rows are below chunks + pairs (balanced: at most num_waves
+    chunks; fixed: at most ceil(max_len / P) per pair)."""
+    rnd = random.Random(seed)
+    B = rnd.randint(1, 40)
+    lens = [rnd.choice([0, 1, 15, 16, 17, rnd.randint(0, 5000)]) for _ in range(B)]
+    hw = rnd.choice([1, 2])
+    hkv = hw * rnd.randint(1, 4)
+    P = rnd.choice([0, 0, 16, 64, 512])
+    nw = rnd.choice([1, 4, 64, 2048])
+    items = R.plan(lens, hkv, P, nw, heads_per_wave=hw)
+    rows = R.segment_rows(lens, hkv, P, nw, heads_per_wave=hw)
+    assert set(rows) == {(s, g, k) for s, g, k, _, _ in items}
+    pairs = B * (hkv // hw)
+    chunks = nw if P == 0 else pairs * max(1, -(-max(lens) // P)) if max(lens) else pairs
+    by_row = {}
+    for (s, g, k), r in rows.items():
+        assert 0 <= r < chunks + pairs
+        by_row.setdefault(r, set()).add((s, g // hw, k))
+    assert all(len(v) == 1 for v in by_row.values())
