@@ -337,6 +337,23 @@ int paged_attn_decode(const pkv_attn_desc* desc, const void* q, const void* k_ca
                       const int32_t* context_lens, float scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/* paged_attn_decode for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode, with the workspace taken from a static scratch array that the
+ * library holds on every GPU it runs on (32 MiB per GPU, kept until the process
+ * ends) instead of a caller buffer.  Arguments as for paged_attn_decode; the
+ * caller still owns q, the caches, the tables, out and lse.  The call makes no
+ * device allocation.  A descriptor whose workspace (paged_attn_workspace_bytes)
+ * exceeds the scratch is refused with PKV_EWORKSPACE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one scratch, which keeps the
+ * last call's contents: calls that overlap on one GPU (different streams or
+ * threads, unsynchronised) race and give undefined results; order them.  The
+ * scratch's address is looked up on the first call on each device. */
+int paged_attn_decode_noalloc(const pkv_attn_desc* desc, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out, float* lse,
+                              pkv_stream_t stream);
+
 /* The two passes on their own (paged_attn_decode == partials then merge). */
 int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,

@@ -24,6 +24,7 @@
 #include "pkv.h"
 #include "pkv_append.h"
 #include "pkv_fp8.h"
+#include "pkv_noalloc.h"
 #include "pkv_kernels.h"
 #include "pkv_prefill.h"
 #include "pkv_tier.h"
@@ -1220,6 +1221,29 @@ int paged_attn_decode(const pkv_attn_desc* d, const void* q, const void* k_cache
                                         workspace, workspace_bytes, stream);
     if (rc) return rc;
     return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_noalloc(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                              float* lse, pkv_stream_t stream) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (d->num_seqs == 0) return PKV_OK;
+    rc = resolve_waves(d, &pl);
+    if (rc) return rc;
+    rc = size_workspace(d, &pl);
+    if (rc) return rc;
+    if (pl.ws_bytes > pkv::kScratchBytes)
+        return fail(PKV_EWORKSPACE,
+                    "paged_attn_decode_noalloc: this split needs %zu bytes of workspace, the static scratch holds "
+                    "%zu (use paged_attn_decode with a caller workspace)",
+                    pl.ws_bytes, pkv::kScratchBytes);
+    void* ws = nullptr;
+    size_t cap = 0;
+    hipError_t e = pkv::static_scratch(&ws, &cap);
+    if (e != hipSuccess) return fail_hip(e, "paged_attn_decode_noalloc: static scratch address");
+    return paged_attn_decode(d, q, k_cache, v_cache, block_tables, context_lens, scale, out, lse, ws, cap, stream);
 }
 
 int paged_attn_decode_fp8(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,

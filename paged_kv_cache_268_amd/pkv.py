@@ -27,6 +27,7 @@ EXPORTS = (
     "kv_host_tier_stats", "kv_block_pool_set_fp8_scales", "kv_quantize_fp8", "paged_attn_decode_fp8",
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
+    "paged_attn_decode_noalloc",
 )
 
 
@@ -101,6 +102,8 @@ def load(path: str = LIB_PATH):
         "paged_attn_decode_partials": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P],
                                        ctypes.c_int),
         "paged_attn_merge": ([ctypes.POINTER(AttnDesc), P, P, P, P, SZ, P], ctypes.c_int),
+        "paged_attn_decode_noalloc": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, ctypes.c_float, P, P, P],
+                                      ctypes.c_int),
         "paged_attn_prefill": ([ctypes.POINTER(PrefillDesc), P, P, P, P, P, P, ctypes.c_float, P, P, P], ctypes.c_int),
         "paged_attn_plan": ([ctypes.POINTER(AttnDesc), P, P, I64, ctypes.POINTER(I64)], ctypes.c_int),
     }
@@ -230,6 +233,13 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
                                    _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_noalloc(desc, q, k_cache, v_cache, block_tables, context_lens, scale, out, lse=None, stream=None):
+    """paged_attn_decode_noalloc: the decode with the library's static scratch as its workspace."""
+    check(load().paged_attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale),
+                                           _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def decode_partials(desc, q, k_cache, v_cache, block_tables, context_lens, scale, out, lse, workspace,

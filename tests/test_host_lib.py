@@ -442,3 +442,14 @@ def test_append_tokens_errors_leave_the_pool_unchanged():
                                 None) == pkv.PKV_OK
     pool.close(); pool2.close()
 
+
+def test_noalloc_refuses_a_workspace_beyond_the_scratch():
+    """paged_attn_decode_noalloc checks the split's workspace against its 32 MiB static scratch
+    before touching the device: PKV_EWORKSPACE, nothing enqueued."""
+    d = pkv.attn_desc(4096, 32, 8, 128, 16, 1 << 20, 512, 8192, 16, num_waves=2048)
+    assert pkv.workspace_bytes(d) > 32 << 20
+    lib = pkv.load()
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.paged_attn_decode_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, ctypes.c_float(1.0), fake,
+                                       None, None)
+    assert rc == pkv.PKV_EWORKSPACE and "scratch" in pkv.last_error()
