@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-tier", action="store_true", help="skip the host-tier offload/restore measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit K/V decode measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling (pkv_read_probe over 2 GiB)")
     ap.add_argument("--gpu-window", type=int, default=32, help="blocks each sequence keeps on the GPU when offloaded")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) three times, "
@@ -216,6 +218,35 @@ def host_tier_leg(pool, wl, q, k, v, tables, lens, max_ctx, gpu_window, dev):
     }
 
 
+def read_ceiling_leg(dev, gib=2):
+    """What HBM delivers to a plain streaming read on this GPU: pkv_read_probe (every wave
+    reading contiguous 16 KiB pieces with 16-byte loads) over a 2 GiB buffer, plain and
+    non-temporal loads, 512 .. 4096 workgroups of 256 threads, five timed launches each."""
+    import torch
+    from paged_kv_cache_268_amd import pkv
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for nt in (False, True):
+        for wg in (512, 1024, 2048, 4096):
+            for _ in range(2):
+                pkv.read_probe(buf, wg, nt, sink, stream=stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[0].record(stream)
+            for i in range(5):
+                pkv.read_probe(buf, wg, nt, sink, stream=stream)
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            ms = min(ev[i].elapsed_time(ev[i + 1]) for i in range(5))
+            rates[f"{'nontemporal' if nt else 'plain'}_{wg}wg"] = round(buf.numel() / (ms * 1e-3) / 1e9, 1)
+    del buf, sink
+    best = max(rates.values())
+    return {"kernel": "read_probe_kernel", "bytes_per_launch": gib << 30, "GBps": rates,
+            "best_GBps": best, "best_frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+
+
 def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
     """Quantise the pool to E4M3 (per-(block, kv head) scales) and time the 8-bit decode."""
     import torch
@@ -232,17 +263,26 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
     ws = pkv.alloc_workspace(desc, dev)
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     stream = torch.cuda.current_stream()
+    single = pkv.decode_launches(desc) == 1
+
+    def run(e):
+        e[0].record(stream)
+        if single:
+            pkv.decode_fp8(q, kc, vc, ks, vs, tables, lens, wl.scale, max_ctx, out=out, desc=desc, workspace=ws,
+                           stream=stream)
+            e[1].record(stream)
+        else:
+            pkv.decode_partials_fp8(desc, q, kc, vc, ks, vs, tables, lens, wl.scale, out, None, ws, stream=stream)
+            e[1].record(stream)
+            pkv.merge(desc, lens, out, None, ws, stream=stream)
+        e[2].record(stream)
+
     for _ in range(warmup):
-        pkv.decode_partials_fp8(desc, q, kc, vc, ks, vs, tables, lens, wl.scale, out, None, ws, stream=stream)
-        pkv.merge(desc, lens, out, None, ws, stream=stream)
+        run([torch.cuda.Event() for _ in range(3)])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:
-        e[0].record(stream)
-        pkv.decode_partials_fp8(desc, q, kc, vc, ks, vs, tables, lens, wl.scale, out, None, ws, stream=stream)
-        e[1].record(stream)
-        pkv.merge(desc, lens, out, None, ws, stream=stream)
-        e[2].record(stream)
+        run(e)
     torch.cuda.synchronize()
     part = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     whole = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
@@ -259,7 +299,7 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
     return kept, {
         "kernel": "paged_decode_split_kernel (E4M3 K/V)",
         "kv_dtype": "e4m3 + fp32 scale per (block, kv head)",
-        "split_ms": round(part, 4), "split_plus_merge_ms": round(whole, 4),
+        "split_ms": round(part, 4), "split_plus_merge_ms": round(whole, 4), "decode_launches": 1 if single else 2,
         "algorithmic_bytes_per_launch": alg,
         "roofline": {"bound": "hbm", "achieved": round(alg / (part * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -459,15 +499,26 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
+    # The split kernel, then the merge kernel (one launch when a single partition covers every
+    # context and the split kernel writes every output).
+    single = pkv.decode_launches(desc) == 1
+
+    def split(e=None):
+        if e: e[0].record(stream)
+        if single:
+            pkv.decode(q, k, v, tables, lens, wl.scale, max_ctx, out=out, desc=desc, workspace=ws, stream=stream)
+        else:
+            pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
+        if e: e[1].record(stream)
+
     def step(e=None, e4=None):
         if e4: e4[0].record(stream)
         pool.append(seq_ids, k_new, v_new, tables, lens, stream=stream)
         if e4: e4[1].record(stream)
-        if e: e[0].record(stream)
-        pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
-        if e: e[1].record(stream)
+        split(e)
         if e4: e4[2].record(stream)
-        pkv.merge(desc, lens, out, None, ws, stream=stream)
+        if not single:
+            pkv.merge(desc, lens, out, None, ws, stream=stream)
         if e4: e4[3].record(stream)
 
     ctx0 = wl.context_lens.astype(np.int64)
@@ -495,7 +546,7 @@ def main():
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(N_B2B):
-        pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
+        split()
     b1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = b0.elapsed_time(b1) / N_B2B
@@ -544,11 +595,12 @@ def main():
         "kv_bytes_per_step": int(kv_bytes),
         "unique_kv_bytes_per_step": int(uniq_bytes),
         "kernel_ms": {
-            "partition": round(part_ms, 4),
+            "split": round(part_ms, 4),
+            "decode_launches": 1 if single else 2,
             "kv_append_event_pass": round(float(np.mean(t_app)), 4),
-            "merge_event_pass": round(float(np.mean(t_merge)), 4),
-            "partition_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
-            "partition_back_to_back": round(b2b_ms, 4),
+            "merge_event_pass": None if single else round(float(np.mean(t_merge)), 4),
+            "split_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
+            "split_back_to_back": round(b2b_ms, 4),
         },
         "roofline": {
             "bound": "hbm",
@@ -583,6 +635,10 @@ def main():
         log("[bench] 8-bit K/V: quantise the pool, time the 8-bit decode")
         fp8_kept, res["fp8_kv"] = fp8_leg(wl, q, k, v, tables, lens, max_ctx, K, Wu, dev)
         res["fp8_kv"]["speedup_vs_16bit_split"] = round(part_ms / res["fp8_kv"]["split_ms"], 3)
+    if not args.no_read_ceiling:
+        log("[bench] streaming-read ceiling")
+        res["read_ceiling"] = read_ceiling_leg(dev)
+        res["roofline"]["frac_of_read_ceiling"] = round(achieved / res["read_ceiling"]["best_GBps"], 4)
     if not args.no_prefill:
         log("[bench] chunked prefill leg")
         res["prefill"] = prefill_leg(20, 3, dev)

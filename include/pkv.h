@@ -312,6 +312,12 @@ int32_t paged_attn_partition_size(const pkv_attn_desc* desc);
  * query on the current device), or a negative status. */
 int32_t paged_attn_grid_waves(const pkv_attn_desc* desc);
 
+/* Kernel launches paged_attn_decode / paged_attn_decode_fp8 makes for the
+ * descriptor: 1 when no (sequence, kv head) can span more than one segment
+ * (the split kernel writes every output itself), else 2 (split kernel, then
+ * merge kernel), or a negative status. */
+int32_t paged_attn_decode_launches(const pkv_attn_desc* desc);
+
 /* Bytes of device workspace paged_attn_decode needs (0 on a bad descriptor).
  * With num_waves = 0 the size depends on the current device (the grid is
  * sized by an occupancy query).  Layout, each part 256-byte aligned, with
@@ -354,7 +360,8 @@ int paged_attn_decode_noalloc(const pkv_attn_desc* desc, const void* q, const vo
                               const int32_t* context_lens, float scale, void* out, float* lse,
                               pkv_stream_t stream);
 
-/* The two passes on their own (paged_attn_decode == partials then merge). */
+/* The two passes on their own (paged_attn_decode == partials then merge; the
+ * partials can be exchanged between them, e.g. for a context-parallel split). */
 int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                const int32_t* context_lens, float scale, void* out, float* lse,
@@ -427,6 +434,16 @@ int paged_attn_prefill(const pkv_prefill_desc* desc, const void* q, const void* 
                        const void* v_cache, const int32_t* block_tables,
                        const int32_t* context_lens, const int32_t* cu_seqlens_q, float scale,
                        void* out, float* lse, pkv_stream_t stream);
+
+/* Measurement: read the first floor(bytes / 16384) * 16384 bytes of buf (device,
+ * 16-byte aligned) once with 16-byte vector loads, each wave taking contiguous
+ * 16 KiB pieces in turn, workgroups x 256 threads, non-temporal loads if
+ * nontemporal != 0 -- the rate HBM delivers to plain streaming reads, the
+ * ceiling for the decode kernels' K/V reads.  sink: device uint32
+ * [workgroups * 256], written only in the (practically never) case that a
+ * thread's XOR of its loaded words equals 0x9E3779B9.  Asynchronous on `stream`. */
+int pkv_read_probe(const void* buf, size_t bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink,
+                   pkv_stream_t stream);
 
 /* Debug: the segments of the split for host context lengths, in (seq, kv
  * head, slot) order, as rows of 5 int32: seq, kv_head, slot, tok_lo, tok_hi.

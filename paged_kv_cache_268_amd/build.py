@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pkv_decode.hip", "pkv_append.hip", "pkv_tier.hip", "pkv_fp8.hip", "pkv_prefill.hip", "pkv_noalloc.hip",
-           "pkv_host.cpp"]
+           "pkv_probe.hip", "pkv_host.cpp"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]

@@ -25,6 +25,7 @@
 #include "pkv_append.h"
 #include "pkv_fp8.h"
 #include "pkv_noalloc.h"
+#include "pkv_probe.h"
 #include "pkv_kernels.h"
 #include "pkv_prefill.h"
 #include "pkv_tier.h"
@@ -1105,6 +1106,15 @@ int32_t paged_attn_grid_waves(const pkv_attn_desc* d) {
     return rc ? rc : pl.num_waves;
 }
 
+int32_t paged_attn_decode_launches(const pkv_attn_desc* d) {
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (pl.fixed_chunk == 0 && (rc = resolve_waves(d, &pl))) return rc;
+    if ((rc = size_workspace(d, &pl))) return rc;
+    return pl.max_seg <= 1 ? 1 : 2;
+}
+
 size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
     Plan pl;
     if (resolve(d, &pl)) return 0;
@@ -1313,6 +1323,18 @@ int paged_attn_prefill(const pkv_prefill_desc* d, const void* q, const void* k_c
     a.grid_tiles = (int32_t)tiles;
     hipError_t e = pkv::launch_prefill(a, d->head_dim, d->block_size, d->q_dtype == PKV_BF16, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "prefill kernel launch");
+    return PKV_OK;
+}
+
+int pkv_read_probe(const void* buf, size_t bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink,
+                   pkv_stream_t stream) {
+    const size_t slice = (size_t)pkv::read_probe_slice_bytes();
+    if (!buf || !aligned(buf, 16) || !sink || !aligned(sink, 4))
+        return fail(PKV_EINVAL, "pkv_read_probe: buf (16-byte aligned) and sink (4-byte aligned) are required");
+    if (bytes < slice) return fail(PKV_EINVAL, "pkv_read_probe: %zu bytes, at least %zu needed", bytes, slice);
+    if (workgroups < 1 || workgroups > (1 << 20)) return fail(PKV_EINVAL, "pkv_read_probe: workgroups %d", workgroups);
+    hipError_t e = pkv::launch_read_probe(buf, (int64_t)bytes, workgroups, nontemporal != 0, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "read probe launch");
     return PKV_OK;
 }
 

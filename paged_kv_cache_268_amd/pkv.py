@@ -27,7 +27,7 @@ EXPORTS = (
     "kv_host_tier_stats", "kv_block_pool_set_fp8_scales", "kv_quantize_fp8", "paged_attn_decode_fp8",
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
-    "paged_attn_decode_noalloc",
+    "paged_attn_decode_noalloc", "paged_attn_decode_launches", "pkv_read_probe",
 )
 
 
@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH):
                                             SZ, P], ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
+        "paged_attn_decode_launches": ([ctypes.POINTER(AttnDesc)], I32),
+        "pkv_read_probe": ([P, SZ, I32, I32, P, P], ctypes.c_int),
         "paged_attn_workspace_bytes": ([ctypes.POINTER(AttnDesc)], SZ),
         "paged_attn_decode": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, SZ, P],
                               ctypes.c_int),
@@ -180,6 +182,14 @@ def partition_size(desc: AttnDesc) -> int:
 
 def grid_waves(desc: AttnDesc) -> int:
     r = load().paged_attn_grid_waves(ctypes.byref(desc))
+    if r < 0:
+        check(r)
+    return r
+
+
+def decode_launches(desc: AttnDesc) -> int:
+    """Launches of paged_attn_decode: 1 if no pair can span several segments, else 2 (split, merge)."""
+    r = load().paged_attn_decode_launches(ctypes.byref(desc))
     if r < 0:
         check(r)
     return r
@@ -319,6 +329,12 @@ def plan(desc: AttnDesc, context_lens_host) -> np.ndarray:
     items = np.zeros((n.value, 5), dtype=np.int32)
     check(lib.paged_attn_plan(ctypes.byref(desc), ctx.ctypes.data, items.ctypes.data, n.value, ctypes.byref(n)))
     return items
+
+
+def read_probe(buf, workgroups: int, nontemporal: bool, sink, stream=None):
+    """pkv_read_probe: one streaming read of the device tensor buf (its whole 16 KiB pieces)."""
+    check(load().pkv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), workgroups, 1 if nontemporal else 0,
+                                _ptr(sink), _stream(stream)))
 
 
 def validate_tables(block_tables_host, context_lens_host, num_blocks: int, block_size: int,

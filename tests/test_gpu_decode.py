@@ -223,6 +223,69 @@ def test_many_pairs_long_segment_lists_merge():
     out, lse = gpu_decode(wl, q, k, v, tab, dctx)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
     compare(out, lse, ref_out, ref_lse, what="many pairs P=64")
+    # The two passes called one by one (a workspace that held other data before).
+    desc = pkv.desc_for(q, k, tab, wl.max_context_len, 64)
+    assert pkv.decode_launches(desc) == 2
+    ws = pkv.alloc_workspace(desc, DEV)
+    ws.random_(0, 256)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    pkv.decode_partials(desc, q, k, v, tab, dctx, wl.scale, out2, lse2, ws)
+    pkv.merge(desc, dctx, out2, lse2, ws)
+    torch.cuda.synchronize()
+    compare(out2, lse2, ref_out, ref_lse, what="many pairs P=64, two passes")
+
+
+@pytest.mark.parametrize("kv8", [False, True])
+def test_long_balanced_segment_lists(kv8):
+    """One 20000-token context among tiny ones on the full grid: the balanced split's chunk is
+    its 8-tile minimum, so the long pairs span about 160 segments each, merged by the merge
+    kernel's workgroup per pair (few pairs); 16-bit and two-kv-heads-per-wave 8-bit caches."""
+    wl = small(B=4, Hq=8, Hkv=2, ctx=(20000, 3, 1, 40), seed=21)
+    note(f"~160 balanced segments per pair, 8-bit={kv8}")
+    tab, ctx = to_dev(wl)
+    if kv8:
+        q = W.fill_normal_(torch.empty((4, 8, 128), dtype=torch.bfloat16, device=DEV), 22)
+        kc, vc, ks, vs = W.make_fp8_cache(wl, DEV, poison=True)
+        desc = pkv.desc_for(q, kc, tab, wl.max_context_len, 0)
+        lse = torch.empty((4, 8), device=DEV)
+        out = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, wl.max_context_len, lse=lse)
+        ref_out, ref_lse = oracle.paged_decode(W.bits16(q), kc.cpu().numpy(), vc.cpu().numpy(), wl.block_tables,
+                                               wl.context_lens, wl.scale, num_kv_heads=2, block_size=16,
+                                               dtype=oracle.BF16, kv_dtype=oracle.FP8, k_scale=ks.cpu().numpy(),
+                                               v_scale=vs.cpu().numpy())
+    else:
+        q, k, v = W.make_values(wl, DEV, poison=True)
+        desc = pkv.desc_for(q, k, tab, wl.max_context_len, 0)
+        out, lse = gpu_decode(wl, q, k, v, tab, ctx)
+        ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
+    torch.cuda.synchronize()
+    items = pkv.plan(desc, wl.context_lens)
+    assert int((items[:, 0] == 0).sum()) // 2 > 100          # segments per pair of the long context
+    compare(out, lse, ref_out, ref_lse, what="long balanced lists")
+
+
+def test_workspace_reused_across_descriptors():
+    """One workspace for calls with different descriptors (sequence counts, splits, kv head
+    counts), filled with garbage before each: its contents on entry do not matter."""
+    shapes = [(6, 8, 2, (5, 700, 1024, 1500, 0, 33), 0, 8), (3, 32, 8, (3000, 17, 900), 0, 0),
+              (8, 4, 4, (1, 15, 16, 17, 511, 512, 513, 2000), 256, 0), (2, 8, 2, (4000, 64), 0, 4)]
+    big = max(pkv.workspace_bytes(pkv.attn_desc(B, Hq, Hkv, 128, 16, 1, 1024, 4096, P, num_waves=nw))
+              for B, Hq, Hkv, _, P, nw in shapes)
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    for i, (B, Hq, Hkv, lens, P, nw) in enumerate(shapes):
+        wl = small(B=B, Hq=Hq, Hkv=Hkv, ctx=lens, seed=30 + i)
+        note(f"workspace reuse {i}: B={B} Hq={Hq} Hkv={Hkv} P={P} nw={nw}")
+        q, k, v = W.make_values(wl, DEV, poison=True)
+        tab, ctx = to_dev(wl)
+        ws.random_(0, 256)
+        desc = pkv.desc_for(q, k, tab, wl.max_context_len, P, num_waves=nw)
+        lse = torch.empty((B, Hq), device=DEV)
+        out = pkv.decode(q, k, v, tab, ctx, wl.scale, wl.max_context_len, lse=lse, desc=desc,
+                         workspace=ws[:pkv.workspace_bytes(desc)])
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
+        compare(out, lse, ref_out, ref_lse, what=f"reuse {i}")
 
 
 @pytest.mark.parametrize("P,nw", [(256, 0), (0, 8), (0, 16), (512, 4)])

@@ -216,6 +216,7 @@ def test_split_sizes_and_workspace():
     # balanced: rows = waves (at most one chunk each) + pairs; one q head per row (MHA)
     rows = 8 + 4 * 4
     assert pkv.workspace_bytes(d) == up(4 * 7) + up(rows * 1 * 64 * 4) + up(rows * 1 * 4)
+    assert pkv.decode_launches(d) == 2                    # split, then merge
     # fixed 512-token partitions: rows = pairs * ceil(8192 / 512) + pairs; the group's 4 q heads per row
     d = pkv.attn_desc(64, 32, 8, 128, 16, 30000, 512, 8192, 512, num_waves=0)
     rows = 64 * 8 * (8192 // 512) + 64 * 8
@@ -224,6 +225,9 @@ def test_split_sizes_and_workspace():
     d = pkv.attn_desc(3, 16, 4, 128, 16, 64, 64, 1000, 0, kv_dtype=pkv.PKV_FP8_E4M3, num_waves=64)
     rows = 64 + 3 * 2
     assert pkv.workspace_bytes(d) == up(4 * 6) + up(rows * 8 * 128 * 4) + up(rows * 8 * 4)
+    # merge launches: none when one partition covers every context
+    assert pkv.decode_launches(pkv.attn_desc(2, 8, 4, 128, 16, 100, 1024, 16384, 512, num_waves=64)) == 2
+    assert pkv.decode_launches(pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 1024, num_waves=64)) == 1
     # a fixed split never gets more waves than chunks
     d = pkv.attn_desc(2, 8, 4, 128, 16, 100, 64, 1000, 512, num_waves=4000)
     assert pkv.grid_waves(d) == 2 * 4 * 2
