@@ -228,6 +228,18 @@ int kv_write_tables(pkv_pool* pool, int32_t* block_tables, int32_t* context_lens
 int kv_block_pool_attach_host_tier(pkv_pool* pool, int32_t num_host_blocks, void* k_host,
                                    void* v_host);
 
+/* The host tier of an 8-bit pool (kv_dtype PKV_FP8_E4M3): as above, with the
+ * codes in k_host / v_host (uint8 [num_host_blocks][num_kv_heads][block_size]
+ * [head_dim]) and each host block's scales in k_scale_host / v_scale_host
+ * (float [num_host_blocks][num_kv_heads], pinned, device-mapped, 4-byte
+ * aligned): a block's K and V scales move with its codes, both ways.  The
+ * pool's device scales (kv_block_pool_set_fp8_scales) must be set before
+ * kv_seq_offload / kv_seq_restore.  At most 256 kv heads.
+ * kv_block_pool_attach_host_tier refuses an 8-bit pool, and this call a
+ * 16-bit one. */
+int kv_block_pool_attach_host_tier_fp8(pkv_pool* pool, int32_t num_host_blocks, void* k_host, void* v_host,
+                                       float* k_scale_host, float* v_scale_host);
+
 /* For each of the n listed sequences (host array, no repeats) holding more
  * than gpu_window blocks (gpu_window >= 1), move every GPU block before its
  * last gpu_window blocks to a new host block, in sequence order then logical

@@ -103,6 +103,8 @@ struct pkv_pool {
     int32_t num_host = 0;
     void* k_host_dev = nullptr;
     void* v_host_dev = nullptr;
+    float* ks_host_dev = nullptr;                // 8-bit pools: host-tier scales [num_host][Hkv]
+    float* vs_host_dev = nullptr;
     std::vector<int32_t> host_stack;
     std::vector<int32_t> host_ref;
     std::vector<int32_t> nhost;                  // host blocks held, per sequence row (> 0: parked)
@@ -654,41 +656,66 @@ int kv_write_tables(pkv_pool* p, int32_t* block_tables, int32_t* context_lens, p
 // Host tier
 // --------------------------------------------------------------------------
 
-int kv_block_pool_attach_host_tier(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host) {
-    if (!p || !k_host || !v_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: null argument");
-    if (p->num_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: the pool already has a host tier");
-    if (p->d.kv_dtype == PKV_FP8_E4M3)
-        return fail(PKV_EUNSUPPORTED, "kv_block_pool_attach_host_tier: 8-bit pools have no host tier (their scales do not move)");
-    if (num_host_blocks < 1) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: %d host blocks", num_host_blocks);
+// Device-mapped address of pinned host memory, or null (pageable memory is refused).
+static void* mapped(void* h) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, h) != hipSuccess || at.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return d;
+}
+
+static int attach_tier(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host, float* ks_host,
+                       float* vs_host, const char* who) {
+    if (p->num_host) return fail(PKV_EINVAL, "%s: the pool already has a host tier", who);
+    if (num_host_blocks < 1) return fail(PKV_EINVAL, "%s: %d host blocks", who, num_host_blocks);
     if (!aligned(k_host, 16) || !aligned(v_host, 16))
-        return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers must be 16-byte aligned");
+        return fail(PKV_EINVAL, "%s: host buffers must be 16-byte aligned", who);
+    if (ks_host && (!aligned(ks_host, 4) || !aligned(vs_host, 4)))
+        return fail(PKV_EINVAL, "%s: host scale arrays must be 4-byte aligned", who);
     // Only pinned host memory (hipHostMalloc) is reachable from a kernel; a
     // pageable buffer is refused here, before any copy could touch it.
-    for (void* h : {k_host, v_host}) {
-        hipPointerAttribute_t at{};
-        const hipError_t pe = hipPointerGetAttributes(&at, h);
-        if (pe != hipSuccess || at.type != hipMemoryTypeHost) {
-            (void)hipGetLastError();
-            return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers are not pinned host memory "
-                                    "(allocate them with hipHostMalloc)");
-        }
-    }
-    void* kd = nullptr;
-    void* vd = nullptr;
-    hipError_t e = hipHostGetDevicePointer(&kd, k_host, 0);
-    if (e == hipSuccess) e = hipHostGetDevicePointer(&vd, v_host, 0);
-    if (e != hipSuccess || !kd || !vd) {
-        (void)hipGetLastError();
-        return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: host buffers are not pinned, device-mapped "
-                                "memory (allocate them with hipHostMalloc)");
-    }
+    void* kd = mapped(k_host);
+    void* vd = mapped(v_host);
+    void* ksd = ks_host ? mapped(ks_host) : nullptr;
+    void* vsd = vs_host ? mapped(vs_host) : nullptr;
+    if (!kd || !vd || (ks_host && (!ksd || !vsd)))
+        return fail(PKV_EINVAL, "%s: host buffers are not pinned, device-mapped host memory "
+                                "(allocate them with hipHostMalloc)", who);
     p->num_host = num_host_blocks;
     p->k_host_dev = kd;
     p->v_host_dev = vd;
+    p->ks_host_dev = static_cast<float*>(ksd);
+    p->vs_host_dev = static_cast<float*>(vsd);
     p->host_stack.resize(num_host_blocks);
     for (int32_t i = 0; i < num_host_blocks; ++i) p->host_stack[i] = num_host_blocks - 1 - i;   // pops 0, 1, ...
     p->host_ref.assign(num_host_blocks, 0);
     return PKV_OK;
+}
+
+int kv_block_pool_attach_host_tier(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host) {
+    if (!p || !k_host || !v_host) return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: null argument");
+    if (p->d.kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_EINVAL, "kv_block_pool_attach_host_tier: an 8-bit pool's host tier also holds the block "
+                                "scales (kv_block_pool_attach_host_tier_fp8)");
+    return attach_tier(p, num_host_blocks, k_host, v_host, nullptr, nullptr, "kv_block_pool_attach_host_tier");
+}
+
+int kv_block_pool_attach_host_tier_fp8(pkv_pool* p, int32_t num_host_blocks, void* k_host, void* v_host,
+                                       float* k_scale_host, float* v_scale_host) {
+    const char* who = "kv_block_pool_attach_host_tier_fp8";
+    if (!p || !k_host || !v_host || !k_scale_host || !v_scale_host) return fail(PKV_EINVAL, "%s: null argument", who);
+    if (p->d.kv_dtype != PKV_FP8_E4M3) return fail(PKV_EINVAL, "%s: not an 8-bit pool", who);
+    if (p->d.num_kv_heads > 256)
+        return fail(PKV_EUNSUPPORTED, "%s: %d kv heads (the block-move kernel carries at most 256 scales per block)",
+                    who, p->d.num_kv_heads);
+    return attach_tier(p, num_host_blocks, k_host, v_host, k_scale_host, v_scale_host, who);
 }
 
 int kv_host_tier_stats(const pkv_pool* p, int32_t* num_free_out, int32_t block, int32_t* refcount_out) {
@@ -752,7 +779,15 @@ static int launch_moves(pkv_pool* p, pkv_pool::CopySlot* c, int64_t n, bool to_h
     a.v_dst = static_cast<uint4*>(to_host ? p->v_host_dev : p->v_cache);
     a.pairs = c->pairs;
     a.n = (int32_t)n;
-    a.vec_per_block = (int32_t)((int64_t)p->d.num_kv_heads * p->d.block_size * p->d.head_dim * 2 / 16);
+    const bool kv8 = p->d.kv_dtype == PKV_FP8_E4M3;
+    a.vec_per_block = (int32_t)((int64_t)p->d.num_kv_heads * p->d.block_size * p->d.head_dim * (kv8 ? 1 : 2) / 16);
+    if (kv8) {
+        a.ks_src = to_host ? p->k_scale : p->ks_host_dev;
+        a.vs_src = to_host ? p->v_scale : p->vs_host_dev;
+        a.ks_dst = to_host ? p->ks_host_dev : p->k_scale;
+        a.vs_dst = to_host ? p->vs_host_dev : p->v_scale;
+        a.scales_per_block = p->d.num_kv_heads;
+    }
     hipError_t e = pkv::launch_tier_copy(a, stream);
     if (e != hipSuccess) return fail_hip(e, "block-move launch (pool state now ahead of the device)");
     e = hipEventRecord(c->ev, stream);
@@ -767,6 +802,8 @@ int kv_seq_offload(pkv_pool* p, int32_t n, const int32_t* seq_ids, int32_t gpu_w
     if (!p->num_host) return fail(PKV_EINVAL, "kv_seq_offload: the pool has no host tier");
     if (gpu_window < 1) return fail(PKV_EINVAL, "kv_seq_offload: gpu_window %d (must be >= 1)", gpu_window);
     if (!p->k_cache || !p->v_cache) return fail(PKV_EINVAL, "kv_seq_offload: the pool has no device caches");
+    if (p->d.kv_dtype == PKV_FP8_E4M3 && !p->k_scale)
+        return fail(PKV_EINVAL, "kv_seq_offload: 8-bit pool without scales (kv_block_pool_set_fp8_scales)");
     int rc = check_ids(p, n, seq_ids, "kv_seq_offload");
     if (rc) return rc;
     int64_t need = 0;
@@ -808,6 +845,8 @@ int kv_seq_restore(pkv_pool* p, int32_t n, const int32_t* seq_ids, pkv_stream_t 
     if (!p) return fail(PKV_EINVAL, "kv_seq_restore: null pool");
     if (!p->num_host) return fail(PKV_EINVAL, "kv_seq_restore: the pool has no host tier");
     if (!p->k_cache || !p->v_cache) return fail(PKV_EINVAL, "kv_seq_restore: the pool has no device caches");
+    if (p->d.kv_dtype == PKV_FP8_E4M3 && !p->k_scale)
+        return fail(PKV_EINVAL, "kv_seq_restore: 8-bit pool without scales (kv_block_pool_set_fp8_scales)");
     int rc = check_ids(p, n, seq_ids, "kv_seq_restore");
     if (rc) return rc;
     int64_t need = 0;

@@ -10,7 +10,8 @@
 // before its stores, which keeps many host-link transactions in flight per
 // workgroup.  The same kernel serves both directions: the host tier is
 // addressed through its device-mapped pointer (the GPU's loads or stores
-// cross the host link).  The copy is bit-exact.
+// cross the host link).  For an 8-bit pool the block's per-kv-head K and V
+// scales move with its codes.  The copy is bit-exact.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +26,12 @@ __global__ void __launch_bounds__(kCopyThreads) kv_tier_copy_kernel(TierCopyArgs
     __shared__ int32_t s_pair[2];
     if (threadIdx.x < 2) s_pair[threadIdx.x] = a.pairs[2 * (int64_t)blockIdx.x + threadIdx.x];
     __syncthreads();
+    if ((int)threadIdx.x < a.scales_per_block) {
+        const int64_t so = (int64_t)s_pair[0] * a.scales_per_block + threadIdx.x;
+        const int64_t dof = (int64_t)s_pair[1] * a.scales_per_block + threadIdx.x;
+        a.ks_dst[dof] = a.ks_src[so];
+        a.vs_dst[dof] = a.vs_src[so];
+    }
     const int64_t src = (int64_t)s_pair[0] * a.vec_per_block;
     const int64_t dst = (int64_t)s_pair[1] * a.vec_per_block;
     for (int base = 0; base < a.vec_per_block; base += kCopyThreads * kCopyUnroll) {
@@ -50,7 +57,9 @@ __global__ void __launch_bounds__(kCopyThreads) kv_tier_copy_kernel(TierCopyArgs
 
 hipError_t launch_tier_copy(const TierCopyArgs& a, hipStream_t stream) {
     if (a.n == 0) return hipSuccess;
-    if (a.n < 0 || a.vec_per_block <= 0) return hipErrorInvalidValue;
+    if (a.n < 0 || a.vec_per_block <= 0 || a.scales_per_block < 0 || a.scales_per_block > kCopyThreads ||
+        (a.scales_per_block > 0 && (!a.ks_src || !a.vs_src || !a.ks_dst || !a.vs_dst)))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(kv_tier_copy_kernel, dim3((unsigned)a.n), dim3(kCopyThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -28,6 +28,7 @@ EXPORTS = (
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
     "paged_attn_decode_noalloc", "paged_attn_decode_launches", "pkv_read_probe",
+    "kv_block_pool_attach_host_tier_fp8",
 )
 
 
@@ -85,6 +86,7 @@ def load(path: str = LIB_PATH):
         "kv_append_tokens": ([P, I32, P, P, P, P, P, P, P], ctypes.c_int),
         "kv_validate_tables": ([I32, P, I32, I32, P, I32, I32], ctypes.c_int),
         "kv_block_pool_attach_host_tier": ([P, I32, P, P], ctypes.c_int),
+        "kv_block_pool_attach_host_tier_fp8": ([P, I32, P, P, P, P], ctypes.c_int),
         "kv_seq_offload": ([P, I32, P, I32, P], ctypes.c_int),
         "kv_seq_restore": ([P, I32, P, P], ctypes.c_int),
         "kv_host_tier_stats": ([P, PI32, I32, PI32], ctypes.c_int),
@@ -443,6 +445,14 @@ class BlockPool:
         """k_host / v_host: pinned CPU tensors [num_host_blocks][Hkv][bs][D] (torch pin_memory=True)."""
         check(self.lib.kv_block_pool_attach_host_tier(self.handle, num_host_blocks, _ptr(k_host), _ptr(v_host)))
         self.k_host, self.v_host = k_host, v_host
+
+    def attach_host_tier_fp8(self, num_host_blocks: int, k_host, v_host, k_scale_host, v_scale_host):
+        """8-bit pools: pinned uint8 codes [num_host_blocks][Hkv][bs][D] and pinned float32 scales
+        [num_host_blocks][Hkv] for K and V."""
+        check(self.lib.kv_block_pool_attach_host_tier_fp8(self.handle, num_host_blocks, _ptr(k_host), _ptr(v_host),
+                                                          _ptr(k_scale_host), _ptr(v_scale_host)))
+        self.k_host, self.v_host = k_host, v_host
+        self.k_scale_host, self.v_scale_host = k_scale_host, v_scale_host
 
     def offload(self, seq_ids, gpu_window: int, stream=None):
         ids = _i32(seq_ids)

@@ -377,9 +377,18 @@ def test_fp8_entry_points_reject_mismatch():
     with pytest.raises(pkv.PkvError) as e:
         pkv.decode_fp8(q, kc, vc, None, vs, tab, ctx, wl.scale, wl.max_context_len)
     assert e.value.code == pkv.PKV_EINVAL
+    # an 8-bit pool's host tier carries the block scales too: the 16-bit attach call refuses it,
+    # and the 8-bit one refuses a 16-bit pool
     pool = pkv.BlockPool(8, 16, 1, 64, pkv.PKV_FP8_E4M3, 2, 2, k_cache=kc, v_cache=vc)
     kh = torch.zeros((2, 1, 16, 64), dtype=torch.uint8, pin_memory=True)
+    sh = torch.zeros((2, 1), dtype=torch.float32, pin_memory=True)
     with pytest.raises(pkv.PkvError) as e:
         pool.attach_host_tier(2, kh, kh)
-    assert e.value.code == pkv.PKV_EUNSUPPORTED
+    assert e.value.code == pkv.PKV_EINVAL and "attach_host_tier_fp8" in str(e.value)
+    pool.close()
+    k16 = torch.zeros((8, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    pool = pkv.BlockPool(8, 16, 1, 64, pkv.PKV_BF16, 2, 2, k_cache=k16, v_cache=k16)
+    with pytest.raises(pkv.PkvError) as e:
+        pool.attach_host_tier_fp8(2, kh, kh, sh, sh)
+    assert e.value.code == pkv.PKV_EINVAL
     pool.close()

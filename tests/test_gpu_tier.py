@@ -286,3 +286,157 @@ def test_tier_errors_launch_nothing():
     torch.cuda.synchronize()
     assert pool.host_stats()[0] == 2
     pool.close()
+
+
+def _fp8_pool_with_spare(wl, spare):
+    """8-bit codes and scales for the workload's pool plus `spare` blocks of NaN codes / NaN scales
+    (restored blocks land there), and the pool over them with the default scales set."""
+    kc, vc, ks, vs = W.make_fp8_cache(wl, DEV)
+    NB = wl.num_blocks
+    kc2 = torch.full((NB + spare,) + tuple(kc.shape[1:]), 0x7F, dtype=torch.uint8, device=DEV)
+    vc2 = torch.full_like(kc2, 0x7F)
+    kc2[:NB] = kc; vc2[:NB] = vc
+    ks2 = torch.full((NB + spare, wl.num_kv_heads), float("nan"), device=DEV)
+    vs2 = torch.full_like(ks2, float("nan"))
+    ks2[:NB] = ks; vs2[:NB] = vs
+    order = np.concatenate([wl.alloc_order, np.arange(NB, NB + spare)]).astype(np.int32)
+    pool = pkv.BlockPool(NB + spare, wl.block_size, wl.num_kv_heads, wl.head_dim, pkv.PKV_FP8_E4M3, wl.num_seqs,
+                         wl.table_width, k_cache=kc2, v_cache=vc2, alloc_order=order)
+    init = torch.full((wl.num_kv_heads,), 0.01, device=DEV)
+    pool.set_fp8_scales(ks2, vs2, init, init)
+    return pool, kc2, vc2, ks2, vs2
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_fp8_decode_after_round_trip_bit_exact(P):
+    """8-bit pool: offload every sequence past a 4-block window (codes and scales land in the host
+    tier), decode (parked rows are empty), restore into fresh blocks, decode again: bit for bit the
+    decode before the round trip."""
+    lens = [700, 2000, 64, 1500, 65, 3000, 100, 999]
+    wl = W.make_workload(len(lens), 32, 8, 128, 16, "bf16", lens, seed=61)
+    note(f"8-bit host tier round trip, P={P}")
+    B, Hkv, bs = wl.num_seqs, wl.num_kv_heads, wl.block_size
+    used = int(sum(-(-n // bs) for n in lens))
+    pool, kc, vc, ks, vs = _fp8_pool_with_spare(wl, used)
+    for s in range(B):
+        n = -(-lens[s] // bs)
+        assert pool.import_seq(lens[s], wl.block_tables[s, :n]) == s
+    kh = torch.zeros((used, Hkv, bs, 128), dtype=torch.uint8, pin_memory=True)
+    vh = torch.zeros_like(kh, pin_memory=True)
+    ksh = torch.zeros((used, Hkv), dtype=torch.float32, pin_memory=True)
+    vsh = torch.zeros_like(ksh, pin_memory=True)
+    with pytest.raises(pkv.PkvError) as e:
+        pool.attach_host_tier(used, kh, vh)                    # an 8-bit tier needs the scale arrays
+    assert e.value.code == pkv.PKV_EINVAL
+    pool.attach_host_tier_fp8(used, kh, vh, ksh, vsh)
+    tab = torch.full((B, wl.table_width), -1, dtype=torch.int32, device=DEV)
+    ctx = torch.zeros(B, dtype=torch.int32, device=DEV)
+    pool.write_tables(tab, ctx)
+    q = W.fill_normal_(torch.empty((B, 32, 128), dtype=torch.bfloat16, device=DEV), 62)
+    mc = max(lens)
+    lse0 = torch.empty((B, 32), device=DEV)
+    out0 = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, mc, partition_size=P, lse=lse0)
+    torch.cuda.synchronize()
+    before = [pool.info(s)[1] for s in range(B)]
+    kc0, vc0, ks0, vs0 = kc.cpu(), vc.cpu(), ks.cpu(), vs.cpu()
+    pool.offload(list(range(B)), 4)
+    pool.write_tables(tab, ctx)
+    out1 = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, mc, partition_size=P)
+    torch.cuda.synchronize()
+    parked = [s for s in range(B) if -(-lens[s] // bs) > 4]     # 64 tokens = 4 blocks: stays on the GPU
+    assert len(parked) == B - 1
+    kept = [s for s in range(B) if s not in parked]
+    assert torch.all(out1[parked] == 0) and torch.equal(out1[kept], out0[kept])
+    for s in range(B):
+        for j, e in enumerate(pool.info(s)[1]):
+            if e <= -2:
+                c, g = -2 - e, before[s][j]
+                assert torch.equal(kh[c], kc0[g]) and torch.equal(vh[c], vc0[g])
+                assert torch.equal(ksh[c], ks0[g]) and torch.equal(vsh[c], vs0[g])
+    pool.restore(list(range(B)))
+    pool.write_tables(tab, ctx)
+    lse2 = torch.empty_like(lse0)
+    out2 = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, mc, partition_size=P, lse=lse2)
+    torch.cuda.synchronize()
+    assert any(a[0] != b[0] for a, b in zip([pool.info(s)[1] for s in range(B)], before))
+    assert torch.equal(out2.view(torch.int32), out0.view(torch.int32))
+    assert torch.equal(lse2.view(torch.int32), lse0.view(torch.int32))
+    pool.close()
+
+
+def test_fp8_tier_random_moves_bit_exact():
+    """8-bit pool: random add / fork / free / offload / restore against the replay; the codes and
+    the scales of both tiers against a host mirror that applies the replay's moves."""
+    NB, NH, S, Wd, Hkv, bs, D = 40, 24, 6, 10, 2, 16, 64
+    note("8-bit host tier random moves")
+    wl = W.make_workload(1, 2, Hkv, D, bs, "bf16", [16], seed=63, num_blocks=NB)
+    kc, vc, ks, vs = W.make_fp8_cache(wl, DEV)
+    order = np.random.default_rng(64).permutation(NB).astype(np.int32)
+    pool = pkv.BlockPool(NB, bs, Hkv, D, pkv.PKV_FP8_E4M3, S, Wd, k_cache=kc, v_cache=vc, alloc_order=order)
+    init = torch.full((Hkv,), 0.01, device=DEV)
+    pool.set_fp8_scales(ks, vs, init, init)
+    kh = torch.zeros((NH, Hkv, bs, D), dtype=torch.uint8, pin_memory=True)
+    vh = torch.zeros_like(kh, pin_memory=True)
+    ksh = torch.zeros((NH, Hkv), dtype=torch.float32, pin_memory=True)
+    vsh = torch.zeros_like(ksh, pin_memory=True)
+    pool.attach_host_tier_fp8(NH, kh, vh, ksh, vsh)
+    ref = R.PoolReplay(NB, bs, S, Wd, alloc_order=order)
+    ref.attach_host_tier(NH)
+    torch.cuda.synchronize()
+    dev = [kc.cpu().numpy().copy(), vc.cpu().numpy().copy(), ks.cpu().numpy().copy(), vs.cpu().numpy().copy()]
+    host = [kh.numpy().copy(), vh.numpy().copy(), ksh.numpy().copy(), vsh.numpy().copy()]
+    rng = np.random.default_rng(65)
+    live, moves = [], 0
+    for it in range(300):
+        op = rng.random()
+        pick = lambda: sorted(rng.choice(live, rng.integers(1, len(live) + 1), replace=False).tolist())
+        if op < 0.25 and len(live) < S:
+            n = int(rng.integers(1, 6 * bs))
+            nb = -(-n // bs)
+            if nb > ref.num_free():
+                continue
+            ids = [ref.free[-1 - i] for i in range(nb)]           # the next blocks the replay hands out
+            s = pool.import_seq(n, ids); assert s == ref.import_seq(ids, n); live.append(s)
+        elif op < 0.32 and live and len(live) < S:
+            src = int(rng.choice(live))
+            s = pool.fork(src); assert s == ref.fork(src); live.append(s)
+        elif op < 0.40 and live:
+            s = int(rng.choice(live)); live.remove(s)
+            pool.free(s); ref.free_seq(s)
+        elif op < 0.70 and live:
+            ids, w = pick(), int(rng.integers(1, 4))
+            try:
+                copies = ref.offload(ids, w)
+            except R.PoolError:
+                with pytest.raises(pkv.PkvError):
+                    pool.offload(ids, w)
+            else:
+                pool.offload(ids, w)
+                for g, c in copies:
+                    for a in range(4):
+                        host[a][c] = dev[a][g]
+                moves += len(copies)
+        elif live:
+            ids = pick()
+            try:
+                copies = ref.restore(ids)
+            except R.PoolError:
+                with pytest.raises(pkv.PkvError):
+                    pool.restore(ids)
+            else:
+                pool.restore(ids)
+                for c, g in copies:
+                    for a in range(4):
+                        dev[a][g] = host[a][c]
+                moves += len(copies)
+        for s in live:
+            assert pool.info(s) == (ref.seqs[s][1], ref.seqs[s][0])
+        if it % 30 == 29:
+            torch.cuda.synchronize()
+            for got, want in zip((kc, vc, ks, vs), dev):
+                assert np.array_equal(got.cpu().numpy(), want)
+            for got, want in zip((kh, vh, ksh, vsh), host):
+                assert np.array_equal(got.numpy(), want)
+    note(f"  {moves} block moves")
+    assert moves > 40
+    pool.close()
