@@ -265,27 +265,32 @@ def fp8_leg(wl, q, k, v, tables, lens, max_ctx, steps, warmup, dev):
     stream = torch.cuda.current_stream()
     single = pkv.decode_launches(desc) == 1
 
-    def run(e):
-        e[0].record(stream)
-        if single:
-            pkv.decode_fp8(q, kc, vc, ks, vs, tables, lens, wl.scale, max_ctx, out=out, desc=desc, workspace=ws,
-                           stream=stream)
-            e[1].record(stream)
+    # Split kernel: events stamped by its own dispatch; split + merge: marker events
+    # around both launches, in a pass of their own.
+    def run(e=None, ew=None):
+        if ew: ew[0].record(stream)
+        if e:
+            pkv.decode_partials_timed(desc, q, kc, vc, ks, vs, tables, lens, wl.scale, out, None, ws, e[0], e[1],
+                                      stream=stream)
         else:
             pkv.decode_partials_fp8(desc, q, kc, vc, ks, vs, tables, lens, wl.scale, out, None, ws, stream=stream)
-            e[1].record(stream)
+        if not single:
             pkv.merge(desc, lens, out, None, ws, stream=stream)
-        e[2].record(stream)
+        if ew: ew[1].record(stream)
 
     for _ in range(warmup):
-        run([torch.cuda.Event() for _ in range(3)])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        run()
+    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] for _ in range(steps)]
+    evw = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:
-        run(e)
+        run(e=e)
     torch.cuda.synchronize()
-    part = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    whole = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+    for e in evw:
+        run(ew=e)
+    torch.cuda.synchronize()
+    part = float(np.mean([e[0].elapsed_ms(e[1]) for e in ev]))
+    whole = float(np.mean([e[0].elapsed_time(e[1]) for e in evw]))
     ctx = lens.cpu().numpy().astype(np.int64)
     nblk = int(((ctx + bs - 1) // bs).sum())
     alg = int(ctx.sum()) * Hkv * D * 2 + nblk * Hkv * 8      # codes of K and V, plus their scales
@@ -493,10 +498,12 @@ def main():
     out = torch.empty((B, Hq, D), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
-    # The timed loop brackets only the split kernel with events (its duration is
-    # the roofline's denominator); every event record adds a marker packet to the
-    # stream, so the append/merge breakdown comes from a separate pass afterwards.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    # The split kernel's duration (the roofline's denominator) comes from two HIP
+    # events per timed step that its own dispatch stamps with its start and end
+    # (paged_attn_decode_partials_timed): no marker packet enters the timed steps.
+    # Marker events cost a few microseconds each, so the append/merge breakdown
+    # comes from a separate pass afterwards.
+    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] for _ in range(K)]
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
     # The split kernel, then the merge kernel (one launch when a single partition covers every
@@ -504,12 +511,11 @@ def main():
     single = pkv.decode_launches(desc) == 1
 
     def split(e=None):
-        if e: e[0].record(stream)
-        if single:
-            pkv.decode(q, k, v, tables, lens, wl.scale, max_ctx, out=out, desc=desc, workspace=ws, stream=stream)
+        if e:
+            pkv.decode_partials_timed(desc, q, k, v, None, None, tables, lens, wl.scale, out, None, ws, e[0], e[1],
+                                      stream=stream)
         else:
             pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
-        if e: e[1].record(stream)
 
     def step(e=None, e4=None):
         if e4: e4[0].record(stream)
@@ -563,7 +569,7 @@ def main():
     tok_bytes = Hkv * D * 2 * 2
     uniq_end = unique_kv_bytes(tables_end, lens_end, bs, tok_bytes)
     uniq_bytes = uniq_end - (K - 1) / 2 * B * tok_bytes
-    t_part = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    t_part = [ev[i][0].elapsed_ms(ev[i][1]) for i in range(K)]
     t_app = [e[0].elapsed_time(e[1]) for e in ev4]
     t_merge = [e[2].elapsed_time(e[3]) for e in ev4]
     part_ms = float(np.mean(t_part))

@@ -43,6 +43,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* pkv_stream_t;   /* the same type as hipStream_t */
+typedef struct ihipEvent_t* pkv_event_t;     /* the same type as hipEvent_t */
 
 enum {
     PKV_OK = 0,
@@ -381,6 +382,24 @@ int paged_attn_decode_partials(const pkv_attn_desc* desc, const void* q, const v
 int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, void* out,
                      float* lse, const void* workspace, size_t workspace_bytes,
                      pkv_stream_t stream);
+
+/* paged_attn_decode_partials (16-bit K/V: k_scale = v_scale = NULL) or
+ * paged_attn_decode_partials_fp8 (8-bit K/V: the scales as there), with the
+ * split kernel's duration taken by two events: start and stop (hipEvent_t,
+ * created by the caller with timing enabled, on the stream's device) receive
+ * the start and end timestamps of the split kernel's own dispatch
+ * (hipExtLaunchKernel), so no marker packets are added to the stream and
+ * timed launches run back to back as untimed ones do;
+ * hipEventElapsedTime(start, stop) is then the kernel's duration.  Both events
+ * must be non-NULL (PKV_EINVAL).  Everything else, including the outputs and
+ * the workspace, is as for the untimed calls. */
+int paged_attn_decode_partials_timed(const pkv_attn_desc* desc, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     float scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, pkv_event_t start, pkv_event_t stop,
+                                     pkv_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decode over an 8-bit K/V cache (kv_dtype PKV_FP8_E4M3, q_dtype PKV_BF16).

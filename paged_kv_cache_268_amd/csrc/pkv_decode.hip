@@ -46,6 +46,7 @@
 // D/4 consecutive output values of head l%16 and the result is either the
 // final output (the segment covers all of (s, g)) or a normalised partial
 // plus its log2-domain lse in the workspace for the merge kernel.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -849,8 +850,12 @@ paged_decode_merge_kernel(MergeArgs a) {
 // Launchers.
 // ---------------------------------------------------------------------------
 
+// Timing events of a split launch: null, or start and stop events that the
+// dispatch itself stamps (hipExtLaunchKernel).
+struct LaunchEvents { hipEvent_t start, stop; };
+
 template <int D, int BS, int GP, bool BF16, bool KV8, int HW>
-static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStream_t stream) {
+static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStream_t stream, const LaunchEvents* ev) {
     auto kern = paged_decode_split_kernel<D, BS, GP, BF16, KV8, HW>;
     if (waves_per_cu) {
         int blocks = 0;
@@ -859,65 +864,72 @@ static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStre
         *waves_per_cu = blocks * kWaves;
         return hipSuccess;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a->num_waves / kWaves)), dim3(kThreads), 0, stream, *a);
+    const dim3 grid((unsigned)(a->num_waves / kWaves));
+    if (ev && (ev->start || ev->stop))
+        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, ev->start, ev->stop, 0, *a);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, *a);
     return hipGetLastError();
 }
 
 template <int D, int BS, bool BF16, bool KV8, int HW>
-static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st) {
+static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st, const LaunchEvents* ev) {
     if constexpr (HW == 1) {
         switch (gp) {
-            case 1: return split_dispatch<D, BS, 1, BF16, KV8, 1>(a, wpc, st);
-            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 1>(a, wpc, st);
-            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 1>(a, wpc, st);
-            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 1>(a, wpc, st);
+            case 1: return split_dispatch<D, BS, 1, BF16, KV8, 1>(a, wpc, st, ev);
+            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 1>(a, wpc, st, ev);
+            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 1>(a, wpc, st, ev);
+            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 1>(a, wpc, st, ev);
         }
     } else {
         switch (gp) {          // columns of two kv heads' q groups: 2 G
-            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 2>(a, wpc, st);
-            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 2>(a, wpc, st);
-            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 2>(a, wpc, st);
-            case 16: return split_dispatch<D, BS, 16, BF16, KV8, 2>(a, wpc, st);
+            case 2: return split_dispatch<D, BS, 2, BF16, KV8, 2>(a, wpc, st, ev);
+            case 4: return split_dispatch<D, BS, 4, BF16, KV8, 2>(a, wpc, st, ev);
+            case 8: return split_dispatch<D, BS, 8, BF16, KV8, 2>(a, wpc, st, ev);
+            case 16: return split_dispatch<D, BS, 16, BF16, KV8, 2>(a, wpc, st, ev);
         }
     }
     return hipErrorInvalidValue;
 }
 
 template <int D, bool BF16, bool KV8, int HW>
-static hipError_t split_b(const DecodeArgs* a, int bs, int gp, int* wpc, hipStream_t st) {
-    if (bs == 16) return split_g<D, 16, BF16, KV8, HW>(a, gp, wpc, st);
-    if (bs == 32) return split_g<D, 32, BF16, KV8, HW>(a, gp, wpc, st);
+static hipError_t split_b(const DecodeArgs* a, int bs, int gp, int* wpc, hipStream_t st, const LaunchEvents* ev) {
+    if (bs == 16) return split_g<D, 16, BF16, KV8, HW>(a, gp, wpc, st, ev);
+    if (bs == 32) return split_g<D, 32, BF16, KV8, HW>(a, gp, wpc, st, ev);
     return hipErrorInvalidValue;
 }
 
 template <int D>
-static hipError_t split_t(const DecodeArgs* a, int bs, int gp, KvKind kind, int* wpc, hipStream_t st) {
+static hipError_t split_t(const DecodeArgs* a, int bs, int gp, KvKind kind, int* wpc, hipStream_t st,
+                          const LaunchEvents* ev) {
     switch (kind) {
-        case KvKind::F16: return split_b<D, false, false, 1>(a, bs, gp, wpc, st);
-        case KvKind::BF16: return split_b<D, true, false, 1>(a, bs, gp, wpc, st);
-        case KvKind::FP8_BF16Q: return split_b<D, true, true, 1>(a, bs, gp, wpc, st);
-        case KvKind::FP8_BF16Q_PAIR: return split_b<D, true, true, 2>(a, bs, gp, wpc, st);
+        case KvKind::F16: return split_b<D, false, false, 1>(a, bs, gp, wpc, st, ev);
+        case KvKind::BF16: return split_b<D, true, false, 1>(a, bs, gp, wpc, st, ev);
+        case KvKind::FP8_BF16Q: return split_b<D, true, true, 1>(a, bs, gp, wpc, st, ev);
+        case KvKind::FP8_BF16Q_PAIR: return split_b<D, true, true, 2>(a, bs, gp, wpc, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
-static hipError_t split_any(const DecodeArgs* a, int head_dim, int bs, int gp, KvKind kind, int* wpc, hipStream_t st) {
-    if (head_dim == 128) return split_t<128>(a, bs, gp, kind, wpc, st);
-    if (head_dim == 64) return split_t<64>(a, bs, gp, kind, wpc, st);
+static hipError_t split_any(const DecodeArgs* a, int head_dim, int bs, int gp, KvKind kind, int* wpc, hipStream_t st,
+                            const LaunchEvents* ev) {
+    if (head_dim == 128) return split_t<128>(a, bs, gp, kind, wpc, st, ev);
+    if (head_dim == 64) return split_t<64>(a, bs, gp, kind, wpc, st, ev);
     return hipErrorInvalidValue;
 }
 
 hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu) {
-    return split_any(nullptr, head_dim, block_size, group_pad, kind, waves_per_cu, nullptr);
+    return split_any(nullptr, head_dim, block_size, group_pad, kind, waves_per_cu, nullptr, nullptr);
 }
 
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     if (a.num_waves < kWaves || a.num_waves % kWaves) return hipErrorInvalidValue;
     const bool pair = kind == KvKind::FP8_BF16Q_PAIR;
     if ((kind == KvKind::FP8_BF16Q || pair) && (!a.k_scale || !a.v_scale)) return hipErrorInvalidValue;
     if (a.heads_per_wave != (pair ? 2 : 1) || a.num_kv_heads % a.heads_per_wave) return hipErrorInvalidValue;
-    return split_any(&a, head_dim, block_size, group_pad, kind, nullptr, stream);
+    const LaunchEvents ev{start, stop};
+    return split_any(&a, head_dim, block_size, group_pad, kind, nullptr, stream, &ev);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

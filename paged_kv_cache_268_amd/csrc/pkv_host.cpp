@@ -93,6 +93,7 @@ struct pkv_pool {
     Slot ring[kRing];
     int next = 0;
     bool ring_ready = false;
+    std::vector<pkv::AppendItem> stage;          // kv_append items before they go to the kernel
 
     int32_t* tab_host = nullptr;                 // staging for kv_write_tables
     hipEvent_t tab_ev = nullptr;
@@ -471,19 +472,36 @@ int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new,
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return fail(PKV_EINVAL, "kv_append: k_new / v_new must be 16-byte aligned");
     if (n < 0 || n > p->d.max_seqs) return fail(PKV_EINVAL, "kv_append: n = %d", n);
+    // Up to kArgItems items without copy-on-write travel in the kernel
+    // arguments: nothing on the device reads host memory and the call needs no
+    // staging slot (and no event to guard one).  Otherwise the items go through
+    // the pinned ring.
     int rc = ensure_ring(p);
     if (rc) return rc;
     auto& slot = p->ring[p->next];
-    if (slot.pending) {
+    const bool small = n <= pkv::kArgItems;
+    if (!small && slot.pending) {
         hipError_t e = hipEventSynchronize(slot.ev);
         if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (append staging)");
         slot.pending = false;
     }
+    if (p->stage.size() < (size_t)n) p->stage.resize((size_t)p->d.max_seqs);
+    pkv::AppendItem* items = small ? p->stage.data() : slot.host;
     bool any_copy = false;
-    rc = reserve_impl(p, n, seq_ids, slot.host, &any_copy);
+    rc = reserve_impl(p, n, seq_ids, items, &any_copy);
     if (rc) return rc;
+    const bool staged = !small || any_copy;   // the device reads the items from the ring slot
+    if (staged && small) {
+        if (slot.pending) {
+            hipError_t e = hipEventSynchronize(slot.ev);
+            if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (append staging; pool state now ahead of the device)");
+            slot.pending = false;
+        }
+        std::memcpy(slot.host, items, sizeof(pkv::AppendItem) * (size_t)n);
+        items = slot.host;
+    }
     pkv::AppendArgs a{};
-    a.items = slot.host;
+    a.items = staged ? slot.host : nullptr;
     a.k_new = k_new;
     a.v_new = v_new;
     a.k_cache = p->k_cache;
@@ -501,16 +519,16 @@ int kv_append(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new,
     a.k_init = p->k_init;
     a.v_init = p->v_init;
     pkv::ArgItems inl;
-    const bool small = n <= pkv::kArgItems;
     if (small)
-        for (int32_t i = 0; i < n; ++i)
-            inl.it[i] = {slot.host[i].seq, slot.host[i].slot, slot.host[i].new_block, slot.host[i].new_len};
+        for (int32_t i = 0; i < n; ++i) inl.it[i] = {items[i].seq, items[i].slot, items[i].new_block, items[i].new_len};
     hipError_t e = pkv::launch_append(a, any_copy, small ? &inl : nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "kv_append launch (pool state now ahead of the device)");
-    e = hipEventRecord(slot.ev, (hipStream_t)stream);
-    if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
-    slot.pending = true;
-    p->next = (p->next + 1) % kRing;
+    if (staged) {
+        e = hipEventRecord(slot.ev, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+        slot.pending = true;
+        p->next = (p->next + 1) % kRing;
+    }
     return PKV_OK;
 }
 
@@ -1166,7 +1184,8 @@ size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
 static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
                          const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, pkv_stream_t stream, bool fp8_call) {
+                         size_t workspace_bytes, pkv_stream_t stream, bool fp8_call, pkv_event_t start = nullptr,
+                         pkv_event_t stop = nullptr) {
     Plan pl;
     int rc = resolve(d, &pl);
     if (rc) return rc;
@@ -1208,9 +1227,21 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
     a.heads_per_wave = pl.heads_per_wave;
-    hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.kind, (hipStream_t)stream);
+    hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.kind, (hipStream_t)stream,
+                                     (hipEvent_t)start, (hipEvent_t)stop);
     if (e != hipSuccess) return fail_hip(e, "split kernel launch");
     return PKV_OK;
+}
+
+int paged_attn_decode_partials_timed(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                                     const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                     const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, pkv_event_t start, pkv_event_t stop,
+                                     pkv_stream_t stream) {
+    if (!d) return fail(PKV_EINVAL, "null descriptor");
+    if (!start || !stop) return fail(PKV_EINVAL, "paged_attn_decode_partials_timed: null start or stop event");
+    return partials_impl(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out, lse,
+                         workspace, workspace_bytes, stream, d->kv_dtype == PKV_FP8_E4M3, start, stop);
 }
 
 int paged_attn_decode_partials(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,

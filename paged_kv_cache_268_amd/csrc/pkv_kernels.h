@@ -63,8 +63,10 @@ struct MergeArgs {
 };
 
 
+// start / stop: null, or events that take the split dispatch's own start and
+// end timestamps (hipExtLaunchKernel; no marker packets join the stream).
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
-                        hipStream_t stream);
+                        hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Resident waves per CU of the split kernel instance (occupancy query).
 hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

@@ -28,7 +28,7 @@ EXPORTS = (
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
     "paged_attn_decode_noalloc", "paged_attn_decode_launches", "pkv_read_probe",
-    "kv_block_pool_attach_host_tier_fp8",
+    "kv_block_pool_attach_host_tier_fp8", "paged_attn_decode_partials_timed",
 )
 
 
@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH):
                                   ctypes.c_int),
         "paged_attn_decode_partials_fp8": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, ctypes.c_float, P, P, P,
                                             SZ, P], ctypes.c_int),
+        "paged_attn_decode_partials_timed": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, ctypes.c_float, P, P,
+                                              P, SZ, P, P, P], ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_decode_launches": ([ctypes.POINTER(AttnDesc)], I32),
@@ -260,6 +262,68 @@ def decode_partials(desc, q, k_cache, v_cache, block_tables, context_lens, scale
                                             _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale),
                                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                             _stream(stream)))
+
+
+def decode_partials_timed(desc, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, out, lse,
+                          workspace, start, stop, stream=None):
+    """paged_attn_decode_partials_timed: start / stop are LaunchEvents stamped by the split dispatch itself
+    (k_scale = v_scale = None for 16-bit K/V)."""
+    check(load().paged_attn_decode_partials_timed(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                                  _ptr(context_lens), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                                  _ptr(workspace), workspace.numel(), start.handle, stop.handle,
+                                                  _stream(stream)))
+
+
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (the one libpkv.so and torch are linked against)."""
+    global _hip
+    if _hip is None:
+        load()
+        path = "libamdhip64.so"
+        with open("/proc/self/maps") as f:
+            for line in f:
+                name = line.split()[-1]
+                if os.path.basename(name).startswith("libamdhip64.so"):
+                    path = name
+                    break
+        h = ctypes.CDLL(path)
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class LaunchEvent:
+    """A HIP event with timing, created on the current device, for paged_attn_decode_partials_timed."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        rc = _hip_runtime().hipEventCreate(ctypes.byref(self.handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed (hipError {rc})")
+
+    def elapsed_ms(self, stop: "LaunchEvent") -> float:
+        """Milliseconds from this event to stop (waits for stop)."""
+        h = _hip_runtime()
+        rc = h.hipEventSynchronize(stop.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventSynchronize failed (hipError {rc})")
+        t = ctypes.c_float()
+        rc = h.hipEventElapsedTime(ctypes.byref(t), self.handle, stop.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed (hipError {rc})")
+        return float(t.value)
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
+            self.handle = ctypes.c_void_p()
 
 
 def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale: float,

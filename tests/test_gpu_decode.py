@@ -288,6 +288,41 @@ def test_workspace_reused_across_descriptors():
         compare(out, lse, ref_out, ref_lse, what=f"reuse {i}")
 
 
+@pytest.mark.parametrize("kv8", [False, True])
+def test_timed_partials_match_untimed(kv8):
+    """paged_attn_decode_partials_timed writes the same outputs and workspace, bit for bit, as the
+    untimed split (16-bit and 8-bit K/V), and its dispatch-stamped events give a positive duration."""
+    wl = small(B=6, Hq=8, Hkv=2, ctx=(5, 700, 1024, 1500, 0, 33), seed=41)
+    note(f"timed split vs untimed, 8-bit={kv8}")
+    tab, ctx = to_dev(wl)
+    if kv8:
+        q = W.fill_normal_(torch.empty((6, 8, 128), dtype=torch.bfloat16, device=DEV), 42)
+        k, v, ks, vs = W.make_fp8_cache(wl, DEV, poison=True)
+    else:
+        q, k, v = W.make_values(wl, DEV, poison=True)
+        ks = vs = None
+    desc = pkv.desc_for(q, k, tab, wl.max_context_len, 0, num_waves=8)
+    results = []
+    for timed in (False, True):
+        ws = pkv.alloc_workspace(desc, DEV)
+        ws.zero_()
+        out = torch.zeros(q.shape, device=DEV)
+        lse = torch.zeros(q.shape[:2], device=DEV)
+        if timed:
+            e0, e1 = pkv.LaunchEvent(), pkv.LaunchEvent()
+            pkv.decode_partials_timed(desc, q, k, v, ks, vs, tab, ctx, wl.scale, out, lse, ws, e0, e1)
+            assert e0.elapsed_ms(e1) > 0
+        elif kv8:
+            pkv.decode_partials_fp8(desc, q, k, v, ks, vs, tab, ctx, wl.scale, out, lse, ws)
+        else:
+            pkv.decode_partials(desc, q, k, v, tab, ctx, wl.scale, out, lse, ws)
+        torch.cuda.synchronize()
+        results.append((out.cpu(), lse.cpu(), ws.cpu()))
+    for a, b in zip(*results):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b)
+
+
 @pytest.mark.parametrize("P,nw", [(256, 0), (0, 8), (0, 16), (512, 4)])
 def test_segments_are_the_plan(P, nw):
     """Each segment's output in the workspace (the row of its chunk and pair) equals the oracle on

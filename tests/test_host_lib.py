@@ -457,3 +457,15 @@ def test_noalloc_refuses_a_workspace_beyond_the_scratch():
     rc = lib.paged_attn_decode_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, ctypes.c_float(1.0), fake,
                                        None, None)
     assert rc == pkv.PKV_EWORKSPACE and "scratch" in pkv.last_error()
+
+
+def test_timed_partials_need_both_events():
+    """paged_attn_decode_partials_timed refuses a null start or stop event (PKV_EINVAL) before
+    anything is enqueued."""
+    d = pkv.attn_desc(4, 32, 8, 128, 16, 64, 64, 1024, 0, num_waves=64)
+    lib = pkv.load()
+    fake = ctypes.c_void_p(1 << 20)
+    for start, stop in ((None, fake), (fake, None), (None, None)):
+        rc = lib.paged_attn_decode_partials_timed(ctypes.byref(d), fake, fake, fake, None, None, fake, fake,
+                                                  ctypes.c_float(1.0), fake, None, fake, 1 << 20, start, stop, None)
+        assert rc == pkv.PKV_EINVAL and "event" in pkv.last_error()
