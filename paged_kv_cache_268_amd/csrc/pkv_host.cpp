@@ -1370,9 +1370,14 @@ int paged_attn_prefill(const pkv_prefill_desc* d, const void* q, const void* k_c
         !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4) || !aligned(out, out_kind == pkv::kOutF32 ? 16 : 8) ||
         (lse && !aligned(lse, 4)))
         return fail(PKV_EINVAL, "paged_attn_prefill: misaligned pointer (q, caches 16 bytes; out 16 (fp32) or 8)");
-    // Query tiles: sum over s of ceil(m_s / 64) <= total_q / 64 + num_seqs.
-    const int64_t tiles = ceil_div(d->total_q, pkv::kPrefillQ) + d->num_seqs;
-    if (tiles * d->num_q_heads > 0x7FFFFFFF) return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: grid too large");
+    // A workgroup takes Qt = 256 / G chunk queries of one kv head's G q heads.
+    // Query tiles: sum over s of ceil(m_s / Qt) <= total_q / Qt + num_seqs.
+    const int32_t qtile = pkv::prefill_query_tile(d->num_q_heads / d->num_kv_heads);
+    if (qtile == 0)
+        return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: group of %d q heads per kv head (at most %d)",
+                    d->num_q_heads / d->num_kv_heads, pkv::kPrefillRows);
+    const int64_t tiles = ceil_div(d->total_q, qtile) + d->num_seqs;
+    if (tiles * d->num_kv_heads > 0x7FFFFFFF) return fail(PKV_EUNSUPPORTED, "paged_attn_prefill: grid too large");
     pkv::PrefillArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -1390,6 +1395,7 @@ int paged_attn_prefill(const pkv_prefill_desc* d, const void* q, const void* k_c
     a.total_q = d->total_q;
     a.max_context_len = d->max_context_len;
     a.out_dtype = out_kind;
+    a.query_tile = qtile;
     a.grid_tiles = (int32_t)tiles;
     hipError_t e = pkv::launch_prefill(a, d->head_dim, d->block_size, d->q_dtype == PKV_BF16, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "prefill kernel launch");

@@ -7,8 +7,15 @@
 
 namespace pkv {
 
-constexpr int kPrefillQ = 64;        // chunk queries per workgroup (16 per wave)
+// A workgroup of kPrefillWaves waves covers kPrefillRows (chunk query, q head)
+// rows of one kv head (32 per wave): kPrefillRows / G consecutive chunk
+// queries times the G q heads of the group.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = 32 * kPrefillWaves;
 constexpr int kPrefillMaxSeqs = 4096;
+
+// Chunk queries per workgroup for a kv group of G q heads (0 when G is too large).
+inline int prefill_query_tile(int group) { return group >= 1 && group <= kPrefillRows ? kPrefillRows / group : 0; }
 
 struct PrefillArgs {
     const void* q;                   // [total_q][Hq][D]
@@ -27,7 +34,8 @@ struct PrefillArgs {
     int32_t total_q;
     int32_t max_context_len;
     int32_t out_dtype;               // kOut* of pkv_kernels.h
-    int32_t grid_tiles;              // query tiles the grid covers (>= sum over s of ceil(m_s / 64))
+    int32_t query_tile;              // chunk queries per workgroup: prefill_query_tile(Hq / Hkv)
+    int32_t grid_tiles;              // query tiles the grid covers (>= sum over s of ceil(m_s / query_tile))
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, hipStream_t stream);

@@ -8,36 +8,46 @@
 // positions 0 .. n - m + i (causal); scores are q.k times the scale, softmax
 // is the stable form, sums are fp32.  A query head h uses kv head h / (Hq/Hkv).
 //
-// Work decomposition.  One 256-thread workgroup (4 wave64) per (64-query tile
-// of a chunk, q head); wave w owns 16 queries.  The workgroup walks 32-key
-// tiles from position 0 to its last query's position.  Each K/V tile is read
-// once per workgroup (16-byte loads through the block table) into LDS, double
-// buffered, with the loads issued two tiles ahead (two register stages).
-// K sits row-major (rows padded by 16 bytes), V transposed ([d][key], rows
-// padded to 72 bytes).  Waves 2-3 load K (four 16-byte pieces per thread);
-// waves 0-1 load V as units of 4 consecutive keys x 8 d values and store, for
-// each d, the 4 keys as one 8-byte word: with 18-dword rows those stores hit
-// every LDS bank once per half wave (2-byte stores of a transposed row would
-// conflict 8- to 16-fold).  Keys at or past the context end are written as
-// zeros, never loaded.
+// Work decomposition.  The G q heads of one kv head share every K/V tile, so a
+// workgroup takes one kv head g and kPrefillRows = 128 rows (chunk query,
+// q head): Qt = 128 / G consecutive chunk queries times the G heads of the
+// group, row r = (query r / G, head g G + r % G).  Four waves of 32 rows each
+// (two 16-row column blocks per wave, so every K or V operand a wave reads
+// from LDS feeds two (QK) or four (PV, hi and lo weights) matrix
+// instructions); two workgroups per CU, so the two waves on a SIMD belong to
+// different workgroups and do not wait at each other's barriers.  The
+// workgroup walks 32-key tiles from position 0 to its last query's position;
+// each tile is read once per workgroup from the pool (16-byte loads through
+// the block table, block ids by scalar loads) into LDS, double buffered, with
+// the loads issued two tiles ahead (two register stages).  Workgroup i covers
+// kv head i / tiles, so consecutive workgroups (one XCD, one L2) read the
+// same kv head's blocks.
+//
+// LDS layout.  K rows are 2D + 16 bytes apart and stored in a key order that
+// puts the 16 keys of each A operand in consecutive rows: LDS row 16 h + 4 a + i
+// holds key 8 a + 4 h + i (a, i < 4, h < 2).  V is stored transposed, one row
+// of 32 keys (+16 bytes) per d, written by units of 2 keys x 8 d (two 16-byte
+// loads, each d's 2 keys stored as one 32-bit word).  Rows past the context
+// end: K as loaded (those scores are masked before use), V zeroed.
 //
 // Both contractions run on v_mfma_f32_16x16x32 (bf16 or f16 inputs, fp32
 // accumulation):
-//   S^T = K Q^T: A = 16 keys x 32 d from LDS, B = the wave's 16 queries x 32 d
-//   held in registers; two 16-key halves per tile.  Lane l receives the scores
-//   of keys 4(l/16) + r and 16 + 4(l/16) + r (r = 0..3) for query l % 16.
-//   O^T += V^T P^T: those 8 weights are already lane l's B operand (query
-//   l % 16, 8 keys), and the A operand is the same 8 keys of one d row of the
-//   transposed V tile (two 8-byte LDS reads), D/16 output blocks.
-// Softmax per query column: a reference max that moves only when a score
-// exceeds it by more than 8 (log2 units), so the accumulator rescale is a rare
-// event (skipped for the whole wave when no column needs it) and every weight
-// stays <= 2^8.  The weights enter the second product as a bf16 (f16) pair hi + lo with
-// hi = round(p) and lo = round(p - hi), two MFMAs per block: one rounded
-// 16-bit weight carries up to 2^-9 relative error, which is too coarse for
-// outputs checked to 2e-3; the pair carries about 2^-17.  The running max,
-// the rescale and the weight sum stay in fp32 per query column (reduced over
-// the 4 lanes of a column with permlane swaps).
+//   S^T = K Q^T: A = 16 keys x 32 d from LDS (half h: LDS rows 16 h ..
+//   16 h + 15), B = 16 rows x 32 d of the queries, held in registers.  Lane l
+//   receives, for row l % 16, the scores of keys 8 (l / 16) + 4 h + i
+//   (i = 0..3): with both halves, 8 consecutive keys.
+//   O^T += V^T P^T: those 8 weights are exactly lane l's B operand (8 keys of
+//   row l % 16), and the A operand is one 16-byte LDS read: the same 8 keys
+//   of one transposed V row.  D/16 output blocks of 16 d.
+// Softmax per row: a reference max that moves only when a score exceeds it by
+// more than 8 (log2 units), so the accumulator rescale is a rare event
+// (skipped for the whole wave when no row needs it) and every weight stays
+// <= 2^8.  The weights enter the second product as a bf16 (f16) pair hi + lo
+// with hi = round(p) and lo = round(p - hi), two matrix instructions per
+// block: one rounded 16-bit weight carries up to 2^-9 relative error, too
+// coarse for outputs checked to 2e-3; the pair carries about 2^-17.  The
+// running max, the rescale and the weight sum stay in fp32 per row (reduced
+// over the 4 lanes of a row with permlane swaps).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,13 +57,16 @@
 namespace pkv {
 namespace {
 
-constexpr int kPThreads = 256;
+constexpr int kPWaves = kPrefillWaves;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPBlocks = kPrefillRows / kPWaves / 16;   // 16-row column blocks per wave
 constexpr int kPKeys = 32;                      // keys per tile
 constexpr float kPLog2e = 1.4426950408889634f;
 constexpr float kPLn2 = 0.6931471805599453f;
 constexpr float kPTau = 8.0f;                   // lazy-rescale threshold (log2 units)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes staged as a plain vector value
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 
@@ -84,6 +97,27 @@ __device__ __forceinline__ float psum32(float x) {
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Two weights -> their 16-bit roundings (hi, one packed word) and the
+// roundings of what is left (lo): p = hi + lo to about 2^-17 relative.
+template <bool BF16>
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    if constexpr (BF16) {
+        const b2 h = {(__bf16)p0, (__bf16)p1};
+        const uint32_t w = __builtin_bit_cast(uint32_t, h);
+        const float f0 = __builtin_bit_cast(float, w << 16), f1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        const b2 l = {(__bf16)(p0 - f0), (__bf16)(p1 - f1)};
+        hi = w;
+        lo = __builtin_bit_cast(uint32_t, l);
+    } else {
+        const h2 h = {(_Float16)p0, (_Float16)p1};
+        const h2 l = {(_Float16)(p0 - (float)h.x), (_Float16)(p1 - (float)h.y)};
+        hi = __builtin_bit_cast(uint32_t, h);
+        lo = __builtin_bit_cast(uint32_t, l);
+    }
+}
+
 // Workgroup i runs on XCD i % 8; consecutive logical ids share an XCD (its L2).
 __device__ __forceinline__ int prefill_xcd_remap(int i, int n) {
     const int per = n / kNumXcds;
@@ -94,33 +128,34 @@ __device__ __forceinline__ int prefill_xcd_remap(int i, int n) {
 }  // namespace
 
 template <int D, int BS, bool BF16>
-// Four waves per SIMD (at most 128 VGPRs; 128 used at D = 128, no spills):
-// with the 35.8 KB of LDS per workgroup that is 4 workgroups per CU, each with
-// two tiles' loads in flight.
-__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(PrefillArgs a) {
     using V8 = typename PType<BF16>::v8;
     using E = typename PType<BF16>::e;
     constexpr int KS = D / 32;                    // k-steps of S^T
     constexpr int DB = D / 16;                    // 16-row output blocks of O^T
+    constexpr int NB = kPBlocks;                  // column blocks per wave
     constexpr int KROW = D * 2 + 16;              // bytes per K row in LDS
-    constexpr int VROW = kPKeys * 2 + 8;          // bytes per transposed V row (8-byte aligned)
+    constexpr int VROW = kPKeys * 2 + 16;         // bytes per transposed V row in LDS
     constexpr int KBUF = kPKeys * KROW, VBUF = D * VROW;
     constexpr int CPR = D / 8;                    // 16-byte pieces per K/V row
-    constexpr int HT = kPThreads / 2;             // threads of the K half and of the V half
-    constexpr int KPT = kPKeys * CPR / HT;        // K pieces per K-half thread
-    constexpr int VU = (kPKeys / 4) * CPR;        // V units (4 keys x 8 d) per tile
-    constexpr int VPT = (VU + HT - 1) / HT;       // V units per V-half thread
-    constexpr int SR = KPT > 4 * VPT ? KPT : 4 * VPT;   // staging registers per thread
-    static_assert(KPT * HT == kPKeys * CPR && VU <= VPT * HT, "tile shape");
+    // Staging: every thread loads KPT 16-byte K pieces and one V unit (2 keys x
+    // 8 d, two 16-byte loads) per tile; all threads run the same loads, so the
+    // wait for a tile's loads is exact.  At D = 64 there are half as many V
+    // units as threads and the upper half repeats the lower half's.
+    constexpr int KPT = kPKeys * CPR / kPThreads; // K pieces per thread
+    constexpr int VU = (kPKeys / 2) * CPR;        // V units per tile
+    constexpr int SR = KPT + 2;                   // staging registers per thread
+    static_assert(KPT >= 1 && KPT * kPThreads == kPKeys * CPR && kPThreads % VU == 0, "tile shape");
     constexpr int LDS = 2 * (KBUF + VBUF);
     static_assert(LDS >= (kPrefillMaxSeqs + 1) * 4, "tile prefix fits the tile buffers");
     __shared__ __align__(16) uint8_t s_mem[LDS];
-    __shared__ int s_wsum[kPThreads / 64];
+    __shared__ int s_wsum[kPWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int B = a.num_seqs, Hq = a.num_q_heads;
+    const int B = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+    const int Qt = a.query_tile;
 
     // ---- query tiles per sequence, prefix in LDS (aliases the tile buffers) ----
     int* s_pre = reinterpret_cast<int*>(s_mem);
@@ -130,7 +165,7 @@ paged_prefill_kernel(PrefillArgs a) {
         int v = 0;
         if (s < B) {
             const int m = a.cu_q[s + 1] - a.cu_q[s];
-            v = m > 0 ? (m + kPrefillQ - 1) / kPrefillQ : 0;
+            v = m > 0 ? (m + Qt - 1) / Qt : 0;
         }
         int x = v;
 #pragma unroll
@@ -142,7 +177,7 @@ paged_prefill_kernel(PrefillArgs a) {
         __syncthreads();
         int woff = 0, tot = 0;
 #pragma unroll
-        for (int w = 0; w < kPThreads / 64; ++w) {
+        for (int w = 0; w < kPWaves; ++w) {
             woff += w < wave ? s_wsum[w] : 0;
             tot += s_wsum[w];
         }
@@ -154,9 +189,9 @@ paged_prefill_kernel(PrefillArgs a) {
     __syncthreads();
     const int T = s_pre[B];
     const int lwg = prefill_xcd_remap(blockIdx.x, gridDim.x);
-    const int h = lwg % Hq;
-    const int tl = lwg / Hq;
-    if (tl >= T) return;                           // uniform over the workgroup
+    const int g = lwg / a.grid_tiles;              // kv head: consecutive workgroups share it
+    const int tl = lwg - g * a.grid_tiles;
+    if (g >= Hkv || tl >= T) return;               // uniform over the workgroup
     const int tile = T - 1 - tl;                   // later (longer) tiles first
     int sl = 0, sh = B;                            // pre[sl] <= tile < pre[sh]
     while (sh - sl > 1) {
@@ -167,237 +202,280 @@ paged_prefill_kernel(PrefillArgs a) {
     const int qt = tile - s_pre[s];
     __syncthreads();                               // prefix dead: LDS now holds K/V tiles
 
-    const int Hkv = a.num_kv_heads, G = Hq / Hkv, g = h / G;
     const int n = min(max(a.context_lens[s], 0), a.max_context_len);
     const int q0 = a.cu_q[s];
     const int m = max(a.cu_q[s + 1] - q0, 0);
     const int base_pos = n - m;                    // position of chunk row 0
-    const int qa = qt * kPrefillQ;
-    const int nq = min(kPrefillQ, m - qa);
+    const int qa = qt * Qt;
+    const int nq = min(Qt, m - qa);                // chunk queries of this tile
+    const int rows = nq * G;                       // rows in use (<= 256)
     const int last_pos = base_pos + qa + nq - 1;
     const int NT = last_pos >= 0 ? (last_pos + kPKeys) / kPKeys : 0;
 
     const int col = lane & 15, quad = lane >> 4;
-    const int qi = qa + wave * 16 + col;           // this lane's chunk query (score column)
-    const bool qvalid = qi < m && q0 + qi < a.total_q;
-    const int qpos = base_pos + qi;
-    const float sl2 = a.scale * kPLog2e;
-    // Tiles [0, nomask_tiles) need no causal mask for this wave: all 16 of its
-    // queries are real and the tile's last key precedes its first query.
-    const int wq0 = qa + wave * 16;
-    const bool wave_full = wq0 + 16 <= m && q0 + wq0 + 16 <= a.total_q;
-    const int wave_pos0 = base_pos + wq0;
-    const int nomask_tiles = (wave_full && wave_pos0 >= 0) ? (wave_pos0 + 1) / kPKeys : 0;
-
-    V8 qb[KS];
+    // This lane's rows (one per column block): chunk query, q head, validity, position.
+    int qrow[NB], qhead[NB], qpos[NB];
+    bool qvalid[NB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (qvalid)
-            w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                ((int64_t)(q0 + qi) * Hq + h) * D + 32 * ks + 8 * quad);
-        qb[ks] = __builtin_bit_cast(V8, w);
+    for (int c = 0; c < NB; ++c) {
+        const int r = wave * (16 * NB) + c * 16 + col;
+        const int qi = qa + r / G;
+        qrow[c] = q0 + qi;
+        qhead[c] = g * G + r % G;
+        qvalid[c] = r < rows && q0 + qi < a.total_q;
+        qpos[c] = base_pos + qi;
     }
+    // Scores enter the softmax as s * sl2 (log2 units) with sl2 >= 0: a
+    // negative scale flips the sign of q instead (exact), so the row max of
+    // s * sl2 is the row max of s times sl2.
+    // (At least FLT_MIN: a zero scale then still maps a masked -inf to -inf, and
+    // every real score to a weight of 1 up to 2^-126.)
+    const float sl2 = fmaxf(fabsf(a.scale) * kPLog2e, 1.17549435e-38f);
+    const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
+    // The wave's rows [r0, r1): tiles [0, nomask_tiles) need no causal mask
+    // (all 32 rows real and the tile's last key before the first row's
+    // query), and tiles from wave_tiles on are masked out for every row.
+    const int r0 = wave * (16 * NB), r1 = min(r0 + 16 * NB, rows);
+    int wave_tiles = 0, nomask_tiles = 0;
+    if (r1 > r0) {
+        const int p0 = base_pos + qa + r0 / G, p1 = base_pos + qa + (r1 - 1) / G;
+        wave_tiles = p1 >= 0 ? p1 / kPKeys + 1 : 0;
+        const bool full = r1 == r0 + 16 * NB && q0 + qa + (r1 - 1) / G < a.total_q;
+        nomask_tiles = (full && p0 >= 0) ? (p0 + 1) / kPKeys : 0;
+    }
+    wave_tiles = __builtin_amdgcn_readfirstlane(wave_tiles);
+    nomask_tiles = __builtin_amdgcn_readfirstlane(nomask_tiles);
 
-    const int32_t* table = a.block_tables + (int64_t)s * a.table_stride;
-    const uint4* kg = reinterpret_cast<const uint4*>(a.k_cache);
-    const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache);
+    V8 qb[NB][KS];
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (qvalid[c])
+                w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                    ((int64_t)qrow[c] * Hq + qhead[c]) * D + 32 * ks + 8 * quad);
+            w.x ^= qflip; w.y ^= qflip; w.z ^= qflip; w.w ^= qflip;
+            qb[c][ks] = __builtin_bit_cast(V8, w);
+        }
 
-    // Block ids of a tile (a 32-key tile spans one block of 32 or two of 16):
-    // lane l loads entry (first + (l & 1)) as a vector load one iteration
-    // before the tile's K/V loads need it, so the table read is off the
-    // critical path; read back with v_readlane, so the two block bases are
-    // wave-uniform (scalar registers) and a lane's offset inside a block is
-    // the same for every tile (computed once below).  Keys at or past the
-    // context end are zeros, never loaded; only the last tile checks.
+    // The block table is not written during the kernel: read it through the
+    // constant address space, so the (wave-uniform) entries come in by scalar
+    // loads, which the vector-load counter does not track (a wait for a table
+    // entry is then not a wait for every K/V load issued before it).
+    typedef const __attribute__((address_space(4))) int32_t* ConstTable;
+    const ConstTable table = (ConstTable)(a.block_tables + (int64_t)s * a.table_stride);
+    const u32x4* kg = reinterpret_cast<const u32x4*>(a.k_cache);
+    const u32x4* vg = reinterpret_cast<const u32x4*>(a.v_cache);
+
+    // Block ids of a tile (a 32-key tile spans one block of 32 or two of 16),
+    // read one iteration before the tile's K/V loads need them.  Keys at or
+    // past the context end are zeros, never loaded; only the last tile checks.
     const int last_blk = (n + BS - 1) / BS - 1;
     auto load_ids = [&](int kt) {
-        return table[min((kt * kPKeys) / BS + (lane & 1), last_blk)];
+        const int f = (kt * kPKeys) / BS;
+        return make_int2(table[min(f, last_blk)], BS == kPKeys ? 0 : table[min(f + 1, last_blk)]);
     };
-    const bool k_half = wave >= 2;                 // uniform per wave
-    const int ht = tid & (HT - 1);
-    // K half: piece ht + HT c is key (ht + HT c) / CPR, chunk (ht + HT c) % CPR;
-    // the keys of one c lie in one block (KEYS_PER_C divides the block size).
-    // V half: unit ht + HT c is keys 4 ((ht + HT c) % 8) .. +3, chunk (ht + HT c) / 8.
-    constexpr int KEYS_PER_C = HT / CPR;
-    static_assert(HT % CPR == 0 && BS % KEYS_PER_C == 0, "a K piece group stays inside one block");
-    int koff[KPT], vkey[VPT], voff[VPT];           // offsets in 16-byte units inside a block
+    // K: piece tid + kPThreads c is key (tid + kPThreads c) / CPR, 16-byte
+    // chunk (tid + kPThreads c) % CPR, stored at LDS row 16 h + 4 a + i for key
+    // 8 a + 4 h + i.  V: unit u = tid % VU is keys 2 (u % 16), 2 (u % 16) + 1 of
+    // d chunk u / 16.
+    int kkey[KPT], ksrc[KPT], kdst[KPT];
 #pragma unroll
     for (int c = 0; c < KPT; ++c) {
-        const int piece = ht + HT * c;
-        koff[c] = ((piece / CPR) % BS) * CPR + piece % CPR;
+        const int piece = tid + kPThreads * c, key = piece / CPR;
+        kkey[c] = key;
+        ksrc[c] = (key % BS) * CPR + piece % CPR;
+        kdst[c] = (16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3)) * KROW + (piece % CPR) * 16;
     }
-#pragma unroll
-    for (int c = 0; c < VPT; ++c) {
-        const int u = ht + HT * c;
-        vkey[c] = 4 * (u % 8);
-        voff[c] = (vkey[c] % BS) * CPR + u / 8;
-    }
+    const int vu = tid % VU, vkey = 2 * (vu % 16), vcd = vu / 16;
     const int64_t blk_stride = (int64_t)Hkv * BS * CPR, head_off = (int64_t)g * BS * CPR;
-    auto gload = [&](int kt, int32_t ids, uint4 (&r)[SR]) {
-        const int32_t b0 = __builtin_amdgcn_readlane(ids, 0), b1 = __builtin_amdgcn_readlane(ids, 1);
+    // Loads are unconditional (a key past the context end reads its clamped
+    // block's stale row) and the bits of `keep` say which pieces are real:
+    // the store to LDS zeroes the others, once the loads have arrived.
+    auto gload = [&](int kt, int2 ids, u32x4 (&r)[SR], int& keep) {
+        const int64_t o0 = ids.x * blk_stride + head_off, o1 = ids.y * blk_stride + head_off;   // uniform
         const int t0 = kt * kPKeys;
         const bool full = t0 + kPKeys <= n;        // uniform: every key of the tile is cached
-        if (k_half) {
-            const uint4* p0 = kg + b0 * blk_stride + head_off;
-            const uint4* p1 = kg + b1 * blk_stride + head_off;
+        keep = 0;
 #pragma unroll
-            for (int c = 0; c < KPT; ++c) {
-                const uint4* p = (BS == kPKeys || (c + 1) * KEYS_PER_C <= BS) ? p0 : p1;
-                const int key = (ht + HT * c) / CPR;
-                r[c] = (full || t0 + key < n) ? p[koff[c]] : make_uint4(0, 0, 0, 0);
-            }
-        } else {
-            const uint4* p0 = vg + b0 * blk_stride + head_off;
-            const uint4* p1 = vg + b1 * blk_stride + head_off;
-#pragma unroll
-            for (int c = 0; c < VPT; ++c) {
-                const int u = ht + HT * c;
-                const uint4* p = ((BS == kPKeys || vkey[c] < BS) ? p0 : p1) + voff[c];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    r[4 * c + kk] = (u < VU && (full || t0 + vkey[c] + kk < n)) ? p[kk * CPR] : make_uint4(0, 0, 0, 0);
-            }
+        for (int c = 0; c < KPT; ++c) {
+            const int key = kkey[c];
+            r[c] = kg[(key < BS ? o0 : o1) + ksrc[c]];
+            keep |= (full || t0 + key < n) ? 1 << c : 0;
         }
+        const u32x4* p = vg + (vkey < BS ? o0 : o1) + (vkey % BS) * CPR + vcd;
+        r[KPT] = p[0];
+        r[KPT + 1] = p[CPR];
+        keep |= (full || t0 + vkey < n) ? 1 << KPT : 0;
+        keep |= (full || t0 + vkey + 1 < n) ? 2 << KPT : 0;
+        keep = full ? -1 : keep;
     };
-    auto lstore = [&](int b, const uint4 (&r)[SR]) {
-        if (k_half) {
-            uint8_t* kb = s_mem + b * KBUF;
+    // The piece itself, or zeros (component selects, so the staging arrays stay in registers).
+    auto kept = [](int keep, int c, u32x4 v) {
+        return ((keep >> c) & 1) ? v : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto lstore = [&](int b, const u32x4 (&r)[SR], int keep) {
+        uint8_t* kb = s_mem + b * KBUF;
+        // K rows past the context end stay as loaded: their scores are masked
+        // to -inf before use.  V rows there are zeroed (weight 0 times a stale
+        // NaN would still be NaN); a full tile (keep == -1 in every lane) skips that.
 #pragma unroll
-            for (int c = 0; c < KPT; ++c) {
-                const int piece = ht + HT * c;
-                *reinterpret_cast<uint4*>(kb + (piece / CPR) * KROW + (piece % CPR) * 16) = r[c];
-            }
+        for (int c = 0; c < KPT; ++c) *reinterpret_cast<u32x4*>(kb + kdst[c]) = r[c];
+        uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
+        u32x4 v0 = r[KPT], v1 = r[KPT + 1];
+        if (!__builtin_amdgcn_ballot_w64(keep != -1)) {
         } else {
-            uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
+            v0 = kept(keep, KPT, v0);
+            v1 = kept(keep, KPT + 1, v1);
+        }
+        const uint32_t w0[4] = {v0[0], v0[1], v0[2], v0[3]};
+        const uint32_t w1[4] = {v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-            for (int c = 0; c < VPT; ++c) {
-                const int u = ht + HT * c;
-                if (u >= VU) continue;
-                const int q4 = u % 8, cd = u / 8;
-                const uint32_t w0[4] = {r[4 * c].x, r[4 * c].y, r[4 * c].z, r[4 * c].w};
-                const uint32_t w1[4] = {r[4 * c + 1].x, r[4 * c + 1].y, r[4 * c + 1].z, r[4 * c + 1].w};
-                const uint32_t w2[4] = {r[4 * c + 2].x, r[4 * c + 2].y, r[4 * c + 2].z, r[4 * c + 2].w};
-                const uint32_t w3[4] = {r[4 * c + 3].x, r[4 * c + 3].y, r[4 * c + 3].z, r[4 * c + 3].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // d = 8 cd + 2e from the low halves, 8 cd + 2e + 1 from the high halves
-                    const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u),
-                                                __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
-                    const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u),
-                                                __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
-                    *reinterpret_cast<uint2*>(vb + (cd * 8 + 2 * e) * VROW + q4 * 8) = lo;
-                    *reinterpret_cast<uint2*>(vb + (cd * 8 + 2 * e + 1) * VROW + q4 * 8) = hi;
-                }
-            }
+        for (int e = 0; e < 4; ++e) {
+            // d = 8 cd + 2e from the low halves, 8 cd + 2e + 1 from the high halves: the two keys' values.
+            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e) * VROW + vkey * 2) =
+                __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e + 1) * VROW + vkey * 2) =
+                __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
         }
     };
 
-    f32x4 acc[DB];
+    f32x4 acc[NB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_l = -INFINITY, l_l = 0.f;
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[c][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_l[NB], l_l[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+        m_l[c] = -INFINITY;
+        l_l[c] = 0.f;
+    }
 
     auto compute = [&](int b, int kt) {
         const uint8_t* kb = s_mem + b * KBUF;
         const uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
-        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+        f32x4 sc[NB][2];
+#pragma unroll
+        for (int c = 0; c < NB; ++c) sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const V8 a0 = *reinterpret_cast<const V8*>(kb + col * KROW + (32 * ks + 8 * quad) * 2);
             const V8 a1 = *reinterpret_cast<const V8*>(kb + (16 + col) * KROW + (32 * ks + 8 * quad) * 2);
-            c0 = mma<BF16>(a0, qb[ks], c0);
-            c1 = mma<BF16>(a1, qb[ks], c1);
-        }
-        const int t0 = kt * kPKeys + 4 * quad;
-        float x[8];
-        float mx = -INFINITY;
-        if (kt < nomask_tiles) {
-            // Every key of the tile is at or before every query of the wave.
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[r] = c0[r] * sl2;
-                x[4 + r] = c1[r] * sl2;
-                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[r] = (qvalid && t0 + r <= qpos) ? c0[r] * sl2 : -INFINITY;
-                x[4 + r] = (qvalid && t0 + 16 + r <= qpos) ? c1[r] * sl2 : -INFINITY;
-                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
+            for (int c = 0; c < NB; ++c) {
+                sc[c][0] = mma<BF16>(a0, qb[c][ks], sc[c][0]);
+                sc[c][1] = mma<BF16>(a1, qb[c][ks], sc[c][1]);
             }
         }
-        mx = pmax32(pmax16(mx));                       // column max of this tile
-        const bool need = mx > m_l + kPTau;            // uniform over the column's 4 lanes
-        const float m_new = need ? mx : m_l;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_l - m_new) : 1.f;   // 0 while nothing was seen
-        const float ref = m_new == -INFINITY ? 0.f : m_new;
-        V8 ph, pl;
-        float ps = 0.f;
+        // Lane (col, quad), half h, i: key kt * 32 + 8 quad + 4 h + i, weight j = 4 h + i.
+        // Keys j < lim of the lane's 8 are at or before its row's query
+        // (every key on the tiles before the diagonal).
+        const int t0 = kt * kPKeys + 8 * quad;
+        const bool nomask = kt < nomask_tiles;     // uniform
+        uint4 ph[NB], pl[NB];
+        bool any_need = false;
+        float alpha[NB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - ref);    // <= 2^8; 0 for a masked key
-            ps += p;
-            const E hi = (E)p;
-            ph[i] = hi;
-            pl[i] = (E)(p - (float)hi);
+        for (int c = 0; c < NB; ++c) {
+            float sv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = sc[c][j >> 2][j & 3];
+            if (!nomask) {
+                // Keys past the row's query (and every key of an unused row)
+                // score -inf: weight exp2(-inf) = 0.  Stale K rows past the
+                // context end only ever reach this branch.
+                const int lim = qvalid[c] ? qpos[c] - t0 : -1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sv[j] = j <= lim ? sv[j] : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = pmax32(pmax16(mx));                   // row max of the raw scores of this tile
+            const float mt = mx == -INFINITY ? -INFINITY : mx * sl2;
+            const bool need = mt > m_l[c] + kPTau;     // uniform over the row's 4 lanes
+            const float m_new = need ? mt : m_l[c];
+            alpha[c] = need ? __builtin_amdgcn_exp2f(m_l[c] - m_new) : 1.f;   // 0 while nothing was seen
+            any_need |= need;
+            const float nref = m_new == -INFINITY ? 0.f : -m_new;
+            float pw[8], ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], sl2, nref));   // <= 2^8; 0 for a masked key
+                ps += pw[j];
+            }
+            split_pair<BF16>(pw[0], pw[1], ph[c].x, pl[c].x);
+            split_pair<BF16>(pw[2], pw[3], ph[c].y, pl[c].y);
+            split_pair<BF16>(pw[4], pw[5], ph[c].z, pl[c].z);
+            split_pair<BF16>(pw[6], pw[7], ph[c].w, pl[c].w);
+            l_l[c] = l_l[c] * alpha[c] + ps;
+            m_l[c] = m_new;
         }
-        l_l = l_l * alpha + ps;
-        m_l = m_new;
-        if (__builtin_amdgcn_ballot_w64(need)) {
+        if (__builtin_amdgcn_ballot_w64(any_need)) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            for (int c = 0; c < NB; ++c)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[c][db] *= alpha[c];
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const uint8_t* row = vb + (db * 16 + col) * VROW;
-            const uint2 lo4 = *reinterpret_cast<const uint2*>(row + 8 * quad);        // keys 4 quad + 0..3
-            const uint2 hi4 = *reinterpret_cast<const uint2*>(row + 32 + 8 * quad);   // keys 16 + 4 quad + 0..3
-            const V8 av = __builtin_bit_cast(V8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-            acc[db] = mma<BF16>(av, ph, acc[db]);
-            acc[db] = mma<BF16>(av, pl, acc[db]);
+            const V8 av = *reinterpret_cast<const V8*>(vb + (db * 16 + col) * VROW + 16 * quad);   // keys 8 quad .. +7
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                acc[c][db] = mma<BF16>(av, __builtin_bit_cast(V8, ph[c]), acc[c][db]);
+                acc[c][db] = mma<BF16>(av, __builtin_bit_cast(V8, pl[c]), acc[c][db]);
+            }
         }
     };
 
     // Two register stages: the global loads of tile kt + 2 are issued while
     // tile kt is consumed, and stored to LDS one iteration later, so each
-    // tile's loads have a whole iteration to arrive.  LDS stays double
-    // buffered: the barrier that ends an iteration separates the reads of one
-    // buffer from the next store into it.
-    uint4 st_a[SR], st_b[SR];
-    int32_t ids_next = 0;                          // block ids of the next tile to load
-    if (NT > 0) {
-        gload(0, load_ids(0), st_a);
-        lstore(0, st_a);
-    }
-    if (NT > 1) gload(1, load_ids(1), st_a);       // tile 1 in flight in st_a
-    if (NT > 2) ids_next = load_ids(2);
+    // tile's loads have a whole iteration to arrive.  Every iteration issues
+    // the same loads and stores (past the last tile it reloads the last tile,
+    // a cache hit, and stores it where nothing reads it): the wait before a
+    // store to LDS is then for that tile's loads only, not for the ones just
+    // issued (the vector-load counter is in order, and a path that skips a
+    // load or its store would force a wait for all of them).
+    // LDS stays double buffered: the barrier that ends an iteration separates
+    // the reads of one buffer from the next store into it.  A wave whose rows
+    // are all past a tile's keys only stages and waits.
+    u32x4 st_a[SR], st_b[SR];
+    int keep_a = 0, keep_b = 0;
+    if (NT > 0) {                                  // uniform; rows with no key still get their output below
+    gload(0, load_ids(0), st_a, keep_a);
+    lstore(0, st_a, keep_a);
+    gload(min(1, NT - 1), load_ids(min(1, NT - 1)), st_a, keep_a);   // tile 1 in flight in st_a
+    int2 ids_next = load_ids(min(2, NT - 1));      // block ids of the next tile to load
     __syncthreads();
     // cur holds tile kt + 1's loads in flight; nxt is free.
-    auto step = [&](int kt, uint4 (&cur)[SR], uint4 (&nxt)[SR]) {
-        if (kt + 2 < NT) {
-            gload(kt + 2, ids_next, nxt);
-            if (kt + 3 < NT) ids_next = load_ids(kt + 3);
-        }
-        compute(kt & 1, kt);
-        if (kt + 1 < NT) lstore((kt + 1) & 1, cur);
+    auto step = [&](int kt, u32x4 (&cur)[SR], int& keep_cur, u32x4 (&nxt)[SR], int& keep_nxt) {
+        gload(min(kt + 2, NT - 1), ids_next, nxt, keep_nxt);
+        ids_next = load_ids(min(kt + 3, NT - 1));
+        if (kt < wave_tiles) compute(kt & 1, kt);
+        lstore((kt + 1) & 1, cur, keep_cur);       // past the last tile: a copy nobody reads
         __syncthreads();
     };
+    // Steps in pairs, both unconditional (an odd NT ends with a step that only
+    // stages a copy: no wave computes tile NT), so the staging registers carry
+    // over the loop edge without copies, which would wait for their loads.
     for (int kt = 0; kt < NT; kt += 2) {
-        step(kt, st_a, st_b);
-        if (kt + 1 < NT) step(kt + 1, st_b, st_a);
+        step(kt, st_a, keep_a, st_b, keep_b);
+        step(kt + 1, st_b, keep_b, st_a, keep_a);
+    }
     }
 
-    // ---- finalize: column totals, normalised output, lse ----
-    const float lt = psum32(psum16(l_l));
-    if (qvalid) {
+    // ---- finalize: row totals, normalised output, lse ----
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+        const float lt = psum32(psum16(l_l[c]));
+        if (!qvalid[c]) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int64_t row = (int64_t)(q0 + qi) * Hq + h;
+        const int64_t row = (int64_t)qrow[c] * Hq + qhead[c];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int d0 = db * 16 + 4 * quad;
-            const float o0 = acc[db][0] * inv, o1 = acc[db][1] * inv, o2 = acc[db][2] * inv, o3 = acc[db][3] * inv;
+            const float o0 = acc[c][db][0] * inv, o1 = acc[c][db][1] * inv, o2 = acc[c][db][2] * inv,
+                        o3 = acc[c][db][3] * inv;
             if (a.out_dtype == kOutF32) {
                 *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + row * D + d0) = make_float4(o0, o1, o2, o3);
             } else if (a.out_dtype == kOutBF16) {
@@ -410,13 +488,13 @@ paged_prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<f16x4v*>(reinterpret_cast<_Float16*>(a.out) + row * D + d0) = v;
             }
         }
-        if (a.lse && quad == 0) a.lse[row] = lt > 0.f ? (m_l + __builtin_amdgcn_logf(lt)) * kPLn2 : -INFINITY;
+        if (a.lse && quad == 0) a.lse[row] = lt > 0.f ? (m_l[c] + __builtin_amdgcn_logf(lt)) * kPLn2 : -INFINITY;
     }
 }
 
 template <int D, int BS, bool BF16>
 static hipError_t prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    const int64_t grid = (int64_t)a.grid_tiles * a.num_q_heads;
+    const int64_t grid = (int64_t)a.grid_tiles * a.num_kv_heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((paged_prefill_kernel<D, BS, BF16>), dim3((unsigned)grid), dim3(kPThreads), 0, stream, a);
@@ -424,7 +502,9 @@ static hipError_t prefill_t(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, hipStream_t stream) {
-    if (a.num_seqs > kPrefillMaxSeqs) return hipErrorInvalidValue;
+    if (a.num_seqs > kPrefillMaxSeqs || a.num_kv_heads < 1 || a.num_q_heads % a.num_kv_heads ||
+        a.query_tile != prefill_query_tile(a.num_q_heads / a.num_kv_heads))
+        return hipErrorInvalidValue;
     if (head_dim == 128) {
         if (block_size == 16) return bf16 ? prefill_t<128, 16, true>(a, stream) : prefill_t<128, 16, false>(a, stream);
         if (block_size == 32) return bf16 ? prefill_t<128, 32, true>(a, stream) : prefill_t<128, 32, false>(a, stream);
