@@ -225,13 +225,7 @@ paged_prefill_kernel(PrefillArgs a) {
         qvalid[c] = r < rows && q0 + qi < a.total_q;
         qpos[c] = base_pos + qi;
     }
-    // Scores enter the softmax as s * sl2 (log2 units) with sl2 >= 0: a
-    // negative scale flips the sign of q instead (exact), so the row max of
-    // s * sl2 is the row max of s times sl2.
-    // (At least FLT_MIN: a zero scale then still maps a masked -inf to -inf, and
-    // every real score to a weight of 1 up to 2^-126.)
-    const float sl2 = fmaxf(fabsf(a.scale) * kPLog2e, 1.17549435e-38f);
-    const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
+    const float sl2 = a.scale * kPLog2e;       // scores in log2 units
     // The wave's rows [r0, r1): tiles [0, nomask_tiles) need no causal mask
     // (all 32 rows real and the tile's last key before the first row's
     // query), and tiles from wave_tiles on are masked out for every row.
@@ -255,7 +249,6 @@ paged_prefill_kernel(PrefillArgs a) {
             if (qvalid[c])
                 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
                                                     ((int64_t)qrow[c] * Hq + qhead[c]) * D + 32 * ks + 8 * quad);
-            w.x ^= qflip; w.y ^= qflip; w.z ^= qflip; w.w ^= qflip;
             qb[c][ks] = __builtin_bit_cast(V8, w);
         }
 
@@ -289,6 +282,10 @@ paged_prefill_kernel(PrefillArgs a) {
         kdst[c] = (16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3)) * KROW + (piece % CPR) * 16;
     }
     const int vu = tid % VU, vkey = 2 * (vu % 16), vcd = vu / 16;
+    // Transposed V rows are 16-byte chunks of 8 keys, chunk q of row d stored at
+    // position q ^ ((d >> 3) & 3): the 2-key stores of lanes 8 rows apart then
+    // fall in different banks, and a lane's 8-key read stays one 16-byte chunk.
+    const int voff = ((vkey >> 3) ^ (vcd & 3)) * 16 + (vkey & 7) * 2;
     const int64_t blk_stride = (int64_t)Hkv * BS * CPR, head_off = (int64_t)g * BS * CPR;
     // Loads are unconditional (a key past the context end reads its clamped
     // block's stale row) and the bits of `keep` say which pieces are real:
@@ -334,10 +331,8 @@ paged_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // d = 8 cd + 2e from the low halves, 8 cd + 2e + 1 from the high halves: the two keys' values.
-            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e) * VROW + vkey * 2) =
-                __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e + 1) * VROW + vkey * 2) =
-                __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e) * VROW + voff) = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e + 1) * VROW + voff) = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
         }
     };
 
@@ -381,27 +376,26 @@ paged_prefill_kernel(PrefillArgs a) {
         for (int c = 0; c < NB; ++c) {
             float sv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = sc[c][j >> 2][j & 3];
+            for (int j = 0; j < 8; ++j) sv[j] = sc[c][j >> 2][j & 3] * sl2;   // log2 units
             if (!nomask) {
                 // Keys past the row's query (and every key of an unused row)
-                // score -inf: weight exp2(-inf) = 0.  Stale K rows past the
+                // get -inf: weight exp2(-inf) = 0.  Stale K rows past the
                 // context end only ever reach this branch.
                 const int lim = qvalid[c] ? qpos[c] - t0 : -1;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sv[j] = j <= lim ? sv[j] : -INFINITY;
             }
             float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            mx = pmax32(pmax16(mx));                   // row max of the raw scores of this tile
-            const float mt = mx == -INFINITY ? -INFINITY : mx * sl2;
+            const float mt = pmax32(pmax16(mx));       // row max of this tile
             const bool need = mt > m_l[c] + kPTau;     // uniform over the row's 4 lanes
             const float m_new = need ? mt : m_l[c];
             alpha[c] = need ? __builtin_amdgcn_exp2f(m_l[c] - m_new) : 1.f;   // 0 while nothing was seen
             any_need |= need;
-            const float nref = m_new == -INFINITY ? 0.f : -m_new;
+            const float ref = m_new == -INFINITY ? 0.f : m_new;
             float pw[8], ps = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], sl2, nref));   // <= 2^8; 0 for a masked key
+                pw[j] = __builtin_amdgcn_exp2f(sv[j] - ref);   // <= 2^8; 0 for a masked key
                 ps += pw[j];
             }
             split_pair<BF16>(pw[0], pw[1], ph[c].x, pl[c].x);
@@ -419,7 +413,8 @@ paged_prefill_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const V8 av = *reinterpret_cast<const V8*>(vb + (db * 16 + col) * VROW + 16 * quad);   // keys 8 quad .. +7
+            const int vr = db * 16 + col;
+            const V8 av = *reinterpret_cast<const V8*>(vb + vr * VROW + 16 * (quad ^ ((vr >> 3) & 3)));   // keys 8 quad .. +7
 #pragma unroll
             for (int c = 0; c < NB; ++c) {
                 acc[c][db] = mma<BF16>(av, __builtin_bit_cast(V8, ph[c]), acc[c][db]);
