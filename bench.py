@@ -2,12 +2,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
-A step is one pass of the whole decode hot path over one batch: kv_append of
+A step is one pass of the whole decode hot path over one batch: the append of
 one new token for every sequence (slot reservation, copy-on-write if needed,
-K/V scatter, table and length updates), then paged_attn_decode (the split-K
-partition kernel and the LSE merge kernel).  Inputs are seeded synthetic
-tensors already resident in HBM; contexts grow by one token per step, as in
-real decoding.
+K/V scatter, table and length updates) and the decode over the grown contexts
+(the split-K partition kernel and the LSE merge kernel), as one
+kv_append_decode call: the append runs inside the split kernel.  The same step
+as separate calls (kv_append, paged_attn_decode) is timed after it for
+comparison (`two_call_step`).  Inputs are seeded synthetic tensors already
+resident in HBM; contexts grow by one token per step, as in real decoding.
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the whole step:
 K/V bytes the step's attention must read (each token's K and V once per kv
@@ -34,9 +36,10 @@ HBM_PEAK_GBS = 8000.0
 N_BREAKDOWN = 10   # instrumented steps after the timed loop (append / merge event timings)
 EVENT_EVERY = 4    # timed steps whose split launch carries timing events: every 4th
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_KERNEL = "paged_decode_split_kernel"
+DECODE_KERNEL = "paged_decode_append_split_kernel"   # the step's split launch: append folded in (kv_append_decode)
+PLAIN_KERNEL = "paged_decode_split_kernel"
 # Counter summary of the decode kernel on the default workload, and the sources it was taken on.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_split_kernel.llama3-8b-gqa.hbm_counters.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "paged_decode_append_split_kernel.llama3-8b-gqa.hbm_counters.txt")
 KERNEL_SOURCES = ("paged_kv_cache_268_amd/csrc/pkv_decode.hip", "paged_kv_cache_268_amd/csrc/pkv_kernels.h")
 
 
@@ -382,11 +385,12 @@ def oracle_on(wl, q, k, v, tables, lens, seqs, nthreads):
 PARITY_TOL = 2e-3
 
 
-def parity_check(wl, q, k, v, tables, lens, out_step, fp8_kept, nthreads):
+def parity_check(wl, q, k, v, tables, lens, out_step, fp8_kept, nthreads, fp8_tables=None, fp8_lens=None):
     """The last step's output (the timed path, q's dtype) on four sequences against the oracle,
     within 2e-3 + half an ulp of the output type; and, if the 8-bit leg ran, its fp32 output on
-    the same sequences against the same 16-bit oracle within 2e-3 + the bound derived from the
-    quantiser's half-step error (oracle/fp8_bound.py)."""
+    the same sequences against the 16-bit oracle of the state it decoded (fp8_tables / fp8_lens,
+    else the same state) within 2e-3 + the bound derived from the quantiser's half-step error
+    (oracle/fp8_bound.py)."""
     B = wl.num_seqs
     seqs = sorted({0, 1, B // 2, B - 1})
     ref, lse = oracle_on(wl, q, k, v, tables, lens, seqs, nthreads)
@@ -402,6 +406,9 @@ def parity_check(wl, q, k, v, tables, lens, out_step, fp8_kept, nthreads):
     }
     if fp8_kept is not None:
         from oracle import fp8_bound as FB
+        if fp8_tables is not None:
+            tables, lens = fp8_tables, fp8_lens
+            ref, lse = oracle_on(wl, q, k, v, tables, lens, seqs, nthreads)
         bound = FB.decode_bound(q[seqs].double().cpu().numpy(), k, v, fp8_kept["k_scale"], fp8_kept["v_scale"],
                                 tables[seqs], lens[seqs], wl.scale, wl.num_kv_heads, ref, lse)
         e8 = np.abs(fp8_kept["out"][seqs].numpy().astype(np.float64) - ref)
@@ -462,7 +469,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     K, Wu = args.steps, args.warmup
-    total_steps = K + Wu + N_BREAKDOWN
+    total_steps = Wu + 2 * K + N_BREAKDOWN   # fused steps, two-call steps, breakdown steps
     grow_blocks = total_steps // 16 + 2
     wl = W.config(args.config, seed=args.seed, extra_table_entries=grow_blocks)
     P = wl.partition_size if args.partition_size is None else args.partition_size
@@ -499,19 +506,26 @@ def main():
     out = torch.empty((B, Hq, D), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
 
-    # The split kernel's duration (the roofline's denominator) comes from two HIP
-    # events that its own dispatch stamps with its start and end
-    # (paged_attn_decode_partials_timed), on every EVENT_EVERY-th timed step.  A
-    # timed dispatch completes with a fence that costs about 10 us of idle GPU
-    # between kernels (measured on a kernel trace: 0 us gaps without events);
-    # on every step that would be 5 % of the step.  Marker events cost the same,
-    # so the append/merge breakdown comes from a separate pass afterwards.
+    # One decode step is one kv_append_decode call: the step's append folded into
+    # the split kernel, then the merge kernel (no merge when a single partition
+    # covers every context).  The split kernel's duration (the roofline's
+    # denominator) comes from two HIP events that its own dispatch stamps with its
+    # start and end, on every EVENT_EVERY-th timed step.  A timed dispatch
+    # completes with a fence that costs about 10 us of idle GPU between kernels
+    # (measured on a kernel trace: 0 us gaps without events); on every step that
+    # would be 5 % of the step.
     ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % EVENT_EVERY == 0 else None for i in range(K)]
-    ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
-
-    # The split kernel, then the merge kernel (one launch when a single partition covers every
-    # context and the split kernel writes every output).
     single = pkv.decode_launches(desc) == 1
+
+    def step(e=None):
+        pool.append_decode(seq_ids, k_new, v_new, tables, lens, desc, q, wl.scale, out, None, ws,
+                           start=e[0] if e else None, stop=e[1] if e else None, stream=stream)
+
+    # The same step as separate calls (kv_append, the plain split kernel, the
+    # merge kernel), timed after the fused steps for comparison; marker events
+    # around each call in a pass of their own give the append / merge breakdown.
+    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % EVENT_EVERY == 0 else None for i in range(K)]
+    ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
     def split(e=None):
         if e:
@@ -520,7 +534,7 @@ def main():
         else:
             pkv.decode_partials(desc, q, k, v, tables, lens, wl.scale, out, None, ws, stream=stream)
 
-    def step(e=None, e4=None):
+    def step2(e=None, e4=None):
         if e4: e4[0].record(stream)
         pool.append(seq_ids, k_new, v_new, tables, lens, stream=stream)
         if e4: e4[1].record(stream)
@@ -541,16 +555,21 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log(f"[bench] timed {K} steps")
+    # The state the last timed step decoded, and that step's output (checked against the
+    # oracle in the CPU-baseline leg; later steps only write rows past these lengths).
     tables_end, lens_end = tables.cpu().numpy(), lens.cpu().numpy()
-    for i in range(N_BREAKDOWN):
-        step(e4=ev4[i])
-    torch.cuda.synchronize()
-    # The state the last step decoded, and that step's output (checked against the oracle in
-    # the CPU-baseline leg).
-    tables_last, lens_last = tables.cpu().numpy(), lens.cpu().numpy()
+    tables_last, lens_last = tables_end, lens_end
     out_last = out.cpu()
-    # Cross-check of the per-launch event timing: back-to-back split-kernel launches
-    # on unchanged inputs between two events, divided by their number.
+    t2 = time.perf_counter()
+    for i in range(K):
+        step2(e=ev2[i])
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for i in range(N_BREAKDOWN):
+        step2(e4=ev4[i])
+    torch.cuda.synchronize()
+    # Cross-check of the plain split kernel's event timing: back-to-back launches on
+    # unchanged inputs between two events, divided by their number.
     N_B2B = 20
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
@@ -559,6 +578,7 @@ def main():
     b1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = b0.elapsed_time(b1) / N_B2B
+    tables_fin, lens_fin = tables.cpu().numpy(), lens.cpu().numpy()     # the state the 8-bit leg decodes
 
     ms_step = (t1 - t0) * 1e3 / K
     # K/V bytes each timed step's attention reads: context after that step's append.
@@ -573,6 +593,10 @@ def main():
     uniq_end = unique_kv_bytes(tables_end, lens_end, bs, tok_bytes)
     uniq_bytes = uniq_end - (K - 1) / 2 * B * tok_bytes
     t_part = [ev[i][0].elapsed_ms(ev[i][1]) for i in range(K) if ev[i]]
+    t_plain = [ev2[i][0].elapsed_ms(ev2[i][1]) for i in range(K) if ev2[i]]
+    ms_step2 = (t3 - t2) * 1e3 / K
+    # The two-call steps run after the fused ones: K more tokens per sequence.
+    kv_bytes2 = float(np.mean([int((ctx0 + Wu + K + i + 1).sum()) * Hkv * D * 2 * 2 for i in range(K)]))
     t_app = [e[0].elapsed_time(e[1]) for e in ev4]
     t_merge = [e[2].elapsed_time(e[3]) for e in ev4]
     part_ms = float(np.mean(t_part))
@@ -605,11 +629,19 @@ def main():
         "unique_kv_bytes_per_step": int(uniq_bytes),
         "kernel_ms": {
             "split": round(part_ms, 4),
+            "split_kernel": DECODE_KERNEL,
             "decode_launches": 1 if single else 2,
-            "kv_append_event_pass": round(float(np.mean(t_app)), 4),
-            "merge_event_pass": None if single else round(float(np.mean(t_merge)), 4),
             "split_timed_launches": f"{len(t_part)} of {K} (events on every {EVENT_EVERY}th timed step)",
             "split_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
+        },
+        "two_call_step": {
+            "calls": "kv_append, paged_attn_decode_partials, paged_attn_merge",
+            "ms_per_step": round(ms_step2, 4),
+            "GBps": round(kv_bytes2 / (ms_step2 * 1e-3) / 1e9, 2),
+            "split_kernel": PLAIN_KERNEL,
+            "split_ms": round(float(np.mean(t_plain)), 4),
+            "kv_append_event_pass": round(float(np.mean(t_app)), 4),
+            "merge_event_pass": None if single else round(float(np.mean(t_merge)), 4),
             "split_back_to_back": round(b2b_ms, 4),
         },
         "roofline": {
@@ -644,7 +676,7 @@ def main():
     elif not args.no_fp8:
         log("[bench] 8-bit K/V: quantise the pool, time the 8-bit decode")
         fp8_kept, res["fp8_kv"] = fp8_leg(wl, q, k, v, tables, lens, max_ctx, K, Wu, dev)
-        res["fp8_kv"]["speedup_vs_16bit_split"] = round(part_ms / res["fp8_kv"]["split_ms"], 3)
+        res["fp8_kv"]["speedup_vs_16bit_split"] = round(float(np.mean(t_plain)) / res["fp8_kv"]["split_ms"], 3)
     if not args.no_read_ceiling:
         log("[bench] streaming-read ceiling")
         res["read_ceiling"] = read_ceiling_leg(dev)
@@ -656,7 +688,8 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         log("[bench] the last step's output against the oracle on four sequences")
-        par = parity_check(wl, q, k, v, tables_last, lens_last, out_last, fp8_kept, oracle.max_threads())
+        par = parity_check(wl, q, k, v, tables_last, lens_last, out_last, fp8_kept, oracle.max_threads(),
+                           fp8_tables=tables_fin, fp8_lens=lens_fin)
         parity_ok = par["parity_ok"] and (par["fp8_vs_16bit_oracle"] is None
                                           or par["fp8_vs_16bit_oracle"]["within_bound"])
         res["parity_max_abs_err"] = round(par.pop("parity_max_abs_err"), 6)

@@ -383,6 +383,34 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
                      float* lse, const void* workspace, size_t workspace_bytes,
                      pkv_stream_t stream);
 
+/* One decode step in one launch (two when the split leaves segments to
+ * merge): kv_append(pool, n, seq_ids, k_new, v_new, block_tables,
+ * context_lens, stream) followed by paged_attn_decode(desc, q, the pool's
+ * k_cache and v_cache, block_tables, context_lens, scale, out, lse, workspace,
+ * workspace_bytes, stream), with the append folded into the split kernel: the
+ * kernel takes the appended sequences' lengths and new table entries from the
+ * call and their new K/V rows from k_new / v_new, and stores what kv_append
+ * stores (rows, lengths, table entries).  Pool state, caches, tables, lengths,
+ * out and lse afterwards are bit for bit those of the two calls (the page's
+ * engine writes the step's K/V into the cache and then runs attention,
+ * "从零开始构建LLM推理引擎：模型执行器深度解析" 5.2; "架构解构：推理引擎的四层抽象",
+ * PagedAttention section).
+ *   16-bit pools only (8-bit pools: PKV_EUNSUPPORTED); the descriptor's kv
+ *   dtype, head_dim, block_size, num_kv_heads must be the pool's and
+ *   table_stride its max_blocks_per_seq; every listed sequence must be below
+ *   desc->num_seqs, and its new length at most desc->max_context_len
+ *   (PKV_EINVAL, nothing enqueued and the pool unchanged).
+ *   Up to 160 appended sequences travel in the kernel arguments; more go
+ *   through kv_append and the plain decode (same results).  Sequences whose
+ *   tail block is shared get their copy-on-write copy in a launch before.
+ *   start / stop: both NULL, or timing events that the split dispatch stamps
+ *   as in paged_attn_decode_partials_timed (the merge is not timed). */
+int kv_append_decode(pkv_pool* pool, int32_t n, const int32_t* seq_ids, const void* k_new,
+                     const void* v_new, int32_t* block_tables, int32_t* context_lens,
+                     const pkv_attn_desc* desc, const void* q, float scale, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, pkv_event_t start, pkv_event_t stop,
+                     pkv_stream_t stream);
+
 /* paged_attn_decode_partials (16-bit K/V: k_scale = v_scale = NULL) or
  * paged_attn_decode_partials_fp8 (8-bit K/V: the scales as there), with the
  * split kernel's duration taken by two events: start and stop (hipEvent_t,

@@ -55,6 +55,9 @@ constexpr int32_t kTokTable = 4;       // publish block_tables[seq][tpos] = slot
 // items_in_args: a.n <= kArgItems and `inl` holds the items (copy-on-write
 // still reads a.items, in the separate copy launch).
 hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream);
+// Only the copy-on-write phase of an append (items in a.items): the fused
+// append + decode writes the rows itself.
+hipError_t launch_append_cow(const AppendArgs& a, hipStream_t stream);
 // Multi-token append: copy-on-write of a.n items of a.items (those with
 // cow_src >= 0) first, then one workgroup per token of `tokens`.
 hipError_t launch_append_tokens(const AppendArgs& a, int32_t n_tokens, const TokenItem* tokens, bool any_copy,

@@ -177,6 +177,12 @@ hipError_t launch_append_tokens(const AppendArgs& a, int32_t n_tokens, const Tok
     return hipGetLastError();
 }
 
+hipError_t launch_append_cow(const AppendArgs& a, hipStream_t stream) {
+    if (a.n == 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_append_cow_kernel, dim3((unsigned)a.n), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, bool any_copy, const ArgItems* inl, hipStream_t stream) {
     if (a.n == 0) return hipSuccess;
     const dim3 grid((unsigned)a.n);

@@ -244,9 +244,10 @@ __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
 // fit, <= 256 VGPRs); the 8-bit ones are held to 168 VGPRs so three fit,
 // which measured about 5 % faster (half the bytes per tile, so more waves
 // keep as many bytes in flight).
-template <int D, int BS, int GP, bool BF16, bool KV8, int HW>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV8 ? (HW == 2 ? 2 : 3) : 1)))
-paged_decode_split_kernel(DecodeArgs a) {
+// FUSE: the same split with the append of the step's new tokens folded in
+// (16-bit K/V, one kv head per wave; see paged_decode_append_split_kernel).
+template <int D, int BS, int GP, bool BF16, bool KV8, int HW, bool FUSE>
+__device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* fit) {
     constexpr int KS = D / 32;            // MFMA k-steps per tile
     constexpr int KL = KV8 ? D / 64 : KS; // K load instructions per tile (16 bytes per lane each)
     constexpr int EPL = D / 16;           // V: values per lane of a row (16 lanes per row)
@@ -256,6 +257,7 @@ paged_decode_split_kernel(DecodeArgs a) {
     static_assert(!KV8 || BF16, "8-bit K/V pair with a bf16 query");
     static_assert(NW == 1 || NW == 2 || NW == 4, "V piece of 4, 8 or 16 bytes");
     static_assert(HW == 1 || HW == 2, "one or two kv heads per wave");
+    static_assert(!FUSE || (!KV8 && HW == 1), "fused append: 16-bit K/V, one kv head per wave");
     using MfmaIn = typename MfmaType<BF16>::vec;
     using VLoad = VPiece<NW>;
     constexpr int DEPTH = 2;              // tiles in flight per wave
@@ -267,6 +269,11 @@ paged_decode_split_kernel(DecodeArgs a) {
     __shared__ int s_pre[kMaxSeqs + 1];
     __shared__ int s_len[kMaxSeqs];       // clamped context lengths, read once per workgroup
     __shared__ int s_wsum[kWaves];
+    // Fused append: item index of each sequence (kNoItem: not appended).
+    constexpr uint8_t kNoItem = 0xFF;
+    static_assert(kFuseItems < kNoItem, "item index fits a byte");
+    __shared__ uint8_t s_item[FUSE ? kMaxSeqs : 1];
+    __shared__ FuseItem s_fit[FUSE ? kFuseItems : 1];   // the items, read from the kernel arguments once
 
     const int lane = threadIdx.x & 63;
     // Wave index as a uniform (scalar) value, so loops stay scalar.
@@ -274,11 +281,32 @@ paged_decode_split_kernel(DecodeArgs a) {
     const int B = a.num_seqs, Hkv = a.num_kv_heads;
     const int HG = Hkv / HW;              // list entries per (sequence, tile): kv heads taken HW at a time
 
+    // The first kThreads context lengths are loaded before anything waits, so
+    // their latency overlaps the fused append's reading of its items.
+    const int len0 = (int)threadIdx.x < B ? a.context_lens[threadIdx.x] : 0;
+    if constexpr (FUSE) {
+        // An appended sequence's length is its item's new length: another
+        // workgroup of this launch may be storing that length (and the new
+        // block's table entry) while this one reads them.
+        for (int s = threadIdx.x; s < B; s += kThreads) s_item[s] = kNoItem;
+        for (int i = threadIdx.x; i < a.n_items; i += kThreads) s_fit[i] = fit[i];
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.n_items; i += kThreads) s_item[s_fit[i].seq] = (uint8_t)i;
+        __syncthreads();
+    }
+    auto len_of = [&](int s) -> int {
+        if constexpr (FUSE) {
+            const int ii = s_item[s];
+            if (ii != kNoItem) return min(max(s_fit[ii].new_len, 0), a.max_context_len);
+        }
+        return min(max(s < kThreads ? len0 : a.context_lens[s], 0), a.max_context_len);
+    };
+
     // ---- prefix of padded tiles over sequences (every workgroup, in LDS) ----
     int running = 0;
     for (int base = 0; base < B; base += kThreads) {
         const int s = base + (int)threadIdx.x;
-        const int n = s < B ? seq_len(a, s) : 0;
+        const int n = s < B ? len_of(s) : 0;
         if (s < B) s_len[s] = n;
         const int v = padded_tiles(len_tiles(n), a.fixed_chunk);
         int x = v;
@@ -311,6 +339,16 @@ paged_decode_split_kernel(DecodeArgs a) {
         // every empty context (no chunk covers it): zeros, lse = -inf.
         for (int i = threadIdx.x; i <= B; i += kThreads) a.ws_hdr[2 + i] = s_pre[i];
         if (threadIdx.x == 0) { a.ws_hdr[0] = T; a.ws_hdr[1] = C; }
+        if constexpr (FUSE) {
+            // What kv_append writes besides the rows: the new lengths and the
+            // table entries of blocks the call opened or copied into.
+            for (int i = threadIdx.x; i < a.n_items; i += kThreads) {
+                const FuseItem it = s_fit[i];
+                a.lens_out[it.seq] = it.new_len;
+                if (it.new_block >= 0)
+                    a.tables_out[(int64_t)it.seq * a.table_stride + (it.new_len - 1) / BS] = it.new_block;
+            }
+        }
         for (int s = 0; s < B; ++s) {
             if (s_pre[s + 1] != s_pre[s]) continue;
             for (int i = threadIdx.x; i < a.num_q_heads * D; i += kThreads)
@@ -490,26 +528,50 @@ paged_decode_split_kernel(DecodeArgs a) {
     // keep: plain loads (the lines stay cached) instead of non-temporal ones.
     // g is the list's head group: kv heads g * HW .. g * HW + HW - 1, whose
     // (block, kv head) pieces are adjacent in memory (BS * D values apart).
-    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[HW * KL], bool keep) {
+    // Fused append: a tile holding a sequence's new token (sub >= 0) reads that
+    // row from the item's k_new / v_new instead of the cache (the cache row is
+    // written by this same position, see new_row_k / new_row_v).
+    const KvElem* knew = reinterpret_cast<const KvElem*>(a.k_new);
+    const KvElem* vnew = reinterpret_cast<const KvElem*>(a.v_new);
+    auto load_k = [&](int j, int g, int32_t blk, uint4 (&kb)[HW * KL], bool keep, int sub) {
         const int64_t base = tile_base(j, g * HW, blk);
 #pragma unroll
         for (int h = 0; h < HW; ++h) {
-            const int64_t hb = base + (int64_t)h * BS * D + k_off;
+            const KvElem* kp = kc + base + (int64_t)h * BS * D + k_off;
+            if constexpr (FUSE) {
+                if (sub >= 0) {                    // uniform: the tile of a new token
+                    if (krow == (sub & 15)) kp = knew + ((int64_t)(sub >> 4) * Hkv + g) * D + kq * 8;
+#pragma unroll
+                    for (int u = 0; u < KL; ++u) kb[h * KL + u] = *reinterpret_cast<const uint4*>(kp + u * 32);
+                    continue;
+                }
+            }
             if (keep) {
 #pragma unroll
-                for (int u = 0; u < KL; ++u) kb[h * KL + u] = *reinterpret_cast<const uint4*>(kc + hb + u * (KV8 ? 64 : 32));
+                for (int u = 0; u < KL; ++u) kb[h * KL + u] = *reinterpret_cast<const uint4*>(kp + u * (KV8 ? 64 : 32));
             } else {
 #pragma unroll
-                for (int u = 0; u < KL; ++u) kb[h * KL + u] = load_once16(kc + hb + u * (KV8 ? 64 : 32));
+                for (int u = 0; u < KL; ++u) kb[h * KL + u] = load_once16(kp + u * (KV8 ? 64 : 32));
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[HW * NI], bool keep) {
+    auto load_v = [&](int j, int g, int32_t blk, VLoad (&vb)[HW * NI], bool keep, int sub) {
         const int64_t base = tile_base(j, g * HW, blk);
 #pragma unroll
         for (int h = 0; h < HW; ++h) {
             const int64_t hb = base + (int64_t)h * BS * D + v_off;
+            if constexpr (FUSE) {
+                if (sub >= 0) {                    // uniform: the tile of a new token
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        const KvElem* vp = vc + hb + i * 4 * D;
+                        if (kq + 4 * i == (sub & 15)) vp = vnew + ((int64_t)(sub >> 4) * Hkv + g) * D + mrow * EPL;
+                        vb[h * NI + i] = load_piece<NW, false>(vp);
+                    }
+                    continue;
+                }
+            }
             if (keep) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) vb[h * NI + i] = load_piece<NW, false>(vc + hb + i * 4 * D);
@@ -519,6 +581,39 @@ paged_decode_split_kernel(DecodeArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // Fused append: the lanes holding the new row write it to its cache slot
+    // once it is in registers (K: the 4 lanes of A-operand row krow; V: the 16
+    // lanes whose i-th load is that row) -- the rows kv_append would write.
+    KvElem* kc_w = reinterpret_cast<KvElem*>(const_cast<void*>(a.k_cache));
+    KvElem* vc_w = reinterpret_cast<KvElem*>(const_cast<void*>(a.v_cache));
+    auto new_row_k = [&](int j, int g, int32_t blk, const uint4 (&kb)[HW * KL], int sub) {
+        if constexpr (FUSE) {
+            if (sub >= 0 && krow == (sub & 15)) {
+                KvElem* kp = kc_w + tile_base(j, g, blk) + k_off;
+#pragma unroll
+                for (int u = 0; u < KL; ++u) *reinterpret_cast<uint4*>(kp + u * 32) = kb[u];
+            }
+        }
+    };
+    auto new_row_v = [&](int j, int g, int32_t blk, const VLoad (&vb)[HW * NI], int sub) {
+        if constexpr (FUSE) {
+            if (sub >= 0) {
+                const int r = sub & 15;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    if (kq + 4 * i == r) {
+                        KvElem* vp = vc_w + tile_base(j, g, blk) + v_off + i * 4 * D;
+                        if constexpr (NW == 4) {
+                            *reinterpret_cast<uint4*>(vp) = make_uint4(vb[i].w[0], vb[i].w[1], vb[i].w[2], vb[i].w[3]);
+                        } else if constexpr (NW == 2) {
+                            *reinterpret_cast<uint2*>(vp) = make_uint2(vb[i].w[0], vb[i].w[1]);
+                        } else {
+                            *reinterpret_cast<uint32_t*>(vp) = vb[i].w[0];
+                        }
+                    }
+            }
+        }
     };
     // The q rows of kv group g of sequence s, as the QK B operand.
     auto load_q = [&](int s, int g, MfmaIn (&qb)[KS]) {
@@ -592,7 +687,10 @@ paged_decode_split_kernel(DecodeArgs a) {
     // V scales.  A new window (every 128 positions of a chunk) waits for its
     // block ids once.  A position that is not processed still loads the
     // chunk's last real tile (see issue_k: a cache hit).
-    struct Win { int sv, g, j, blk; float ks, vs, ks1, vs1; };
+    // sub (fused append): (item << 4) | row when the position's tile holds the
+    // sequence's new token at that row (the row comes from the item's k_new /
+    // v_new, and this position writes it to the cache), else -1.
+    struct Win { int sv, g, j, blk; float ks, vs, ks1, vs1; int sub; };
     auto win_info = [&](int p, int hi) -> Win {
         const int pc = min(p, hi - 1);
         int sl = 0, sh = B;                        // invariant: pre[sl] <= pc < pre[sh]
@@ -610,6 +708,16 @@ paged_decode_split_kernel(DecodeArgs a) {
         w.sv = (p < hi && j < nt) ? sl : ~sl;
         w.blk = a.block_tables[(int64_t)sl * a.table_stride + (w.j * kTile) / BS];
         w.ks = w.vs = w.ks1 = w.vs1 = 1.f;
+        w.sub = -1;
+        if constexpr (FUSE) {
+            const int ii = s_item[sl];
+            if (ii != kNoItem) {
+                const FuseItem it = s_fit[ii];
+                const int tn = it.new_len - 1;     // position of the new token
+                if (it.new_block >= 0 && (w.j * kTile) / BS == tn / BS) w.blk = it.new_block;
+                if (w.j == tn / kTile) w.sub = (ii << 4) | (tn % kTile);
+            }
+        }
         if constexpr (KV8) {
             const int64_t si = (int64_t)w.blk * Hkv + w.g * HW;   // scales of the group's first kv head
             w.ks = a.k_scale[si];
@@ -639,7 +747,7 @@ paged_decode_split_kernel(DecodeArgs a) {
         uint4 kbuf[DEPTH][HW * KL];
         VLoad vbuf[DEPTH][HW * NI];
         MfmaIn qs[DEPTH][KS];
-        int ps[DEPTH], pg[DEPTH], pj[DEPTH], pblk[DEPTH];
+        int ps[DEPTH], pg[DEPTH], pj[DEPTH], pblk[DEPTH], psub[DEPTH];
         bool pkeep[DEPTH];
         float pks[DEPTH], pvs[DEPTH], pks1[DEPTH], pvs1[DEPTH];
         // Slot st takes position x: its K, and its q rows when the slot's
@@ -649,6 +757,7 @@ paged_decode_split_kernel(DecodeArgs a) {
             pg[st] = pick(wlo.g, whi.g, x);
             pj[st] = pick(wlo.j, whi.j, x);
             pblk[st] = pick(wlo.blk, whi.blk, x);
+            psub[st] = FUSE ? pick(wlo.sub, whi.sub, x) : -1;
             pks1[st] = pvs1[st] = 1.f;
             if constexpr (KV8) {
                 pks[st] = pickf(wlo.ks, whi.ks, x);
@@ -664,10 +773,10 @@ paged_decode_split_kernel(DecodeArgs a) {
             // re-read it, use plain loads: that tile stays in the cache and
             // the re-reads hit.
             pkeep[st] = ps[st] < 0 || x == hi - 1;
-            load_k(pj[st], pg[st], pblk[st], kbuf[st], pkeep[st]);
+            load_k(pj[st], pg[st], pblk[st], kbuf[st], pkeep[st], psub[st]);
             if (ps[st] >= 0 && (x < lo + DEPTH || pj[st] < DEPTH)) load_q(ps[st], pg[st], qs[st]);
         };
-        auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st], pkeep[st]); };
+        auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st], pkeep[st], psub[st]); };
 #pragma unroll
         for (int st = 0; st < DEPTH; ++st) {
             issue_k(st, lo + st);
@@ -705,13 +814,40 @@ paged_decode_split_kernel(DecodeArgs a) {
                 }
                 uint2 phi = make_uint2(0u, 0u), plo = make_uint2(0u, 0u);
                 if (live) qk_softmax(j, kbuf[st], qs[st], pks[st], pvs[st], pks1[st], pvs1[st], phi, plo);
+                const int32_t blk_x = pblk[st];    // issue_k below moves the slot on to x + DEPTH
+                const int sub_x = psub[st];
+                if constexpr (FUSE) {
+                    if (live) new_row_k(j, g, blk_x, kbuf[st], sub_x);
+                }
                 issue_k(st, x + DEPTH);
                 if (live) pv(j, vbuf[st], phi, plo);
+                if constexpr (FUSE) {
+                    if (live) new_row_v(j, g, blk_x, vbuf[st], sub_x);
+                }
                 issue_v(st);
                 if (live && (x == hi - 1 || j == seg_nt - 1)) finish_segment();
             }
         }
     }
+}
+
+template <int D, int BS, int GP, bool BF16, bool KV8, int HW>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KV8 ? (HW == 2 ? 2 : 3) : 1)))
+paged_decode_split_kernel(DecodeArgs a) {
+    split_body<D, BS, GP, BF16, KV8, HW, false>(a, nullptr);
+}
+
+// The split with the step's append folded in: a.n_items new tokens (items in
+// the kernel arguments, rows in a.k_new / a.v_new) are part of the contexts
+// this launch decodes, and the launch stores what kv_append stores: each new
+// K/V row (by the wave that reads it), each new length and each table entry
+// of a block the step opened or copied into (by workgroup 0).  Readers in
+// this launch take lengths and those table entries from the items, so the
+// stores race with nothing they use.
+template <int D, int BS, int GP, bool BF16>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+paged_decode_append_split_kernel(DecodeArgs a, FuseItems items) {
+    split_body<D, BS, GP, BF16, false, 1, true>(a, items.it);
 }
 
 // Merge kernel: WPP waves per (sequence, q head) whose (s, g) spans more than
@@ -872,6 +1008,30 @@ static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStre
     return hipGetLastError();
 }
 
+template <int D, int BS, int GP, bool BF16>
+static hipError_t split_append_dispatch(const DecodeArgs& a, const FuseItems& items, hipStream_t stream,
+                                        const LaunchEvents& ev) {
+    auto kern = paged_decode_append_split_kernel<D, BS, GP, BF16>;
+    const dim3 grid((unsigned)(a.num_waves / kWaves));
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a, items);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a, items);
+    return hipGetLastError();
+}
+
+template <int D, int BS, bool BF16>
+static hipError_t split_append_g(const DecodeArgs& a, const FuseItems& items, int gp, hipStream_t st,
+                                 const LaunchEvents& ev) {
+    switch (gp) {
+        case 1: return split_append_dispatch<D, BS, 1, BF16>(a, items, st, ev);
+        case 2: return split_append_dispatch<D, BS, 2, BF16>(a, items, st, ev);
+        case 4: return split_append_dispatch<D, BS, 4, BF16>(a, items, st, ev);
+        case 8: return split_append_dispatch<D, BS, 8, BF16>(a, items, st, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int D, int BS, bool BF16, bool KV8, int HW>
 static hipError_t split_g(const DecodeArgs* a, int gp, int* wpc, hipStream_t st, const LaunchEvents* ev) {
     if constexpr (HW == 1) {
@@ -930,6 +1090,29 @@ hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int g
     if (a.heads_per_wave != (pair ? 2 : 1) || a.num_kv_heads % a.heads_per_wave) return hipErrorInvalidValue;
     const LaunchEvents ev{start, stop};
     return split_any(&a, head_dim, block_size, group_pad, kind, nullptr, stream, &ev);
+}
+
+hipError_t launch_split_append(const DecodeArgs& a, const FuseItems& items, int head_dim, int block_size, int group_pad,
+                               KvKind kind, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (a.num_waves < kWaves || a.num_waves % kWaves || a.heads_per_wave != 1) return hipErrorInvalidValue;
+    if (a.n_items < 0 || a.n_items > kFuseItems || (a.n_items > 0 && (!a.k_new || !a.v_new)) || !a.lens_out ||
+        !a.tables_out || a.num_seqs > kMaxSeqs)
+        return hipErrorInvalidValue;
+    const LaunchEvents ev{start, stop};
+    const bool bf = kind == KvKind::BF16;
+    if (kind != KvKind::BF16 && kind != KvKind::F16) return hipErrorInvalidValue;
+    if (head_dim == 128) {
+        if (block_size == 16) return bf ? split_append_g<128, 16, true>(a, items, group_pad, stream, ev)
+                                        : split_append_g<128, 16, false>(a, items, group_pad, stream, ev);
+        if (block_size == 32) return bf ? split_append_g<128, 32, true>(a, items, group_pad, stream, ev)
+                                        : split_append_g<128, 32, false>(a, items, group_pad, stream, ev);
+    } else if (head_dim == 64) {
+        if (block_size == 16) return bf ? split_append_g<64, 16, true>(a, items, group_pad, stream, ev)
+                                        : split_append_g<64, 16, false>(a, items, group_pad, stream, ev);
+        if (block_size == 32) return bf ? split_append_g<64, 32, true>(a, items, group_pad, stream, ev)
+                                        : split_append_g<64, 32, false>(a, items, group_pad, stream, ev);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

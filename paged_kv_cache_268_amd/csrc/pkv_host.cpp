@@ -1181,6 +1181,39 @@ size_t paged_attn_workspace_bytes(const pkv_attn_desc* d) {
     return pl.ws_bytes;
 }
 
+// Kernel arguments of a split launch for a resolved, checked plan.
+static pkv::DecodeArgs decode_args(const pkv_attn_desc* d, const Plan& pl, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                                   float* lse, void* workspace) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse = lse;
+    a.ws_hdr = reinterpret_cast<int32_t*>(ws);
+    a.ws_out = reinterpret_cast<float*>(ws + pl.hdr_bytes);
+    a.ws_lse = reinterpret_cast<float*>(ws + pl.hdr_bytes + pl.out_bytes);
+    a.scale = scale;
+    a.num_seqs = d->num_seqs;
+    a.num_q_heads = d->num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.table_stride = d->table_stride;
+    a.fixed_chunk = pl.fixed_chunk;
+    a.num_waves = pl.num_waves;
+    a.seg_rows = pl.seg_rows;
+    a.max_context_len = d->max_context_len;
+    a.out_dtype = pl.out_kind;
+    a.heads_per_wave = pl.heads_per_wave;
+    return a;
+}
+
 static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
                          const int32_t* context_lens, float scale, void* out, float* lse, void* workspace,
@@ -1202,31 +1235,8 @@ static int partials_impl(const pkv_attn_desc* d, const void* q, const void* k_ca
     if (rc) return rc;
     rc = check_ptrs(pl, q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes, true);
     if (rc) return rc;
-    char* ws = reinterpret_cast<char*>(workspace);
-    pkv::DecodeArgs a{};
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.k_scale = kv8 ? k_scale : nullptr;
-    a.v_scale = kv8 ? v_scale : nullptr;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = out;
-    a.lse = lse;
-    a.ws_hdr = reinterpret_cast<int32_t*>(ws);
-    a.ws_out = reinterpret_cast<float*>(ws + pl.hdr_bytes);
-    a.ws_lse = reinterpret_cast<float*>(ws + pl.hdr_bytes + pl.out_bytes);
-    a.scale = scale;
-    a.num_seqs = d->num_seqs;
-    a.num_q_heads = d->num_q_heads;
-    a.num_kv_heads = d->num_kv_heads;
-    a.table_stride = d->table_stride;
-    a.fixed_chunk = pl.fixed_chunk;
-    a.num_waves = pl.num_waves;
-    a.seg_rows = pl.seg_rows;
-    a.max_context_len = d->max_context_len;
-    a.out_dtype = pl.out_kind;
-    a.heads_per_wave = pl.heads_per_wave;
+    const pkv::DecodeArgs a = decode_args(d, pl, q, k_cache, v_cache, kv8 ? k_scale : nullptr, kv8 ? v_scale : nullptr,
+                                          block_tables, context_lens, scale, out, lse, workspace);
     hipError_t e = pkv::launch_split(a, d->head_dim, d->block_size, pl.group_pad, pl.kind, (hipStream_t)stream,
                                      (hipEvent_t)start, (hipEvent_t)stop);
     if (e != hipSuccess) return fail_hip(e, "split kernel launch");
@@ -1292,6 +1302,108 @@ int paged_attn_merge(const pkv_attn_desc* d, const int32_t* context_lens, void* 
     hipError_t e = pkv::launch_merge(a, d->head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "merge kernel launch");
     return PKV_OK;
+}
+
+int kv_append_decode(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void* k_new, const void* v_new,
+                     int32_t* block_tables, int32_t* context_lens, const pkv_attn_desc* d, const void* q, float scale,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes, pkv_event_t start,
+                     pkv_event_t stop, pkv_stream_t stream) {
+    if (!p || !d) return fail(PKV_EINVAL, "kv_append_decode: null pool or descriptor");
+    if (p->d.kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_EUNSUPPORTED, "kv_append_decode: 8-bit pools append with kv_append and decode with "
+                                      "paged_attn_decode_fp8");
+    if (d->kv_dtype != p->d.kv_dtype || d->head_dim != p->d.head_dim || d->block_size != p->d.block_size ||
+        d->num_kv_heads != p->d.num_kv_heads || d->table_stride != p->d.max_blocks_per_seq)
+        return fail(PKV_EINVAL, "kv_append_decode: the descriptor's kv dtype, head_dim, block_size, num_kv_heads and "
+                                "table_stride must be the pool's");
+    if (n < 0 || n > p->d.max_seqs || (n > 0 && !seq_ids)) return fail(PKV_EINVAL, "kv_append_decode: bad n or seq_ids");
+    if (n > 0 && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
+        return fail(PKV_EINVAL, "kv_append_decode: k_new / v_new null or not 16-byte aligned");
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(PKV_EINVAL, "kv_append_decode: give both timing events or neither");
+    if (d->num_seqs > p->d.max_seqs) return fail(PKV_EINVAL, "kv_append_decode: num_seqs beyond the pool's rows");
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = seq_ids[i];
+        if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_append_decode: unknown sequence %d", s);
+        if (s >= d->num_seqs)
+            return fail(PKV_EINVAL, "kv_append_decode: sequence %d is not among the %d decoded rows", s, d->num_seqs);
+        if ((int64_t)p->len[s] + 1 > d->max_context_len)
+            return fail(PKV_EINVAL, "kv_append_decode: sequence %d would exceed max_context_len %d", s,
+                        d->max_context_len);
+    }
+    Plan pl;
+    int rc = resolve(d, &pl);
+    if (rc) return rc;
+    if (d->num_seqs == 0) return PKV_OK;
+    rc = resolve_waves(d, &pl);
+    if (rc) return rc;
+    rc = size_workspace(d, &pl);
+    if (rc) return rc;
+    rc = check_ptrs(pl, q, p->k_cache, p->v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes,
+                    true);
+    if (rc) return rc;
+    if (n > pkv::kFuseItems) {
+        // More items than the kernel arguments carry: the same work as two calls.
+        rc = kv_append(p, n, seq_ids, k_new, v_new, block_tables, context_lens, stream);
+        if (rc) return rc;
+        rc = start ? paged_attn_decode_partials_timed(d, q, p->k_cache, p->v_cache, nullptr, nullptr, block_tables,
+                                                      context_lens, scale, out, lse, workspace, workspace_bytes, start,
+                                                      stop, stream)
+                   : paged_attn_decode_partials(d, q, p->k_cache, p->v_cache, block_tables, context_lens, scale, out,
+                                                lse, workspace, workspace_bytes, stream);
+        if (rc) return rc;
+        return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
+    }
+    rc = ensure_ring(p);
+    if (rc) return rc;
+    if (p->stage.size() < (size_t)n) p->stage.resize((size_t)p->d.max_seqs);
+    bool any_copy = false;
+    rc = reserve_impl(p, n, seq_ids, p->stage.data(), &any_copy);
+    if (rc) return rc;
+    pkv::AppendArgs aa{};
+    aa.k_cache = p->k_cache;
+    aa.v_cache = p->v_cache;
+    aa.block_tables = block_tables;
+    aa.context_lens = context_lens;
+    aa.n = n;
+    aa.num_kv_heads = p->d.num_kv_heads;
+    aa.head_dim = p->d.head_dim;
+    aa.block_size = p->d.block_size;
+    aa.table_stride = p->d.max_blocks_per_seq;
+    if (any_copy) {
+        // A copied tail must hold its rows before the decode reads the copy:
+        // the copy-on-write phase runs first, from the pinned ring.
+        auto& slot = p->ring[p->next];
+        if (slot.pending) {
+            hipError_t e = hipEventSynchronize(slot.ev);
+            if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize (append staging; pool state now ahead of the device)");
+            slot.pending = false;
+        }
+        std::memcpy(slot.host, p->stage.data(), sizeof(pkv::AppendItem) * (size_t)n);
+        aa.items = slot.host;
+        hipError_t e = pkv::launch_append_cow(aa, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "copy-on-write launch (pool state now ahead of the device)");
+        e = hipEventRecord(slot.ev, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+        slot.pending = true;
+        p->next = (p->next + 1) % kRing;
+    }
+    pkv::FuseItems fi;
+    for (int32_t i = 0; i < n; ++i) {
+        const pkv::AppendItem& it = p->stage[(size_t)i];
+        fi.it[i] = {it.seq, it.slot, it.new_block, it.new_len};
+    }
+    pkv::DecodeArgs a = decode_args(d, pl, q, p->k_cache, p->v_cache, nullptr, nullptr, block_tables, context_lens,
+                                    scale, out, lse, workspace);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.tables_out = block_tables;
+    a.lens_out = context_lens;
+    a.n_items = n;
+    hipError_t e = pkv::launch_split_append(a, fi, d->head_dim, d->block_size, pl.group_pad, pl.kind,
+                                            (hipStream_t)stream, (hipEvent_t)start, (hipEvent_t)stop);
+    if (e != hipSuccess) return fail_hip(e, "fused append + split launch (pool state now ahead of the device)");
+    return paged_attn_merge(d, context_lens, out, lse, workspace, workspace_bytes, stream);
 }
 
 int paged_attn_decode(const pkv_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,

@@ -42,6 +42,24 @@ struct DecodeArgs {
     int32_t max_context_len;
     int32_t out_dtype;       // kOut*
     int32_t heads_per_wave;  // kv heads a wave takes per tile: 1, or 2 for FP8_BF16Q_PAIR
+    // Fused append (paged_decode_append_split_kernel only): the new rows
+    // [n_items][Hkv][D] and the tables and lengths the kernel updates.
+    const void* k_new;
+    const void* v_new;
+    int32_t* tables_out;     // = block_tables
+    int32_t* lens_out;       // = context_lens
+    int32_t n_items;
+};
+
+// One appended token of a fused append + decode: sequence, cache slot
+// (block * block_size + row), the block the call opened or copied into (-1:
+// none) and the sequence's new length.  Travels in the kernel arguments.
+struct FuseItem {
+    int32_t seq, slot, new_block, new_len;
+};
+constexpr int kFuseItems = 160;
+struct FuseItems {
+    FuseItem it[kFuseItems];
 };
 
 struct MergeArgs {
@@ -67,6 +85,12 @@ struct MergeArgs {
 // end timestamps (hipExtLaunchKernel; no marker packets join the stream).
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The split kernel with the append of a.n_items new tokens (16-bit K/V, one
+// kv head per wave): lengths and tables come from the items for the appended
+// sequences, the new rows from k_new / v_new, and the kernel writes the rows,
+// lengths and table entries that kv_append would have written.
+hipError_t launch_split_append(const DecodeArgs& a, const FuseItems& items, int head_dim, int block_size, int group_pad,
+                               KvKind kind, hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Resident waves per CU of the split kernel instance (occupancy query).
 hipError_t split_waves_per_cu(int head_dim, int block_size, int group_pad, KvKind kind, int* waves_per_cu);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

@@ -131,7 +131,6 @@ template <int D, int BS, bool BF16>
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(PrefillArgs a) {
     using V8 = typename PType<BF16>::v8;
-    using E = typename PType<BF16>::e;
     constexpr int KS = D / 32;                    // k-steps of S^T
     constexpr int DB = D / 16;                    // 16-row output blocks of O^T
     constexpr int NB = kPBlocks;                  // column blocks per wave

@@ -28,7 +28,7 @@ EXPORTS = (
     "paged_attn_decode_partials_fp8", "paged_attn_prefill", "paged_attn_partition_size", "paged_attn_grid_waves", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_merge", "paged_attn_plan",
     "paged_attn_decode_noalloc", "paged_attn_decode_launches", "pkv_read_probe",
-    "kv_block_pool_attach_host_tier_fp8", "paged_attn_decode_partials_timed",
+    "kv_block_pool_attach_host_tier_fp8", "paged_attn_decode_partials_timed", "kv_append_decode",
 )
 
 
@@ -98,6 +98,8 @@ def load(path: str = LIB_PATH):
                                             SZ, P], ctypes.c_int),
         "paged_attn_decode_partials_timed": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                               P, SZ, P, P, P], ctypes.c_int),
+        "kv_append_decode": ([P, I32, P, P, P, P, P, ctypes.POINTER(AttnDesc), P, ctypes.c_float, P, P, P, SZ, P, P, P],
+                             ctypes.c_int),
         "paged_attn_partition_size": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_grid_waves": ([ctypes.POINTER(AttnDesc)], I32),
         "paged_attn_decode_launches": ([ctypes.POINTER(AttnDesc)], I32),
@@ -487,6 +489,17 @@ class BlockPool:
         ids = _i32(seq_ids)
         check(self.lib.kv_append(self.handle, ids.size, ids.ctypes.data if ids.size else None, _ptr(k_new),
                                  _ptr(v_new), _ptr(block_tables), _ptr(context_lens), _stream(stream)))
+
+    def append_decode(self, seq_ids, k_new, v_new, block_tables, context_lens, desc, q, scale, out, lse, workspace,
+                      start=None, stop=None, stream=None):
+        """kv_append_decode: append one token to each listed sequence and decode (16-bit pools); start / stop:
+        LaunchEvents for the split dispatch, or None."""
+        ids = _i32(seq_ids)
+        check(self.lib.kv_append_decode(self.handle, ids.size, ids.ctypes.data if ids.size else None, _ptr(k_new),
+                                        _ptr(v_new), _ptr(block_tables), _ptr(context_lens), ctypes.byref(desc),
+                                        _ptr(q), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel(), start.handle if start else None,
+                                        stop.handle if stop else None, _stream(stream)))
 
     def append_tokens(self, seq_ids, counts, k_new, v_new, block_tables, context_lens, stream=None):
         ids, cnt = _i32(seq_ids), _i32(counts)

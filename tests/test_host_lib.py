@@ -469,3 +469,41 @@ def test_timed_partials_need_both_events():
         rc = lib.paged_attn_decode_partials_timed(ctypes.byref(d), fake, fake, fake, None, None, fake, fake,
                                                   ctypes.c_float(1.0), fake, None, fake, 1 << 20, start, stop, None)
         assert rc == pkv.PKV_EINVAL and "event" in pkv.last_error()
+
+
+def test_append_decode_refusals_leave_the_pool_unchanged():
+    """kv_append_decode checks the pool, the descriptor and every listed sequence before it changes
+    anything: 8-bit pools, a descriptor that is not the pool's, a sequence outside the decoded rows or
+    past max_context_len are refused and the pool still appends as before."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(1 << 20)
+    pool = pkv.BlockPool(16, 16, 2, 64, pkv.PKV_BF16, 4, 8)
+    s0, s1 = pool.add(), pool.add()
+    ids = np.array([s0, s1], dtype=np.int32)
+
+    def call(desc, seq_ids=ids):
+        return lib.kv_append_decode(pool.handle, seq_ids.size, seq_ids.ctypes.data, fake, fake, fake, fake,
+                                    ctypes.byref(desc), fake, ctypes.c_float(1.0), fake, None, fake, 1 << 30,
+                                    None, None, None)
+
+    good = pkv.attn_desc(2, 4, 2, 64, 16, 16, 8, 128, 0, num_waves=8)
+    bad_stride = pkv.attn_desc(2, 4, 2, 64, 16, 16, 9, 128, 0, num_waves=8)
+    bad_dim = pkv.attn_desc(2, 4, 2, 128, 16, 16, 8, 128, 0, num_waves=8)
+    one_row = pkv.attn_desc(1, 4, 2, 64, 16, 16, 8, 128, 0, num_waves=8)
+    no_room = pkv.attn_desc(2, 4, 2, 64, 16, 16, 8, 0, 0, num_waves=8)
+    for d, what in ((bad_stride, "table_stride"), (bad_dim, "head_dim"), (one_row, "decoded rows"),
+                    (no_room, "max_context_len")):
+        assert call(d) == pkv.PKV_EINVAL, what
+        assert what.split()[0] in pkv.last_error() or "pool's" in pkv.last_error(), pkv.last_error()
+    assert call(good, np.array([s0, 3], dtype=np.int32)) == pkv.PKV_EINVAL      # unknown sequence
+    # Nothing was taken: the pool's next append still opens each sequence's first block.
+    items = np.zeros((2, 7), dtype=np.int32)
+    assert lib.kv_reserve(pool.handle, 2, ids.ctypes.data, items.ctypes.data) == pkv.PKV_OK
+    assert list(items[:, 6]) == [1, 1] and all(items[:, 3] >= 0)
+    p8 = pkv.BlockPool(16, 16, 2, 64, pkv.PKV_FP8_E4M3, 4, 8)
+    p8.add()
+    d8 = pkv.attn_desc(1, 4, 2, 64, 16, 16, 8, 128, 0, num_waves=8, dtype=pkv.PKV_BF16, kv_dtype=pkv.PKV_FP8_E4M3)
+    one = np.array([0], dtype=np.int32)
+    rc = lib.kv_append_decode(p8.handle, 1, one.ctypes.data, fake, fake, fake, fake, ctypes.byref(d8), fake,
+                              ctypes.c_float(1.0), fake, None, fake, 1 << 30, None, None, None)
+    assert rc == pkv.PKV_EUNSUPPORTED and "8-bit" in pkv.last_error()
