@@ -34,7 +34,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 N_BREAKDOWN = 10   # instrumented steps after the timed loop (append / merge event timings)
-EVENT_EVERY = 4    # timed steps whose split launch carries timing events: every 4th
+EVENT_SAMPLES = 12  # timed steps whose split launch carries timing events: about this many, evenly spaced
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE_KERNEL = "paged_decode_append_split_kernel"   # the step's split launch: append folded in (kv_append_decode)
 PLAIN_KERNEL = "paged_decode_split_kernel"
@@ -51,7 +51,7 @@ def parse():
     from paged_kv_cache_268_amd.workloads import CONFIG_NAMES
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3,
                     help="decode workload 1..5: " + ", ".join(f"{k} = {v}" for k, v in sorted(CONFIG_NAMES.items())))
@@ -510,11 +510,12 @@ def main():
     # the split kernel, then the merge kernel (no merge when a single partition
     # covers every context).  The split kernel's duration (the roofline's
     # denominator) comes from two HIP events that its own dispatch stamps with its
-    # start and end, on every EVENT_EVERY-th timed step.  A timed dispatch
+    # start and end, on about EVENT_SAMPLES evenly spaced timed steps.  A timed dispatch
     # completes with a fence that costs about 10 us of idle GPU between kernels
     # (measured on a kernel trace: 0 us gaps without events); on every step that
     # would be 5 % of the step.
-    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % EVENT_EVERY == 0 else None for i in range(K)]
+    every = max(1, K // EVENT_SAMPLES)
+    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every == 0 else None for i in range(K)]
     single = pkv.decode_launches(desc) == 1
 
     def step(e=None):
@@ -524,7 +525,7 @@ def main():
     # The same step as separate calls (kv_append, the plain split kernel, the
     # merge kernel), timed after the fused steps for comparison; marker events
     # around each call in a pass of their own give the append / merge breakdown.
-    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % EVENT_EVERY == 0 else None for i in range(K)]
+    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every == 0 else None for i in range(K)]
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
     def split(e=None):
@@ -631,7 +632,7 @@ def main():
             "split": round(part_ms, 4),
             "split_kernel": DECODE_KERNEL,
             "decode_launches": 1 if single else 2,
-            "split_timed_launches": f"{len(t_part)} of {K} (events on every {EVENT_EVERY}th timed step)",
+            "split_timed_launches": f"{len(t_part)} of {K} (events on every {every}th timed step)",
             "split_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
         },
         "two_call_step": {
