@@ -274,6 +274,9 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
     static_assert(kFuseItems < kNoItem, "item index fits a byte");
     __shared__ uint8_t s_item[FUSE ? kMaxSeqs : 1];
     __shared__ FuseItem s_fit[FUSE ? kFuseItems : 1];   // the items, read from the kernel arguments once
+    // Paired halves (a.pair_halves): softmax state exchange, 2 buffers x 2
+    // wave pairs x (4 EPL + 2) floats x 64 lanes, dynamic LDS of the launch.
+    extern __shared__ __align__(16) float xch[];
 
     const int lane = threadIdx.x & 63;
     // Wave index as a uniform (scalar) value, so loops stay scalar.
@@ -729,9 +732,10 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
         }
         return w;
     };
-    const int w_global = lwg * kWaves + wave;
-    for (int ch = w_global; ch < NC; ch += a.num_waves) {
-        const int lo = ch * C, hi = min(lo + C, T);
+    // Positions [lo, hi) of chunk ch through the pipeline.  finish: each
+    // segment ending in the range is written (else the caller combines the
+    // range's softmax state with its partner's first).
+    auto run_range = [&](int ch, int lo, int hi, bool finish) {
         int c0 = lo;
         Win wlo = win_info(c0 + lane, hi);
         Win whi = win_info(c0 + 64 + lane, hi);
@@ -825,8 +829,64 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
                     if (live) new_row_v(j, g, blk_x, vbuf[st], sub_x);
                 }
                 issue_v(st);
-                if (live && (x == hi - 1 || j == seg_nt - 1)) finish_segment();
+                if (finish && live && (x == hi - 1 || j == seg_nt - 1)) finish_segment();
             }
+        }
+    };
+    auto reset_state = [&]() {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+        m_lane = mrow < GC ? -INFINITY : 0.f;
+        l_lane = 0.f;
+    };
+    if (!a.pair_halves) {
+        const int w_global = lwg * kWaves + wave;
+        for (int ch = w_global; ch < NC; ch += a.num_waves) run_range(ch, ch * C, min(ch * C + C, T), true);
+        return;
+    }
+    // Fixed partitions, two waves per chunk: waves 2 q and 2 q + 1 of a
+    // workgroup take the two halves of chunk 2 lwg + q + k NP (NP: wave pairs
+    // in the grid), k = 0, 1, ...  The second half's softmax state goes
+    // through LDS to the first, which merges it into its own and writes the
+    // chunk's one segment (the same segment, row and output as one wave
+    // taking the whole chunk).  Twice as many work units as chunks: a number
+    // of partitions just above the grid's wave count no longer costs a second
+    // full round.  Every wave passes one barrier per k; the exchange buffers
+    // alternate with k, so a second-half wave never overwrites a state its
+    // partner has not read.
+    const int pq = wave >> 1, half = wave & 1;
+    const int NP = a.num_waves >> 1;
+    constexpr int XF = 4 * EPL + 2;                 // floats per lane: acc, m, l
+    for (int k = 0; 2 * lwg + k * NP < NC; ++k) {
+        const int ch = 2 * lwg + pq + k * NP;
+        reset_state();
+        const int mid = ch * C + C / 2;
+        if (ch < NC) run_range(ch, half ? mid : ch * C, half ? min(ch * C + C, T) : min(mid, T), false);
+        float* xb = xch + (size_t)(((k & 1) * 2 + pq) * XF) * 64;   // [field][lane]
+        if (half == 1 && ch < NC) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xb[(4 * e + i) * 64 + lane] = acc[e][i];
+            xb[(4 * EPL) * 64 + lane] = m_lane;
+            xb[(4 * EPL + 1) * 64 + lane] = l_lane;
+        }
+        __syncthreads();
+        if (half == 0 && ch < NC) {
+            const float m1 = xb[(4 * EPL) * 64 + lane], l1 = xb[(4 * EPL + 1) * 64 + lane];
+            const float M = fmaxf(m_lane, m1);
+            // Scale factors of the two halves (a half with no tile of this
+            // chunk has m = -inf, l = 0, acc = 0: factor 0).  Padding heads
+            // (rows >= GC) keep m = 0 in both halves.
+            const float f0 = m_lane == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_lane - M);
+            const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[e][i] = acc[e][i] * f0 + xb[(4 * e + i) * 64 + lane] * f1;
+            l_lane = l_lane * f0 + l1 * f1;
+            m_lane = M;
+            finish_segment();
         }
     }
 }
@@ -1001,10 +1061,11 @@ static hipError_t split_dispatch(const DecodeArgs* a, int* waves_per_cu, hipStre
         return hipSuccess;
     }
     const dim3 grid((unsigned)(a->num_waves / kWaves));
+    const unsigned lds = a->pair_halves ? (unsigned)split_pair_lds_bytes(D) : 0u;
     if (ev && (ev->start || ev->stop))
-        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, ev->start, ev->stop, 0, *a);
+        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, ev->start, ev->stop, 0, *a);
     else
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, *a);
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, *a);
     return hipGetLastError();
 }
 
@@ -1013,10 +1074,11 @@ static hipError_t split_append_dispatch(const DecodeArgs& a, const FuseItems& it
                                         const LaunchEvents& ev) {
     auto kern = paged_decode_append_split_kernel<D, BS, GP, BF16>;
     const dim3 grid((unsigned)(a.num_waves / kWaves));
+    const unsigned lds = a.pair_halves ? (unsigned)split_pair_lds_bytes(D) : 0u;
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a, items);
+        hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, ev.start, ev.stop, 0, a, items);
     else
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a, items);
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a, items);
     return hipGetLastError();
 }
 

@@ -1211,6 +1211,7 @@ static pkv::DecodeArgs decode_args(const pkv_attn_desc* d, const Plan& pl, const
     a.max_context_len = d->max_context_len;
     a.out_dtype = pl.out_kind;
     a.heads_per_wave = pl.heads_per_wave;
+    a.pair_halves = pl.fixed_chunk >= 2 ? 1 : 0;   // fixed partitions: two waves per chunk
     return a;
 }
 

@@ -42,6 +42,7 @@ struct DecodeArgs {
     int32_t max_context_len;
     int32_t out_dtype;       // kOut*
     int32_t heads_per_wave;  // kv heads a wave takes per tile: 1, or 2 for FP8_BF16Q_PAIR
+    int32_t pair_halves;     // fixed partitions of >= 2 tiles: two waves per chunk (split_pair_lds_bytes of LDS)
     // Fused append (paged_decode_append_split_kernel only): the new rows
     // [n_items][Hkv][D] and the tables and lengths the kernel updates.
     const void* k_new;
@@ -83,6 +84,9 @@ struct MergeArgs {
 
 // start / stop: null, or events that take the split dispatch's own start and
 // end timestamps (hipExtLaunchKernel; no marker packets join the stream).
+// Dynamic LDS a split launch with pair_halves needs (the softmax state exchange).
+inline size_t split_pair_lds_bytes(int head_dim) { return (size_t)2 * 2 * (4 * (head_dim / 16) + 2) * 64 * sizeof(float); }
+
 hipError_t launch_split(const DecodeArgs& a, int head_dim, int block_size, int group_pad, KvKind kind,
                         hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // The split kernel with the append of a.n_items new tokens (16-bit K/V, one
