@@ -686,14 +686,14 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
     // keep going.  Position p's tile comes from per-lane windows of 128
     // positions (lane i: p = c0 + i and c0 + 64 + i): its sequence (~s when p
     // is not a tile to process: past the chunk, or padding of a fixed chunk),
-    // kv head, tile index and block id, and with 8-bit K/V the block's K and
-    // V scales.  A new window (every 128 positions of a chunk) waits for its
-    // block ids once.  A position that is not processed still loads the
+    // kv head, tile index and block id (8-bit K/V: the block's scales come
+    // with each tile, see issue_k).  A new window (every 128 positions of a
+    // chunk) waits for its block ids once.  A position that is not processed still loads the
     // chunk's last real tile (see issue_k: a cache hit).
     // sub (fused append): (item << 4) | row when the position's tile holds the
     // sequence's new token at that row (the row comes from the item's k_new /
     // v_new, and this position writes it to the cache), else -1.
-    struct Win { int sv, g, j, blk; float ks, vs, ks1, vs1; int sub; };
+    struct Win { int sv, g, j, blk; int sub; };
     auto win_info = [&](int p, int hi) -> Win {
         const int pc = min(p, hi - 1);
         int sl = 0, sh = B;                        // invariant: pre[sl] <= pc < pre[sh]
@@ -710,7 +710,6 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
         w.j = min(j, nt - 1);
         w.sv = (p < hi && j < nt) ? sl : ~sl;
         w.blk = a.block_tables[(int64_t)sl * a.table_stride + (w.j * kTile) / BS];
-        w.ks = w.vs = w.ks1 = w.vs1 = 1.f;
         w.sub = -1;
         if constexpr (FUSE) {
             const int ii = s_item[sl];
@@ -719,15 +718,6 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
                 const int tn = it.new_len - 1;     // position of the new token
                 if (it.new_block >= 0 && (w.j * kTile) / BS == tn / BS) w.blk = it.new_block;
                 if (w.j == tn / kTile) w.sub = (ii << 4) | (tn % kTile);
-            }
-        }
-        if constexpr (KV8) {
-            const int64_t si = (int64_t)w.blk * Hkv + w.g * HW;   // scales of the group's first kv head
-            w.ks = a.k_scale[si];
-            w.vs = a.v_scale[si];
-            if constexpr (HW == 2) {
-                w.ks1 = a.k_scale[si + 1];
-                w.vs1 = a.v_scale[si + 1];
             }
         }
         return w;
@@ -742,9 +732,6 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
         auto pick = [&](int vlo, int vhi, int x) -> int {
             const int i = x - c0;                  // in [0, 128)
             return i < 64 ? __builtin_amdgcn_readlane(vlo, i) : __builtin_amdgcn_readlane(vhi, i - 64);
-        };
-        auto pickf = [&](float vlo, float vhi, int x) -> float {
-            return __builtin_bit_cast(float, pick(__builtin_bit_cast(int, vlo), __builtin_bit_cast(int, vhi), x));
         };
         // Per pipeline slot: the K, V and q operands of the position it holds,
         // and that position's (~)s, kv head, tile index and scales.
@@ -762,22 +749,26 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
             pj[st] = pick(wlo.j, whi.j, x);
             pblk[st] = pick(wlo.blk, whi.blk, x);
             psub[st] = FUSE ? pick(wlo.sub, whi.sub, x) : -1;
-            pks1[st] = pvs1[st] = 1.f;
-            if constexpr (KV8) {
-                pks[st] = pickf(wlo.ks, whi.ks, x);
-                pvs[st] = pickf(wlo.vs, whi.vs, x);
-                if constexpr (HW == 2) {
-                    pks1[st] = pickf(wlo.ks1, whi.ks1, x);
-                    pvs1[st] = pickf(wlo.vs1, whi.vs1, x);
-                }
-            } else {
-                pks[st] = pvs[st] = 1.f;
-            }
+            pks[st] = pvs[st] = pks1[st] = pvs1[st] = 1.f;
             // The chunk's last real tile, and the positions past it that
             // re-read it, use plain loads: that tile stays in the cache and
             // the re-reads hit.
             pkeep[st] = ps[st] < 0 || x == hi - 1;
             load_k(pj[st], pg[st], pblk[st], kbuf[st], pkeep[st], psub[st]);
+            if constexpr (KV8) {
+                // The tile's K and V scales (one per (block, kv head)), wave-uniform:
+                // scalar loads through the constant address space (the scales are not
+                // written during the kernel), issued after the tile's K loads and first
+                // used at its QK, and never waited on together with the vector loads.
+                typedef const __attribute__((address_space(4))) float* ConstScale;
+                const int64_t si = (int64_t)pblk[st] * Hkv + pg[st] * HW;   // the group's first kv head
+                pks[st] = ((ConstScale)a.k_scale)[si];
+                pvs[st] = ((ConstScale)a.v_scale)[si];
+                if constexpr (HW == 2) {
+                    pks1[st] = ((ConstScale)a.k_scale)[si + 1];
+                    pvs1[st] = ((ConstScale)a.v_scale)[si + 1];
+                }
+            }
             if (ps[st] >= 0 && (x < lo + DEPTH || pj[st] < DEPTH)) load_q(ps[st], pg[st], qs[st]);
         };
         auto issue_v = [&](int st) { load_v(pj[st], pg[st], pblk[st], vbuf[st], pkeep[st], psub[st]); };
