@@ -469,9 +469,21 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     K, Wu = args.steps, args.warmup
-    total_steps = Wu + 2 * K + N_BREAKDOWN   # fused steps, two-call steps, breakdown steps
+    K2 = min(K, 40)                          # two-call comparison steps
+    total_steps = Wu + K + K2 + N_BREAKDOWN   # fused steps, two-call steps, breakdown steps
     grow_blocks = total_steps // 16 + 2
     wl = W.config(args.config, seed=args.seed, extra_table_entries=grow_blocks)
+    # A workload with a fixed pool (the tiny batch's 64 blocks) holds only so many
+    # appended tokens: fewer steps then, stated in the output.
+    def new_blocks(n):
+        c = wl.context_lens.astype(np.int64)
+        return int((-(-(c + n) // wl.block_size) - (-(-c // wl.block_size))).sum())
+    free = wl.num_blocks - int((-(-wl.context_lens.astype(np.int64) // wl.block_size)).sum())
+    while K > 1 and new_blocks(Wu + K + K2 + N_BREAKDOWN) > free:
+        K -= 1
+        K2 = min(K, 40)
+    if K != args.steps:
+        log(f"[bench] the pool holds {free} free blocks: {K} timed steps instead of {args.steps}")
     P = wl.partition_size if args.partition_size is None else args.partition_size
     B, Hq, Hkv, D, bs = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
     log(f"[bench] {wl.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} {wl.dtype} "
@@ -525,7 +537,8 @@ def main():
     # The same step as separate calls (kv_append, the plain split kernel, the
     # merge kernel), timed after the fused steps for comparison; marker events
     # around each call in a pass of their own give the append / merge breakdown.
-    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every == 0 else None for i in range(K)]
+    every2 = max(1, K2 // EVENT_SAMPLES)
+    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every2 == 0 else None for i in range(K2)]
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
     def split(e=None):
@@ -562,7 +575,7 @@ def main():
     tables_last, lens_last = tables_end, lens_end
     out_last = out.cpu()
     t2 = time.perf_counter()
-    for i in range(K):
+    for i in range(K2):
         step2(e=ev2[i])
     torch.cuda.synchronize()
     t3 = time.perf_counter()
@@ -594,10 +607,10 @@ def main():
     uniq_end = unique_kv_bytes(tables_end, lens_end, bs, tok_bytes)
     uniq_bytes = uniq_end - (K - 1) / 2 * B * tok_bytes
     t_part = [ev[i][0].elapsed_ms(ev[i][1]) for i in range(K) if ev[i]]
-    t_plain = [ev2[i][0].elapsed_ms(ev2[i][1]) for i in range(K) if ev2[i]]
-    ms_step2 = (t3 - t2) * 1e3 / K
+    t_plain = [ev2[i][0].elapsed_ms(ev2[i][1]) for i in range(K2) if ev2[i]]
+    ms_step2 = (t3 - t2) * 1e3 / K2
     # The two-call steps run after the fused ones: K more tokens per sequence.
-    kv_bytes2 = float(np.mean([int((ctx0 + Wu + K + i + 1).sum()) * Hkv * D * 2 * 2 for i in range(K)]))
+    kv_bytes2 = float(np.mean([int((ctx0 + Wu + K + i + 1).sum()) * Hkv * D * 2 * 2 for i in range(K2)]))
     t_app = [e[0].elapsed_time(e[1]) for e in ev4]
     t_merge = [e[2].elapsed_time(e[3]) for e in ev4]
     part_ms = float(np.mean(t_part))
@@ -637,6 +650,7 @@ def main():
         },
         "two_call_step": {
             "calls": "kv_append, paged_attn_decode_partials, paged_attn_merge",
+            "steps": K2,
             "ms_per_step": round(ms_step2, 4),
             "GBps": round(kv_bytes2 / (ms_step2 * 1e-3) / 1e9, 2),
             "split_kernel": PLAIN_KERNEL,
