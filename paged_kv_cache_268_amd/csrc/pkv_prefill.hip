@@ -79,14 +79,21 @@ __device__ __forceinline__ f32x4 mma(typename PType<BF16>::v8 a, typename PType<
     else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950): unlike fmaxf it needs
+// no quieting of its inputs, so a chain of them is one instruction per two values.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax8(const float (&v)[8]) {
+    return vmax(vmax(vmax(vmax(vmax(vmax(vmax(v[0], v[1]), v[2]), v[3]), v[4]), v[5]), v[6]), v[7]);
+}
+
 // Reductions across lanes l ^ 16 and l ^ 32 (the 4 lanes of one score column).
 __device__ __forceinline__ float pmax16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+    return vmax(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ __forceinline__ float pmax32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+    return vmax(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ __forceinline__ float psum16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
@@ -105,7 +112,9 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uin
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     if constexpr (BF16) {
         const b2 h = {(__bf16)p0, (__bf16)p1};
-        const uint32_t w = __builtin_bit_cast(uint32_t, h);
+        uint32_t w = __builtin_bit_cast(uint32_t, h);
+        // Opaque to the optimiser, which would otherwise convert p0 a second time to get its half.
+        asm("" : "+v"(w));
         const float f0 = __builtin_bit_cast(float, w << 16), f1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
         const b2 l = {(__bf16)(p0 - f0), (__bf16)(p1 - f1)};
         hi = w;
@@ -224,7 +233,13 @@ paged_prefill_kernel(PrefillArgs a) {
         qvalid[c] = r < rows && q0 + qi < a.total_q;
         qpos[c] = base_pos + qi;
     }
-    const float sl2 = a.scale * kPLog2e;       // scores in log2 units
+    // Scores in log2 units: s * sl2 with sl2 > 0, so that the maximum of the
+    // scaled scores is the scaled maximum (rounding is monotone).  A negative
+    // scale is carried by the q operand instead (its sign bits flipped: exact);
+    // a zero scale becomes the smallest normal float (weights 1 to within
+    // 1e-37, and a masked score -inf still scales to -inf, not NaN).
+    const bool qneg = a.scale < 0.f;
+    const float sl2 = fmaxf(fabsf(a.scale) * kPLog2e, __FLT_MIN__);
     // The wave's rows [r0, r1): tiles [0, nomask_tiles) need no causal mask
     // (all 32 rows real and the tile's last key before the first row's
     // query), and tiles from wave_tiles on are masked out for every row.
@@ -248,6 +263,7 @@ paged_prefill_kernel(PrefillArgs a) {
             if (qvalid[c])
                 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
                                                     ((int64_t)qrow[c] * Hq + qhead[c]) * D + 32 * ks + 8 * quad);
+            if (qneg) w = make_uint4(w.x ^ 0x80008000u, w.y ^ 0x80008000u, w.z ^ 0x80008000u, w.w ^ 0x80008000u);
             qb[c][ks] = __builtin_bit_cast(V8, w);
         }
 
@@ -343,7 +359,7 @@ paged_prefill_kernel(PrefillArgs a) {
     float m_l[NB], l_l[NB];
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
-        m_l[c] = -INFINITY;
+        m_l[c] = -__FLT_MAX__;   // finite: the first tile's exponents are +huge, so it sets the reference
         l_l[c] = 0.f;
     }
 
@@ -368,47 +384,58 @@ paged_prefill_kernel(PrefillArgs a) {
         // (every key on the tiles before the diagonal).
         const int t0 = kt * kPKeys + 8 * quad;
         const bool nomask = kt < nomask_tiles;     // uniform
-        uint4 ph[NB], pl[NB];
-        bool any_need = false;
-        float alpha[NB];
+        // Exponents x = s sl2 - m of the lane's 8 keys per row (one fma each),
+        // relative to the row's reference m.  The reference moves only when a
+        // score exceeds it by more than kPTau: a lane that sees no such score
+        // needs no row maximum, so the maximum and its reduction over the
+        // row's 4 lanes run only when some lane of the wave sees one (the
+        // first tile of every row, where m starts at -FLT_MAX, and rare later
+        // tiles).  Masked keys are -inf and stay -inf (sl2 > 0 and finite).
+        float sv[NB][8], x[NB][8];
+        bool hot = false;
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-            float sv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = sc[c][j >> 2][j & 3] * sl2;   // log2 units
+            for (int j = 0; j < 8; ++j) sv[c][j] = sc[c][j >> 2][j & 3];
             if (!nomask) {
                 // Keys past the row's query (and every key of an unused row)
                 // get -inf: weight exp2(-inf) = 0.  Stale K rows past the
                 // context end only ever reach this branch.
                 const int lim = qvalid[c] ? qpos[c] - t0 : -1;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sv[j] = j <= lim ? sv[j] : -INFINITY;
+                for (int j = 0; j < 8; ++j) sv[c][j] = j <= lim ? sv[c][j] : -INFINITY;
             }
-            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            const float mt = pmax32(pmax16(mx));       // row max of this tile
-            const bool need = mt > m_l[c] + kPTau;     // uniform over the row's 4 lanes
-            const float m_new = need ? mt : m_l[c];
-            alpha[c] = need ? __builtin_amdgcn_exp2f(m_l[c] - m_new) : 1.f;   // 0 while nothing was seen
-            any_need |= need;
-            const float ref = m_new == -INFINITY ? 0.f : m_new;
-            float pw[8], ps = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pw[j] = __builtin_amdgcn_exp2f(sv[j] - ref);   // <= 2^8; 0 for a masked key
-                ps += pw[j];
+            for (int j = 0; j < 8; ++j) x[c][j] = __builtin_fmaf(sv[c][j], sl2, -m_l[c]);
+            hot |= vmax8(x[c]) > kPTau;
+        }
+        if (__builtin_amdgcn_ballot_w64(hot)) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                const float mt = pmax32(pmax16(vmax8(sv[c]))) * sl2;   // the row's scaled maximum
+                const bool need = mt > m_l[c] + kPTau;                 // uniform over the row's 4 lanes
+                if (need) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_l[c] - mt);   // 0 on the first tile
+                    l_l[c] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[c][db] *= alpha;
+                    m_l[c] = mt;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[c][j] = __builtin_fmaf(sv[c][j], sl2, -mt);
+                }
             }
+        }
+        uint4 ph[NB], pl[NB];
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            float pw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pw[j] = __builtin_amdgcn_exp2f(x[c][j]);   // <= 2^8 (about); 0 for a masked key
+            l_l[c] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
             split_pair<BF16>(pw[0], pw[1], ph[c].x, pl[c].x);
             split_pair<BF16>(pw[2], pw[3], ph[c].y, pl[c].y);
             split_pair<BF16>(pw[4], pw[5], ph[c].z, pl[c].z);
             split_pair<BF16>(pw[6], pw[7], ph[c].w, pl[c].w);
-            l_l[c] = l_l[c] * alpha[c] + ps;
-            m_l[c] = m_new;
-        }
-        if (__builtin_amdgcn_ballot_w64(any_need)) {
-#pragma unroll
-            for (int c = 0; c < NB; ++c)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) acc[c][db] *= alpha[c];
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {

@@ -78,6 +78,22 @@ def test_prefill_parity(case):
     assert np.all(np.abs(o - ro) <= TOL + np.abs(ro) * (2.0 ** -8 if dtype == "bf16" else 2.0 ** -11))
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.7])
+def test_prefill_scale_sign_and_size(scale):
+    """Negative, zero and large softmax scales: the kernel keeps a positive score scale and
+    carries a negative one by the query's sign (exact); zero gives uniform weights."""
+    import dataclasses
+    wl, cu = W.make_prefill_workload(8, 2, 128, 16, "bf16", [0, 40, 300], [70, 1, 45], seed=331)
+    wl = dataclasses.replace(wl, scale=scale)
+    note(f"prefill scale {scale}")
+    _, k, v = W.make_values(wl, DEV, poison=True)
+    q = W.make_prefill_q(wl, cu, DEV)
+    ro, rl = oracle.paged_prefill(W.bits16(q), W.bits16(k), W.bits16(v), wl.block_tables, wl.context_lens, cu,
+                                  wl.scale, num_kv_heads=2, block_size=16, dtype=oracle.BF16)
+    out, lse = run_gpu(wl, cu, q, k, v)
+    check(out, lse, ro, rl, f"scale {scale}")
+
+
 def test_prefill_benchmark_shape_sampled():
     """The benchmark's batch at full size; the oracle on sampled rows (each row is decode over its
     own prefix), including the first and last row of every chunk."""
