@@ -23,12 +23,14 @@
 // kv head i / tiles, so consecutive workgroups (one XCD, one L2) read the
 // same kv head's blocks.
 //
-// LDS layout.  K rows are 2D + 16 bytes apart and stored in a key order that
+// LDS layout.  K rows are 2D bytes apart and stored in a key order that
 // puts the 16 keys of each A operand in consecutive rows: LDS row 16 h + 4 a + i
 // holds key 8 a + 4 h + i (a, i < 4, h < 2).  V is stored transposed, one row
-// of 32 keys (+16 bytes) per d, written by units of 2 keys x 8 d (two 16-byte
-// loads, each d's 2 keys stored as one 32-bit word).  Rows past the context
-// end: K as loaded (those scores are masked before use), V zeroed.
+// of 32 keys per d, written by units of 2 keys x 8 d (two 16-byte loads, each
+// d's 2 keys stored as one 32-bit word).  No row padding: 16-byte chunks are
+// swizzled (kswz, vrow_phys, vchunk) so that no access shape has a bank
+// conflict.  Rows past the context end: K as loaded (those scores are masked
+// before use), V zeroed.
 //
 // Both contractions run on v_mfma_f32_16x16x32 (bf16 or f16 inputs, fp32
 // accumulation):
@@ -127,6 +129,22 @@ __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uin
     }
 }
 
+// LDS layouts without padding and without bank conflicts on gfx950, whose LDS
+// serves a 16-byte read in four passes of 16 lanes (lanes 32 h + 4 j .. + 3
+// for the j of one popcount parity) and a 4-byte write in two passes of 32
+// lanes, over 64 banks of 4 bytes.  K: row R (D bf16 values, D / 8 chunks of
+// 16 bytes) keeps chunk c at chunk c ^ kswz(R).  V transposed: rows of 32
+// keys (64 bytes, four chunks of 8 keys); row d is stored at row
+// vrow_phys(d) = d ^ ((d >> 3) & 3) and chunk q of it at chunk q ^ vchunk(row).
+// Checked against the hardware's conflict counter for every access shape of
+// this kernel: the operand reads (16 rows of one chunk column per wave), the
+// K row stores (16 lanes per row) and the two-key V stores (four rows 8 apart
+// per store).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 7) << 1 : r & 6; }
+__device__ __forceinline__ int vrow_phys(int d) { return d ^ ((d >> 3) & 3); }
+__device__ __forceinline__ int vchunk(int p) { return (p & 4) >> 1; }
+
 // Workgroup i runs on XCD i % 8; consecutive logical ids share an XCD (its L2).
 __device__ __forceinline__ int prefill_xcd_remap(int i, int n) {
     const int per = n / kNumXcds;
@@ -143,8 +161,8 @@ paged_prefill_kernel(PrefillArgs a) {
     constexpr int KS = D / 32;                    // k-steps of S^T
     constexpr int DB = D / 16;                    // 16-row output blocks of O^T
     constexpr int NB = kPBlocks;                  // column blocks per wave
-    constexpr int KROW = D * 2 + 16;              // bytes per K row in LDS
-    constexpr int VROW = kPKeys * 2 + 16;         // bytes per transposed V row in LDS
+    constexpr int KROW = D * 2;                   // bytes per K row in LDS (unpadded: chunks swizzled, see kswz)
+    constexpr int VROW = kPKeys * 2;              // bytes per transposed V row in LDS (see vrow_phys)
     constexpr int KBUF = kPKeys * KROW, VBUF = D * VROW;
     constexpr int CPR = D / 8;                    // 16-byte pieces per K/V row
     // Staging: every thread loads KPT 16-byte K pieces and one V unit (2 keys x
@@ -155,8 +173,9 @@ paged_prefill_kernel(PrefillArgs a) {
     constexpr int VU = (kPKeys / 2) * CPR;        // V units per tile
     constexpr int SR = KPT + 2;                   // staging registers per thread
     static_assert(KPT >= 1 && KPT * kPThreads == kPKeys * CPR && kPThreads % VU == 0, "tile shape");
-    constexpr int LDS = 2 * (KBUF + VBUF);
-    static_assert(LDS >= (kPrefillMaxSeqs + 1) * 4, "tile prefix fits the tile buffers");
+    // The tile buffers, or the tile prefix over sequences that precedes them (it
+    // aliases their space), whichever is larger.
+    constexpr int LDS = 2 * (KBUF + VBUF) > (kPrefillMaxSeqs + 1) * 4 ? 2 * (KBUF + VBUF) : ((kPrefillMaxSeqs + 1) * 4 + 15) / 16 * 16;
     __shared__ __align__(16) uint8_t s_mem[LDS];
     __shared__ int s_wsum[kPWaves];
 
@@ -294,13 +313,18 @@ paged_prefill_kernel(PrefillArgs a) {
         const int piece = tid + kPThreads * c, key = piece / CPR;
         kkey[c] = key;
         ksrc[c] = (key % BS) * CPR + piece % CPR;
-        kdst[c] = (16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3)) * KROW + (piece % CPR) * 16;
+        const int row = 16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3);
+        kdst[c] = row * KROW + ((piece % CPR) ^ kswz<D>(row)) * 16;
     }
     const int vu = tid % VU, vkey = 2 * (vu % 16), vcd = vu / 16;
-    // Transposed V rows are 16-byte chunks of 8 keys, chunk q of row d stored at
-    // position q ^ ((d >> 3) & 3): the 2-key stores of lanes 8 rows apart then
-    // fall in different banks, and a lane's 8-key read stays one 16-byte chunk.
-    const int voff = ((vkey >> 3) ^ (vcd & 3)) * 16 + (vkey & 7) * 2;
+    // Byte offsets of this thread's 8 two-key words in a transposed V buffer
+    // (row d = 8 vcd + r, keys vkey and vkey + 1; see vrow_phys and vchunk).
+    int vst[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int pr = vrow_phys(vcd * 8 + r);
+        vst[r] = pr * VROW + ((vkey >> 3) ^ vchunk(pr)) * 16 + (vkey & 7) * 2;
+    }
     const int64_t blk_stride = (int64_t)Hkv * BS * CPR, head_off = (int64_t)g * BS * CPR;
     // Loads are unconditional (a key past the context end reads its clamped
     // block's stale row) and the bits of `keep` say which pieces are real:
@@ -346,8 +370,8 @@ paged_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // d = 8 cd + 2e from the low halves, 8 cd + 2e + 1 from the high halves: the two keys' values.
-            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e) * VROW + voff) = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(vb + (vcd * 8 + 2 * e + 1) * VROW + voff) = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(vb + vst[2 * e]) = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vb + vst[2 * e + 1]) = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
         }
     };
 
@@ -363,6 +387,19 @@ paged_prefill_kernel(PrefillArgs a) {
         l_l[c] = 0.f;
     }
 
+    // This lane's LDS read offsets: its K row col at 16-byte chunk 4 ks + quad
+    // (the rows 16 + col of the second half add 16 KROW), and its transposed V
+    // row col of an even or an odd 16-row block (vrow_phys depends on the
+    // block's parity, not its index).
+    int krd[KS], vrd[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) krd[ks] = col * KROW + ((4 * ks + quad) ^ kswz<D>(col)) * 16;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int pr = vrow_phys(16 * par + col) - 16 * par;
+        vrd[par] = pr * VROW + 16 * (quad ^ vchunk(pr));
+    }
+
     auto compute = [&](int b, int kt) {
         const uint8_t* kb = s_mem + b * KBUF;
         const uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
@@ -371,8 +408,8 @@ paged_prefill_kernel(PrefillArgs a) {
         for (int c = 0; c < NB; ++c) sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const V8 a0 = *reinterpret_cast<const V8*>(kb + col * KROW + (32 * ks + 8 * quad) * 2);
-            const V8 a1 = *reinterpret_cast<const V8*>(kb + (16 + col) * KROW + (32 * ks + 8 * quad) * 2);
+            const V8 a0 = *reinterpret_cast<const V8*>(kb + krd[ks]);
+            const V8 a1 = *reinterpret_cast<const V8*>(kb + 16 * KROW + krd[ks]);
 #pragma unroll
             for (int c = 0; c < NB; ++c) {
                 sc[c][0] = mma<BF16>(a0, qb[c][ks], sc[c][0]);
@@ -439,8 +476,8 @@ paged_prefill_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int vr = db * 16 + col;
-            const V8 av = *reinterpret_cast<const V8*>(vb + vr * VROW + 16 * (quad ^ ((vr >> 3) & 3)));   // keys 8 quad .. +7
+            // Row 16 db + col, keys 8 quad .. 8 quad + 7: one 16-byte chunk.
+            const V8 av = *reinterpret_cast<const V8*>(vb + db * 16 * VROW + vrd[db & 1]);
 #pragma unroll
             for (int c = 0; c < NB; ++c) {
                 acc[c][db] = mma<BF16>(av, __builtin_bit_cast(V8, ph[c]), acc[c][db]);
