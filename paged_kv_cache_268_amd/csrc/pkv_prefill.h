@@ -13,6 +13,7 @@ namespace pkv {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = 32 * kPrefillWaves;
 constexpr int kPrefillMaxSeqs = 4096;
+constexpr int kPrefillSortSeqs = 128;   // up to this many sequences, longest contexts are scheduled first
 
 // Chunk queries per workgroup for a kv group of G q heads (0 when G is too large).
 inline int prefill_query_tile(int group) { return group >= 1 && group <= kPrefillRows ? kPrefillRows / group : 0; }

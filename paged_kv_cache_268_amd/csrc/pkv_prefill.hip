@@ -21,7 +21,9 @@
 // the block table, block ids by scalar loads) into LDS, double buffered, with
 // the loads issued two tiles ahead (two register stages).  Workgroup i covers
 // kv head i / tiles, so consecutive workgroups (one XCD, one L2) read the
-// same kv head's blocks.
+// same kv head's blocks, and within a kv head the query tiles go longest
+// first (sequences by context length, each sequence's tiles last first), so
+// that each XCD's last workgroups are short ones.
 //
 // LDS layout.  K rows are 2D bytes apart and stored in a key order that
 // puts the 16 keys of each A operand in consecutive rows: LDS row 16 h + 4 a + i
@@ -176,6 +178,7 @@ paged_prefill_kernel(PrefillArgs a) {
     // The tile buffers, or the tile prefix over sequences that precedes them (it
     // aliases their space), whichever is larger.
     constexpr int LDS = 2 * (KBUF + VBUF) > (kPrefillMaxSeqs + 1) * 4 ? 2 * (KBUF + VBUF) : ((kPrefillMaxSeqs + 1) * 4 + 15) / 16 * 16;
+    static_assert((4 * kPrefillSortSeqs + 1) * 4 <= LDS, "the sorted work order fits");
     __shared__ __align__(16) uint8_t s_mem[LDS];
     __shared__ int s_wsum[kPWaves];
 
@@ -184,16 +187,40 @@ paged_prefill_kernel(PrefillArgs a) {
     const int B = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
     const int Qt = a.query_tile;
 
-    // ---- query tiles per sequence, prefix in LDS (aliases the tile buffers) ----
-    int* s_pre = reinterpret_cast<int*>(s_mem);
+    // ---- work order (in LDS, aliasing the tile buffers) ----
+    // Query tiles are handed out longest first, so that the last workgroups of
+    // each XCD are short ones: sequences in order of context length, longest
+    // first (ties by index; up to kPrefillSortSeqs sequences, else last to
+    // first), and a sequence's tiles last to first.  Position i of the order
+    // holds sequence ord(i); s_pre[i] counts the query tiles before it.
+    auto tiles_of = [&](int s) {
+        const int m = a.cu_q[s + 1] - a.cu_q[s];
+        return m > 0 ? (m + Qt - 1) / Qt : 0;
+    };
+    int* s_pre = reinterpret_cast<int*>(s_mem);    // [B + 1]
+    int* s_key = s_pre + B + 1;                    // [B], sorted order only: context lengths
+    int* s_ord = s_key + B;                        // [B]: the sequence at position i
+    int* s_cnt = s_ord + B;                        // [B]: its query tiles
+    const bool by_len = B <= kPrefillSortSeqs;     // uniform
+    if (by_len) {
+        for (int s = tid; s < B; s += kPThreads) s_key[s] = min(max(a.context_lens[s], 0), a.max_context_len);
+        __syncthreads();
+        for (int s = tid; s < B; s += kPThreads) {
+            const int k = s_key[s];
+            int r = 0;                             // sequences ahead of s
+            for (int t = 0; t < B; ++t) {
+                const int kt = s_key[t];
+                r += (kt > k || (kt == k && t < s)) ? 1 : 0;
+            }
+            s_ord[r] = s;
+            s_cnt[r] = tiles_of(s);
+        }
+        __syncthreads();
+    }
     int running = 0;
     for (int base = 0; base < B; base += kPThreads) {
-        const int s = base + tid;
-        int v = 0;
-        if (s < B) {
-            const int m = a.cu_q[s + 1] - a.cu_q[s];
-            v = m > 0 ? (m + Qt - 1) / Qt : 0;
-        }
+        const int i = base + tid;
+        const int v = i < B ? (by_len ? s_cnt[i] : tiles_of(B - 1 - i)) : 0;
         int x = v;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -208,7 +235,7 @@ paged_prefill_kernel(PrefillArgs a) {
             woff += w < wave ? s_wsum[w] : 0;
             tot += s_wsum[w];
         }
-        if (s < B) s_pre[s] = running + woff + x - v;
+        if (i < B) s_pre[i] = running + woff + x - v;
         running += tot;
         __syncthreads();
     }
@@ -217,17 +244,16 @@ paged_prefill_kernel(PrefillArgs a) {
     const int T = s_pre[B];
     const int lwg = prefill_xcd_remap(blockIdx.x, gridDim.x);
     const int g = lwg / a.grid_tiles;              // kv head: consecutive workgroups share it
-    const int tl = lwg - g * a.grid_tiles;
+    const int tl = lwg - g * a.grid_tiles;         // rank of the query tile in the order
     if (g >= Hkv || tl >= T) return;               // uniform over the workgroup
-    const int tile = T - 1 - tl;                   // later (longer) tiles first
-    int sl = 0, sh = B;                            // pre[sl] <= tile < pre[sh]
+    int sl = 0, sh = B;                            // pre[sl] <= tl < pre[sh]
     while (sh - sl > 1) {
         const int mid = (sl + sh) >> 1;
-        if (s_pre[mid] <= tile) sl = mid; else sh = mid;
+        if (s_pre[mid] <= tl) sl = mid; else sh = mid;
     }
-    const int s = sl;
-    const int qt = tile - s_pre[s];
-    __syncthreads();                               // prefix dead: LDS now holds K/V tiles
+    const int s = by_len ? s_ord[sl] : B - 1 - sl;
+    const int qt = s_pre[sl + 1] - 1 - tl;         // the sequence's tiles, last first
+    __syncthreads();                               // order dead: LDS now holds K/V tiles
 
     const int n = min(max(a.context_lens[s], 0), a.max_context_len);
     const int q0 = a.cu_q[s];
