@@ -529,6 +529,9 @@ def main():
     every = max(1, K // EVENT_SAMPLES)
     ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every == 0 else None for i in range(K)]
     single = pkv.decode_launches(desc) == 1
+    # kv_append_decode folds at most PKV_FUSE_MAX_ITEMS appended sequences into the
+    # split kernel; past that it runs kv_append and the plain split kernel.
+    step_kernel = DECODE_KERNEL if B <= pkv.PKV_FUSE_MAX_ITEMS else PLAIN_KERNEL
 
     def step(e=None):
         pool.append_decode(seq_ids, k_new, v_new, tables, lens, desc, q, wl.scale, out, None, ws,
@@ -643,7 +646,7 @@ def main():
         "unique_kv_bytes_per_step": int(uniq_bytes),
         "kernel_ms": {
             "split": round(part_ms, 4),
-            "split_kernel": DECODE_KERNEL,
+            "split_kernel": step_kernel,
             "decode_launches": 1 if single else 2,
             "split_timed_launches": f"{len(t_part)} of {K} (events on every {every}th timed step)",
             "split_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
@@ -661,7 +664,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": DECODE_KERNEL,
+            "kernel": step_kernel,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -400,11 +400,12 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
  *   table_stride its max_blocks_per_seq; every listed sequence must be below
  *   desc->num_seqs, and its new length at most desc->max_context_len
  *   (PKV_EINVAL, nothing enqueued and the pool unchanged).
- *   Up to 160 appended sequences travel in the kernel arguments; more go
+ *   Up to PKV_FUSE_MAX_ITEMS appended sequences travel in the kernel arguments; more go
  *   through kv_append and the plain decode (same results).  Sequences whose
  *   tail block is shared get their copy-on-write copy in a launch before.
  *   start / stop: both NULL, or timing events that the split dispatch stamps
  *   as in paged_attn_decode_partials_timed (the merge is not timed). */
+enum { PKV_FUSE_MAX_ITEMS = 160 };
 int kv_append_decode(pkv_pool* pool, int32_t n, const int32_t* seq_ids, const void* k_new,
                      const void* v_new, int32_t* block_tables, int32_t* context_lens,
                      const pkv_attn_desc* desc, const void* q, float scale, void* out, float* lse,

@@ -30,6 +30,8 @@
 #include "pkv_prefill.h"
 #include "pkv_tier.h"
 
+static_assert(pkv::kFuseItems == PKV_FUSE_MAX_ITEMS, "the fused kernel carries the documented number of items");
+
 namespace {
 
 thread_local std::string g_err;
