@@ -94,6 +94,23 @@ def test_prefill_scale_sign_and_size(scale):
     check(out, lse, ro, rl, f"scale {scale}")
 
 
+@pytest.mark.parametrize("B", [127, 128, 129])
+def test_prefill_work_order_boundary(B):
+    """Up to 128 sequences the kernel orders its work by context length (ties by index), above
+    that last to first: batches on both sides, with many equal context lengths, compared in full."""
+    rng = np.random.default_rng(400 + B)
+    pre = [int(x) for x in rng.choice([0, 16, 33, 100], size=B)]
+    chk = [int(x) for x in rng.choice([1, 5, 32, 40], size=B)]
+    wl, cu = W.make_prefill_workload(8, 2, 64, 16, "bf16", pre, chk, seed=410 + B)
+    note(f"prefill work order B={B}")
+    _, k, v = W.make_values(wl, DEV, poison=True)
+    q = W.make_prefill_q(wl, cu, DEV)
+    ro, rl = oracle.paged_prefill(W.bits16(q), W.bits16(k), W.bits16(v), wl.block_tables, wl.context_lens, cu,
+                                  wl.scale, num_kv_heads=2, block_size=16, dtype=oracle.BF16)
+    out, lse = run_gpu(wl, cu, q, k, v)
+    check(out, lse, ro, rl, f"B={B}")
+
+
 def test_prefill_benchmark_shape_sampled():
     """The benchmark's batch at full size; the oracle on sampled rows (each row is decode over its
     own prefix), including the first and last row of every chunk."""
