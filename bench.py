@@ -34,7 +34,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 N_BREAKDOWN = 10   # instrumented steps after the timed loop (append / merge event timings)
-EVENT_SAMPLES = 12  # timed steps whose split launch carries timing events: about this many, evenly spaced
+EVENT_SAMPLES = 12  # at most this many timed steps (one in eight, at least 2) carry timing events on their split launch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE_KERNEL = "paged_decode_append_split_kernel"   # the step's split launch: append folded in (kv_append_decode)
 PLAIN_KERNEL = "paged_decode_split_kernel"
@@ -522,12 +522,13 @@ def main():
     # the split kernel, then the merge kernel (no merge when a single partition
     # covers every context).  The split kernel's duration (the roofline's
     # denominator) comes from two HIP events that its own dispatch stamps with its
-    # start and end, on about EVENT_SAMPLES evenly spaced timed steps.  A timed dispatch
-    # completes with a fence that costs about 10 us of idle GPU between kernels
-    # (measured on a kernel trace: 0 us gaps without events); on every step that
-    # would be 5 % of the step.
-    every = max(1, K // EVENT_SAMPLES)
-    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every == 0 else None for i in range(K)]
+    # start and end, on a few evenly spaced timed steps: one in eight, between 2 and
+    # EVENT_SAMPLES of them.  A timed dispatch completes with a fence that costs about
+    # 10 us of idle GPU between kernels (measured on a kernel trace: 0 us gaps without
+    # events); on every step that would be 5 % of the step, on one in eight 0.6 %.
+    n_ev = max(2, min(EVENT_SAMPLES, K // 8)) if K > 1 else 1
+    ev_at = {int(round(j * (K - 1) / max(n_ev - 1, 1))) for j in range(n_ev)}
+    ev = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i in ev_at else None for i in range(K)]
     single = pkv.decode_launches(desc) == 1
     # kv_append_decode folds at most PKV_FUSE_MAX_ITEMS appended sequences into the
     # split kernel; past that it runs kv_append and the plain split kernel.
@@ -540,8 +541,9 @@ def main():
     # The same step as separate calls (kv_append, the plain split kernel, the
     # merge kernel), timed after the fused steps for comparison; marker events
     # around each call in a pass of their own give the append / merge breakdown.
-    every2 = max(1, K2 // EVENT_SAMPLES)
-    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i % every2 == 0 else None for i in range(K2)]
+    n_ev2 = max(2, min(EVENT_SAMPLES, K2 // 8)) if K2 > 1 else 1
+    ev2_at = {int(round(j * (K2 - 1) / max(n_ev2 - 1, 1))) for j in range(n_ev2)}
+    ev2 = [[pkv.LaunchEvent(), pkv.LaunchEvent()] if i in ev2_at else None for i in range(K2)]
     ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(N_BREAKDOWN)]
 
     def split(e=None):
@@ -648,7 +650,7 @@ def main():
             "split": round(part_ms, 4),
             "split_kernel": step_kernel,
             "decode_launches": 1 if single else 2,
-            "split_timed_launches": f"{len(t_part)} of {K} (events on every {every}th timed step)",
+            "split_timed_launches": f"{len(t_part)} of {K} timed steps, evenly spaced",
             "split_p10_p50_p90": [round(float(x), 4) for x in np.percentile(t_part, [10, 50, 90])],
         },
         "two_call_step": {
