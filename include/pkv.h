@@ -391,10 +391,11 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
  * kernel takes the appended sequences' lengths and new table entries from the
  * call and their new K/V rows from k_new / v_new, and stores what kv_append
  * stores (rows, lengths, table entries).  Pool state, caches, tables, lengths,
- * out and lse afterwards are bit for bit those of the two calls (the page's
- * engine writes the step's K/V into the cache and then runs attention,
- * "从零开始构建LLM推理引擎：模型执行器深度解析" 5.2; "架构解构：推理引擎的四层抽象",
- * PagedAttention section).
+ * out and lse afterwards are bit for bit those of the two calls: the new token
+ * attends to itself, as a causal mask lets a query attend to its own position
+ * ("从零开始构建LLM推理引擎：模型执行器深度解析" 3.1; the KV cache update is part of
+ * executing a batch there, 5.1; metadata is updated between launches,
+ * "架构解构：推理引擎的四层抽象", PagedAttention section).
  *   16-bit pools only (8-bit pools: PKV_EUNSUPPORTED); the descriptor's kv
  *   dtype, head_dim, block_size, num_kv_heads must be the pool's and
  *   table_stride its max_blocks_per_seq; every listed sequence must be below
