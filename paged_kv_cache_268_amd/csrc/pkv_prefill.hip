@@ -110,18 +110,21 @@ __device__ __forceinline__ float psum32(float x) {
 
 // Two weights -> their 16-bit roundings (hi, one packed word) and the
 // roundings of what is left (lo): p = hi + lo to about 2^-17 relative.
+// bf16: each residual p - hi comes from one v_dot2_f32_bf16, hi . (-1, 0) + p0
+// and hi . (0, -1) + p1, exact (every term is); sel0 / sel1 hold those two
+// bf16 pairs in registers: encoded by the compiler as an inline constant, the
+// pair (-1, 0) gave wrong residuals.  Checked bit-exact against p - RNE(p) on
+// four million weights, denormals included.
 template <bool BF16>
-__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t sel0, uint32_t sel1, uint32_t& hi, uint32_t& lo) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     if constexpr (BF16) {
         const b2 h = {(__bf16)p0, (__bf16)p1};
-        uint32_t w = __builtin_bit_cast(uint32_t, h);
-        // Opaque to the optimiser, which would otherwise convert p0 a second time to get its half.
-        asm("" : "+v"(w));
-        const float f0 = __builtin_bit_cast(float, w << 16), f1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
-        const b2 l = {(__bf16)(p0 - f0), (__bf16)(p1 - f1)};
-        hi = w;
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(b2, sel0), p0, false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(b2, sel1), p1, false);
+        const b2 l = {(__bf16)r0, (__bf16)r1};
+        hi = __builtin_bit_cast(uint32_t, h);
         lo = __builtin_bit_cast(uint32_t, l);
     } else {
         const h2 h = {(_Float16)p0, (_Float16)p1};
@@ -426,6 +429,10 @@ paged_prefill_kernel(PrefillArgs a) {
         vrd[par] = pr * VROW + 16 * (quad ^ vchunk(pr));
     }
 
+    // The bf16 pairs (-1, 0) and (0, -1) of split_pair, opaque to the compiler.
+    uint32_t sel0 = 0x0000BF80u, sel1 = 0xBF800000u;
+    asm("" : "+v"(sel0), "+v"(sel1));
+
     auto compute = [&](int b, int kt) {
         const uint8_t* kb = s_mem + b * KBUF;
         const uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
@@ -495,10 +502,10 @@ paged_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) pw[j] = __builtin_amdgcn_exp2f(x[c][j]);   // <= 2^8 (about); 0 for a masked key
             l_l[c] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-            split_pair<BF16>(pw[0], pw[1], ph[c].x, pl[c].x);
-            split_pair<BF16>(pw[2], pw[3], ph[c].y, pl[c].y);
-            split_pair<BF16>(pw[4], pw[5], ph[c].z, pl[c].z);
-            split_pair<BF16>(pw[6], pw[7], ph[c].w, pl[c].w);
+            split_pair<BF16>(pw[0], pw[1], sel0, sel1, ph[c].x, pl[c].x);
+            split_pair<BF16>(pw[2], pw[3], sel0, sel1, ph[c].y, pl[c].y);
+            split_pair<BF16>(pw[4], pw[5], sel0, sel1, ph[c].z, pl[c].z);
+            split_pair<BF16>(pw[6], pw[7], sel0, sel1, ph[c].w, pl[c].w);
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
