@@ -398,9 +398,10 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
  * "架构解构：推理引擎的四层抽象", PagedAttention section).
  *   16-bit pools only (8-bit pools: PKV_EUNSUPPORTED); the descriptor's kv
  *   dtype, head_dim, block_size, num_kv_heads must be the pool's and
- *   table_stride its max_blocks_per_seq; every listed sequence must be below
- *   desc->num_seqs, and its new length at most desc->max_context_len
- *   (PKV_EINVAL, nothing enqueued and the pool unchanged).
+ *   table_stride its max_blocks_per_seq; every listed sequence must be listed
+ *   once, below desc->num_seqs, with room in its table and no blocks in the
+ *   host tier, and its new length at most desc->max_context_len (PKV_EINVAL,
+ *   nothing enqueued and the pool unchanged).
  *   Up to PKV_FUSE_MAX_ITEMS appended sequences travel in the kernel arguments; more go
  *   through kv_append and the plain decode (same results).  Sequences whose
  *   tail block is shared get their copy-on-write copy in a launch before.

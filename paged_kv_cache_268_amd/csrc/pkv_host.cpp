@@ -1325,9 +1325,18 @@ int kv_append_decode(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void*
     if ((start == nullptr) != (stop == nullptr))
         return fail(PKV_EINVAL, "kv_append_decode: give both timing events or neither");
     if (d->num_seqs > p->d.max_seqs) return fail(PKV_EINVAL, "kv_append_decode: num_seqs beyond the pool's rows");
+    std::vector<uint8_t> listed(p->d.max_seqs, 0);
     for (int32_t i = 0; i < n; ++i) {
         const int32_t s = seq_ids[i];
         if (!p->valid_seq(s)) return fail(PKV_EINVAL, "kv_append_decode: unknown sequence %d", s);
+        // The append's own refusals (kv_reserve), checked here too so that they
+        // come before anything is set up.
+        if (listed[s]) return fail(PKV_EINVAL, "kv_append_decode: sequence %d listed twice", s);
+        listed[s] = 1;
+        if (p->nhost[s])
+            return fail(PKV_EINVAL, "kv_append_decode: sequence %d has blocks in the host tier (restore it first)", s);
+        if (p->len[s] % p->d.block_size == 0 && p->len[s] / p->d.block_size >= p->d.max_blocks_per_seq)
+            return fail(PKV_EINVAL, "kv_append_decode: sequence %d is full (%d blocks)", s, p->d.max_blocks_per_seq);
         if (s >= d->num_seqs)
             return fail(PKV_EINVAL, "kv_append_decode: sequence %d is not among the %d decoded rows", s, d->num_seqs);
         if ((int64_t)p->len[s] + 1 > d->max_context_len)

@@ -473,8 +473,9 @@ def test_timed_partials_need_both_events():
 
 def test_append_decode_refusals_leave_the_pool_unchanged():
     """kv_append_decode checks the pool, the descriptor and every listed sequence before it changes
-    anything: 8-bit pools, a descriptor that is not the pool's, a sequence outside the decoded rows or
-    past max_context_len are refused and the pool still appends as before."""
+    anything: 8-bit pools, a descriptor that is not the pool's, a sequence outside the decoded rows,
+    past max_context_len, listed twice or with a full table are refused and the pool still appends
+    as before."""
     lib = pkv.load()
     fake = ctypes.c_void_p(1 << 20)
     pool = pkv.BlockPool(16, 16, 2, 64, pkv.PKV_BF16, 4, 8)
@@ -496,6 +497,11 @@ def test_append_decode_refusals_leave_the_pool_unchanged():
         assert call(d) == pkv.PKV_EINVAL, what
         assert what.split()[0] in pkv.last_error() or "pool's" in pkv.last_error(), pkv.last_error()
     assert call(good, np.array([s0, 3], dtype=np.int32)) == pkv.PKV_EINVAL      # unknown sequence
+    assert call(good, np.array([s1, s1], dtype=np.int32)) == pkv.PKV_EINVAL     # listed twice
+    assert "twice" in pkv.last_error(), pkv.last_error()
+    full = pool.import_seq(128, np.arange(8, dtype=np.int32))                   # all 8 table entries used
+    assert call(good, np.array([s0, full], dtype=np.int32)) == pkv.PKV_EINVAL
+    assert "full" in pkv.last_error(), pkv.last_error()
     # Nothing was taken: the pool's next append still opens each sequence's first block.
     items = np.zeros((2, 7), dtype=np.int32)
     assert lib.kv_reserve(pool.handle, 2, ids.ctypes.data, items.ctypes.data) == pkv.PKV_OK
