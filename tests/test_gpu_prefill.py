@@ -56,6 +56,9 @@ CASES = [
     (8, 2, 128, 16, "bf16", [0, 0, 31, 250], [65, 200, 63, 33]),
     (32, 8, 128, 32, "bf16", [300, 0, 1], [128, 96, 7]),
     (12, 4, 64, 32, "f16", [64, 0], [64, 193]),
+    (16, 2, 128, 16, "bf16", [10, 300], [47, 90]),     # G = 8: 16 chunk queries per workgroup
+    (8, 4, 128, 32, "bf16", [0, 77], [100, 3]),         # G = 2
+    (32, 2, 64, 16, "f16", [33, 0, 200], [20, 57, 9]),  # G = 16: 8 chunk queries per workgroup
 ]
 
 
