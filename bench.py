@@ -532,7 +532,7 @@ def main():
     single = pkv.decode_launches(desc) == 1
     # kv_append_decode folds at most PKV_FUSE_MAX_ITEMS appended sequences into the
     # split kernel; past that it runs kv_append and the plain split kernel.
-    step_kernel = DECODE_KERNEL if B <= pkv.PKV_FUSE_MAX_ITEMS else PLAIN_KERNEL
+    step_kernel = DECODE_KERNEL if B <= pkv.PKV_FUSE_MAX_ITEMS and max_ctx < (1 << 20) else PLAIN_KERNEL
 
     def step(e=None):
         pool.append_decode(seq_ids, k_new, v_new, tables, lens, desc, q, wl.scale, out, None, ws,

@@ -402,12 +402,13 @@ int paged_attn_merge(const pkv_attn_desc* desc, const int32_t* context_lens, voi
  *   once, below desc->num_seqs, with room in its table and no blocks in the
  *   host tier, and its new length at most desc->max_context_len (PKV_EINVAL,
  *   nothing enqueued and the pool unchanged).
- *   Up to PKV_FUSE_MAX_ITEMS appended sequences travel in the kernel arguments; more go
- *   through kv_append and the plain decode (same results).  Sequences whose
+ *   Up to PKV_FUSE_MAX_ITEMS appended sequences travel in the kernel arguments
+ *   (with max_context_len below 2^20); more go through kv_append and the plain
+ *   decode (same results).  Sequences whose
  *   tail block is shared get their copy-on-write copy in a launch before.
  *   start / stop: both NULL, or timing events that the split dispatch stamps
  *   as in paged_attn_decode_partials_timed (the merge is not timed). */
-enum { PKV_FUSE_MAX_ITEMS = 160 };
+enum { PKV_FUSE_MAX_ITEMS = 320 };
 int kv_append_decode(pkv_pool* pool, int32_t n, const int32_t* seq_ids, const void* k_new,
                      const void* v_new, int32_t* block_tables, int32_t* context_lens,
                      const pkv_attn_desc* desc, const void* q, float scale, void* out, float* lse,

@@ -270,9 +270,9 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
     __shared__ int s_len[kMaxSeqs];       // clamped context lengths, read once per workgroup
     __shared__ int s_wsum[kWaves];
     // Fused append: item index of each sequence (kNoItem: not appended).
-    constexpr uint8_t kNoItem = 0xFF;
-    static_assert(kFuseItems < kNoItem, "item index fits a byte");
-    __shared__ uint8_t s_item[FUSE ? kMaxSeqs : 1];
+    constexpr uint16_t kNoItem = 0xFFFF;
+    static_assert(kFuseItems < kNoItem, "item index fits 16 bits");
+    __shared__ uint16_t s_item[FUSE ? kMaxSeqs : 1];
     __shared__ FuseItem s_fit[FUSE ? kFuseItems : 1];   // the items, read from the kernel arguments once
     // Paired halves (a.pair_halves): softmax state exchange, 2 buffers x 2
     // wave pairs x (4 EPL + 2) floats x 64 lanes, dynamic LDS of the launch.
@@ -294,13 +294,13 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
         for (int s = threadIdx.x; s < B; s += kThreads) s_item[s] = kNoItem;
         for (int i = threadIdx.x; i < a.n_items; i += kThreads) s_fit[i] = fit[i];
         __syncthreads();
-        for (int i = threadIdx.x; i < a.n_items; i += kThreads) s_item[s_fit[i].seq] = (uint8_t)i;
+        for (int i = threadIdx.x; i < a.n_items; i += kThreads) s_item[s_fit[i].seq()] = (uint16_t)i;
         __syncthreads();
     }
     auto len_of = [&](int s) -> int {
         if constexpr (FUSE) {
             const int ii = s_item[s];
-            if (ii != kNoItem) return min(max(s_fit[ii].new_len, 0), a.max_context_len);
+            if (ii != kNoItem) return min(max(s_fit[ii].new_len(), 0), a.max_context_len);
         }
         return min(max(s < kThreads ? len0 : a.context_lens[s], 0), a.max_context_len);
     };
@@ -347,9 +347,9 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
             // table entries of blocks the call opened or copied into.
             for (int i = threadIdx.x; i < a.n_items; i += kThreads) {
                 const FuseItem it = s_fit[i];
-                a.lens_out[it.seq] = it.new_len;
+                a.lens_out[it.seq()] = it.new_len();
                 if (it.new_block >= 0)
-                    a.tables_out[(int64_t)it.seq * a.table_stride + (it.new_len - 1) / BS] = it.new_block;
+                    a.tables_out[(int64_t)it.seq() * a.table_stride + (it.new_len() - 1) / BS] = it.new_block;
             }
         }
         for (int s = 0; s < B; ++s) {
@@ -715,7 +715,7 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, const FuseItem* 
             const int ii = s_item[sl];
             if (ii != kNoItem) {
                 const FuseItem it = s_fit[ii];
-                const int tn = it.new_len - 1;     // position of the new token
+                const int tn = it.new_len() - 1;   // position of the new token
                 if (it.new_block >= 0 && (w.j * kTile) / BS == tn / BS) w.blk = it.new_block;
                 if (w.j == tn / kTile) w.sub = (ii << 4) | (tn % kTile);
             }

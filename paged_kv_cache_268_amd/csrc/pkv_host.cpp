@@ -1354,8 +1354,9 @@ int kv_append_decode(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void*
     rc = check_ptrs(pl, q, p->k_cache, p->v_cache, block_tables, context_lens, out, lse, workspace, workspace_bytes,
                     true);
     if (rc) return rc;
-    if (n > pkv::kFuseItems) {
-        // More items than the kernel arguments carry: the same work as two calls.
+    if (n > pkv::kFuseItems || d->max_context_len > pkv::kFuseMaxLen) {
+        // More items than the kernel arguments carry, or lengths beyond what an
+        // item holds: the same work as two calls.
         rc = kv_append(p, n, seq_ids, k_new, v_new, block_tables, context_lens, stream);
         if (rc) return rc;
         rc = start ? paged_attn_decode_partials_timed(d, q, p->k_cache, p->v_cache, nullptr, nullptr, block_tables,
@@ -1403,7 +1404,7 @@ int kv_append_decode(pkv_pool* p, int32_t n, const int32_t* seq_ids, const void*
     pkv::FuseItems fi;
     for (int32_t i = 0; i < n; ++i) {
         const pkv::AppendItem& it = p->stage[(size_t)i];
-        fi.it[i] = {it.seq, it.slot, it.new_block, it.new_len};
+        fi.it[i] = {(uint32_t)it.seq | ((uint32_t)it.new_len << 12), it.new_block};
     }
     pkv::DecodeArgs a = decode_args(d, pl, q, p->k_cache, p->v_cache, nullptr, nullptr, block_tables, context_lens,
                                     scale, out, lse, workspace);

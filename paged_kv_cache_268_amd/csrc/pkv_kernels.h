@@ -52,13 +52,20 @@ struct DecodeArgs {
     int32_t n_items;
 };
 
-// One appended token of a fused append + decode: sequence, cache slot
-// (block * block_size + row), the block the call opened or copied into (-1:
-// none) and the sequence's new length.  Travels in the kernel arguments.
+// One appended token of a fused append + decode, 8 bytes: the sequence (low
+// 12 bits) and its new length (high 20 bits) in one word, and the block the
+// call opened or copied into (-1: none).  The new row's slot is not carried:
+// the kernel stores the row into the block of the tile that holds it, which
+// it finds as it reads that tile.  Travels in the kernel arguments.
 struct FuseItem {
-    int32_t seq, slot, new_block, new_len;
+    uint32_t seq_len;
+    int32_t new_block;
+    __host__ __device__ int seq() const { return (int)(seq_len & 0xFFFu); }
+    __host__ __device__ int new_len() const { return (int)(seq_len >> 12); }
 };
-constexpr int kFuseItems = 160;
+constexpr int kFuseItems = 320;
+constexpr int kFuseMaxLen = (1 << 20) - 1;   // largest new length an item holds
+static_assert(kMaxSeqs <= 4096, "a sequence index fits the item's 12 bits");
 struct FuseItems {
     FuseItem it[kFuseItems];
 };

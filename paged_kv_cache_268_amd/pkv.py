@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOMEM, PKV_EUNSUPPORTED, PKV_EHIP, PKV_EWORKSPACE = 0, -1, -2, -3, -4, -5
 PKV_F16, PKV_BF16, PKV_F32, PKV_FP8_E4M3 = 0, 1, 2, 3
-PKV_FUSE_MAX_ITEMS = 160   # appended sequences kv_append_decode folds into the split kernel (include/pkv.h)
+PKV_FUSE_MAX_ITEMS = 320   # appended sequences kv_append_decode folds into the split kernel (include/pkv.h)
 
 # Every entry point include/pkv.h declares.
 EXPORTS = (

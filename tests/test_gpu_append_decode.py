@@ -154,12 +154,20 @@ def test_fused_copy_on_write():
     check_oracle(b, q, out, lse, 8, "bf16", 16)
 
 
+def test_fused_many_items():
+    """300 appended sequences, all in the kernel arguments (item indexes past 255)."""
+    lens = list(np.random.default_rng(4).integers(1, 300, size=300))
+    note("fused append+decode, 300 sequences")
+    a, b, tdt = make_pair(300, 8, 2, 64, 16, "bf16", lens, seed=19, spare_blocks=400)
+    run_steps(a, b, 8, tdt, steps=3, P=0, nw=0, seed=20)
+
+
 def test_fused_more_items_than_kernel_arguments():
-    """200 appended sequences: past the 160 the kernel arguments carry, the call runs kv_append and the
+    """340 appended sequences: past the 320 the kernel arguments carry, the call runs kv_append and the
     plain decode, with the same results."""
-    lens = list(np.random.default_rng(3).integers(1, 300, size=200))
-    note("fused append+decode, 200 sequences (fallback)")
-    a, b, tdt = make_pair(200, 8, 2, 64, 16, "bf16", lens, seed=17)
+    lens = list(np.random.default_rng(3).integers(1, 300, size=340))
+    note("fused append+decode, 340 sequences (fallback)")
+    a, b, tdt = make_pair(340, 8, 2, 64, 16, "bf16", lens, seed=17, spare_blocks=400)
     run_steps(a, b, 8, tdt, steps=3, P=0, nw=0, seed=18)
 
 
