@@ -355,44 +355,44 @@ paged_prefill_kernel(PrefillArgs a) {
         vst[r] = pr * VROW + ((vkey >> 3) ^ vchunk(pr)) * 16 + (vkey & 7) * 2;
     }
     const int64_t blk_stride = (int64_t)Hkv * BS * CPR, head_off = (int64_t)g * BS * CPR;
+    // The keys of K piece c (tid + kPThreads c) lie in one block of the tile
+    // when a piece index spans at most a block (D = 128: 16 keys per c): that
+    // block's base is then wave-uniform, and the piece's address a 32-bit
+    // lane offset from it.
+    constexpr int SETK = kPThreads / CPR;
+    constexpr bool KUNI = SETK <= BS;
     // Loads are unconditional (a key past the context end reads its clamped
-    // block's stale row) and the bits of `keep` say which pieces are real:
-    // the store to LDS zeroes the others, once the loads have arrived.
-    auto gload = [&](int kt, int2 ids, u32x4 (&r)[SR], int& keep) {
+    // block's stale row); the store to LDS zeroes the V values of such keys,
+    // once the loads have arrived.  gload returns the tile's first key.
+    auto gload = [&](int kt, int2 ids, u32x4 (&r)[SR], int& t0) {
         const int64_t o0 = ids.x * blk_stride + head_off, o1 = ids.y * blk_stride + head_off;   // uniform
-        const int t0 = kt * kPKeys;
-        const bool full = t0 + kPKeys <= n;        // uniform: every key of the tile is cached
-        keep = 0;
+        t0 = kt * kPKeys;
 #pragma unroll
         for (int c = 0; c < KPT; ++c) {
-            const int key = kkey[c];
-            r[c] = kg[(key < BS ? o0 : o1) + ksrc[c]];
-            keep |= (full || t0 + key < n) ? 1 << c : 0;
+            if constexpr (KUNI) {
+                const uint8_t* kb = reinterpret_cast<const uint8_t*>(kg + ((c * SETK) / BS ? o1 : o0));
+                r[c] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)ksrc[c] * 16u);
+            } else {
+                r[c] = kg[(kkey[c] < BS ? o0 : o1) + ksrc[c]];
+            }
         }
         const u32x4* p = vg + (vkey < BS ? o0 : o1) + (vkey % BS) * CPR + vcd;
         r[KPT] = p[0];
         r[KPT + 1] = p[CPR];
-        keep |= (full || t0 + vkey < n) ? 1 << KPT : 0;
-        keep |= (full || t0 + vkey + 1 < n) ? 2 << KPT : 0;
-        keep = full ? -1 : keep;
     };
-    // The piece itself, or zeros (component selects, so the staging arrays stay in registers).
-    auto kept = [](int keep, int c, u32x4 v) {
-        return ((keep >> c) & 1) ? v : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto lstore = [&](int b, const u32x4 (&r)[SR], int keep) {
+    auto lstore = [&](int b, const u32x4 (&r)[SR], int t0) {
         uint8_t* kb = s_mem + b * KBUF;
         // K rows past the context end stay as loaded: their scores are masked
         // to -inf before use.  V rows there are zeroed (weight 0 times a stale
-        // NaN would still be NaN); a full tile (keep == -1 in every lane) skips that.
+        // NaN would still be NaN), on the tile that holds the context end only.
 #pragma unroll
         for (int c = 0; c < KPT; ++c) *reinterpret_cast<u32x4*>(kb + kdst[c]) = r[c];
         uint8_t* vb = s_mem + 2 * KBUF + b * VBUF;
         u32x4 v0 = r[KPT], v1 = r[KPT + 1];
-        if (!__builtin_amdgcn_ballot_w64(keep != -1)) {
-        } else {
-            v0 = kept(keep, KPT, v0);
-            v1 = kept(keep, KPT + 1, v1);
+        if (t0 + kPKeys > n) {                     // uniform
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            v0 = t0 + vkey < n ? v0 : z;
+            v1 = t0 + vkey + 1 < n ? v1 : z;
         }
         const uint32_t w0[4] = {v0[0], v0[1], v0[2], v0[3]};
         const uint32_t w1[4] = {v1[0], v1[1], v1[2], v1[3]};
@@ -531,27 +531,27 @@ paged_prefill_kernel(PrefillArgs a) {
     // the reads of one buffer from the next store into it.  A wave whose rows
     // are all past a tile's keys only stages and waits.
     u32x4 st_a[SR], st_b[SR];
-    int keep_a = 0, keep_b = 0;
+    int t_a = 0, t_b = 0;
     if (NT > 0) {                                  // uniform; rows with no key still get their output below
-    gload(0, load_ids(0), st_a, keep_a);
-    lstore(0, st_a, keep_a);
-    gload(min(1, NT - 1), load_ids(min(1, NT - 1)), st_a, keep_a);   // tile 1 in flight in st_a
+    gload(0, load_ids(0), st_a, t_a);
+    lstore(0, st_a, t_a);
+    gload(min(1, NT - 1), load_ids(min(1, NT - 1)), st_a, t_a);   // tile 1 in flight in st_a
     int2 ids_next = load_ids(min(2, NT - 1));      // block ids of the next tile to load
     __syncthreads();
     // cur holds tile kt + 1's loads in flight; nxt is free.
-    auto step = [&](int kt, u32x4 (&cur)[SR], int& keep_cur, u32x4 (&nxt)[SR], int& keep_nxt) {
-        gload(min(kt + 2, NT - 1), ids_next, nxt, keep_nxt);
+    auto step = [&](int kt, u32x4 (&cur)[SR], int& t_cur, u32x4 (&nxt)[SR], int& t_nxt) {
+        gload(min(kt + 2, NT - 1), ids_next, nxt, t_nxt);
         ids_next = load_ids(min(kt + 3, NT - 1));
         if (kt < wave_tiles) compute(kt & 1, kt);
-        lstore((kt + 1) & 1, cur, keep_cur);       // past the last tile: a copy nobody reads
+        lstore((kt + 1) & 1, cur, t_cur);       // past the last tile: a copy nobody reads
         __syncthreads();
     };
     // Steps in pairs, both unconditional (an odd NT ends with a step that only
     // stages a copy: no wave computes tile NT), so the staging registers carry
     // over the loop edge without copies, which would wait for their loads.
     for (int kt = 0; kt < NT; kt += 2) {
-        step(kt, st_a, keep_a, st_b, keep_b);
-        step(kt + 1, st_b, keep_b, st_a, keep_a);
+        step(kt, st_a, t_a, st_b, t_b);
+        step(kt + 1, st_b, t_b, st_a, t_a);
     }
     }
 
