@@ -68,10 +68,11 @@ def make_pair(B, Hq, Hkv, D, bs, dtype, lens, seed, spare_blocks=64, rows=None):
     return a, b, tdt
 
 
-def run_steps(a, b, Hq, tdt, steps, P, nw, seed, pick=None, timed=False):
+def run_steps(a, b, Hq, tdt, steps, P, nw, seed, pick=None, timed=False, max_ctx=None):
     """Steps on both sides; returns the last step's (q, out, lse) of the fused side."""
     B, Hkv, D = a.nseq, a.k.shape[1], a.k.shape[3]
-    max_ctx = int(a.lens.max().item()) + steps + 1
+    if max_ctx is None:
+        max_ctx = int(a.lens.max().item()) + steps + 1
     desc = pkv.desc_for(torch.empty((B, Hq, D), dtype=tdt), a.k, a.tab, max_ctx, P, num_waves=nw)
     ws_a, ws_b = pkv.alloc_workspace(desc, DEV), pkv.alloc_workspace(desc, DEV)
     rng = np.random.default_rng(seed)
@@ -169,6 +170,19 @@ def test_fused_more_items_than_kernel_arguments():
     note("fused append+decode, 340 sequences (fallback)")
     a, b, tdt = make_pair(340, 8, 2, 64, 16, "bf16", lens, seed=17, spare_blocks=400)
     run_steps(a, b, 8, tdt, steps=3, P=0, nw=0, seed=18)
+
+
+@pytest.mark.parametrize("max_ctx,start", [((1 << 20) - 1, (1 << 20) - 4), ((1 << 20) + 2, (1 << 20) - 2)])
+def test_fused_longest_contexts(max_ctx, start):
+    """A context that grows to the largest length an item carries (2^20 - 1, all 20 bits set), and one
+    that grows past it under a descriptor whose max_context_len leaves the fused kernel (two calls):
+    both bit for bit against kv_append + paged_attn_decode, the last step against the oracle."""
+    lens = [start, 100]
+    note(f"fused append+decode, context {start} -> {start + 3}, max_context_len {max_ctx}")
+    a, b, tdt = make_pair(2, 4, 1, 64, 16, "bf16", lens, seed=23, spare_blocks=16)
+    q, out, lse = run_steps(a, b, 4, tdt, steps=3, P=0, nw=0, seed=24, max_ctx=max_ctx)
+    assert int(b.lens[0].item()) == start + 3
+    check_oracle(b, q, out, lse, 4, "bf16", 16)
 
 
 def test_fused_timed():
