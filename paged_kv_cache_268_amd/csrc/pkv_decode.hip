@@ -241,9 +241,10 @@ __device__ __forceinline__ int padded_tiles(int nt, int fixed_chunk) {
 // output and log2-domain lse to slot k = c - first(s, g) / C, or the final
 // output directly when it covers all of (s, g).
 // Waves per SIMD: the 16-bit instances take what the compiler gives (two
-// fit, <= 256 VGPRs); the 8-bit ones are held to 168 VGPRs so three fit,
-// which measured about 5 % faster (half the bytes per tile, so more waves
-// keep as many bytes in flight).
+// fit, <= 256 registers); the 8-bit one-head instances are held to 168 so
+// three fit, which measured about 5 % faster (half the bytes per tile, so
+// more waves keep as many bytes in flight); the 8-bit two-head instances
+// (a whole 4 KiB K or V tile per wave) run two per SIMD.
 // FUSE: the same split with the append of the step's new tokens folded in
 // (16-bit K/V, one kv head per wave; see paged_decode_append_split_kernel).
 template <int D, int BS, int GP, bool BF16, bool KV8, int HW, bool FUSE>
