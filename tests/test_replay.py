@@ -223,6 +223,47 @@ def test_plan_pairs_equal_half_the_heads(P, nw):
         R.plan(lens, 3, P, nw, heads_per_wave=2)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_covers_each_context_once(seed):
+    """Invariants of the split, whatever the lengths, heads, partition size and grid: the segments
+    of each (sequence, kv head) have slots 0, 1, ... in token order and tile [0, len) with no gap or
+    overlap; a segment holds at least one token and at most one chunk of tiles; fixed partitions
+    cut at multiples of P (ceil(len / P) segments per pair); and the tiles of all segments add up
+    to the list's total."""
+    rnd = random.Random(1000 + seed)
+    B = rnd.randint(1, 30)
+    lens = [rnd.choice([0, 1, 15, 16, 17, 128, 129, rnd.randint(0, 9000)]) for _ in range(B)]
+    hw = rnd.choice([1, 2])
+    hkv = hw * rnd.randint(1, 4)
+    P = rnd.choice([0, 0, 16, 48, 512])
+    nw = rnd.choice([1, 3, 4, 64, 2048])
+    items = R.plan(lens, hkv, P, nw, heads_per_wave=hw)
+    tiles = [-(-n // R.TILE) for n in lens]
+    total = sum(tiles) * (hkv // hw) if P == 0 else None
+    C = max(R.MIN_CHUNK, -(-total // nw)) if P == 0 else P // R.TILE
+    by_pair = {}
+    for s, g, k, lo, hi in items:
+        by_pair.setdefault((s, g), []).append((k, lo, hi))
+    for s in range(B):
+        for g in range(hkv):
+            segs = sorted(by_pair.get((s, g), []))
+            if lens[s] == 0:
+                assert segs == []
+                continue
+            assert [k for k, _, _ in segs] == list(range(len(segs)))
+            assert segs[0][1] == 0 and segs[-1][2] == lens[s]
+            for (_, lo, hi), (_, lo2, _) in zip(segs, segs[1:]):
+                assert hi == lo2
+            for _, lo, hi in segs:
+                assert lo < hi and -(-hi // R.TILE) - lo // R.TILE <= C
+            if P:
+                assert len(segs) == -(-lens[s] // P)
+                assert all(lo % P == 0 for _, lo, _ in segs)
+    if P == 0:
+        seg_tiles = sum(-(-hi // R.TILE) - lo // R.TILE for s, g, k, lo, hi in items if g % hw == 0)
+        assert seg_tiles == total
+
+
 # ---------------------------------------------------------------- host tier
 
 GOLDEN_TIER = os.path.join(os.path.dirname(__file__), "golden", "tiered_evict_to_cpu.json")
