@@ -456,3 +456,51 @@ def test_table_stride_wider_than_needed():
     out, lse = gpu_decode(wl, q, k, v, tab, ctx)
     ref_out, ref_lse = oracle.paged_decode_workload(wl, q, k, v)
     compare(out, lse, ref_out, ref_lse, what="wide table")
+
+
+def ramped_keys_(wl, k, q, heights, seed):
+    """Keys whose scores against q climb (or fall) along each context: K[t] = r(t) u_g + small
+    noise and every q head of kv group g equal to u_g (a unit direction per kv head), with r(t)
+    the profile `heights` gives over the positions of each sequence.  With r reaching a few
+    hundred the scores span tens of natural-log units, so the running reference of the online
+    softmax moves many times along a context (rising) or never after the first tile (falling)."""
+    g = torch.Generator().manual_seed(seed)
+    Hkv, D, bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+    u = torch.randn(Hkv, D, generator=g, dtype=torch.float64)
+    u /= u.norm(dim=1, keepdim=True)
+    G = wl.num_q_heads // Hkv
+    q.copy_(u.repeat_interleave(G, dim=0)[None].expand_as(q).to(q.dtype))
+    kc = torch.zeros(k.shape, dtype=torch.float64)
+    for s in range(wl.num_seqs):
+        n = int(wl.context_lens[s])
+        if n == 0:
+            continue
+        t = torch.arange(n)
+        blk = torch.from_numpy(wl.block_tables[s, (t // bs).numpy()].astype(np.int64))
+        r = heights(t.double(), n)
+        noise = 0.05 * torch.randn(n, Hkv, D, generator=g, dtype=torch.float64)
+        kc[blk, :, t % bs] = r[:, None, None] * u[None] + noise
+    k.copy_(kc.to(k.dtype))
+
+
+@pytest.mark.parametrize("profile", ["rising", "falling", "sawtooth"])
+@pytest.mark.parametrize("P", [0, 512])
+def test_score_ramps_exercise_the_rescale(profile, P):
+    """Scores that climb along the context move the softmax reference tile after tile (the rare
+    rescale path taken again and again), falling ones never after the first tile, a sawtooth
+    both; the 16-bit decode still matches the oracle within 2e-3, lse included."""
+    prof = {"rising": lambda t, n: 600.0 * t / max(n - 1, 1),
+            "falling": lambda t, n: 600.0 * (1 - t / max(n - 1, 1)),
+            "sawtooth": lambda t, n: 90.0 * torch.remainder(t, 700) / 100.0 + 40.0 * t / max(n - 1, 1)}[profile]
+    wl = W.make_workload(5, 8, 2, 128, 16, "bf16", [1, 17, 300, 1000, 4000], seed=77)
+    note(f"score ramp {profile}, P={P}")
+    q, k, v = W.make_values(wl, DEV)
+    qc, kc = q.cpu(), k.cpu()
+    ramped_keys_(wl, kc, qc, prof, seed=78)
+    q.copy_(qc)
+    k.copy_(kc)
+    tab, ctx = to_dev(wl)
+    out, lse = gpu_decode(wl, q, k, v, tab, ctx, partition_size=P)
+    ref_out, ref_lse = oracle.paged_decode(W.bits16(q), W.bits16(k), W.bits16(v), wl.block_tables, wl.context_lens,
+                                           wl.scale, num_kv_heads=2, block_size=16, dtype=oracle.BF16)
+    compare(out, lse, ref_out, ref_lse, what=f"{profile} P={P}")
