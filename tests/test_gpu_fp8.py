@@ -392,3 +392,43 @@ def test_fp8_entry_points_reject_mismatch():
         pool.attach_host_tier_fp8(2, kh, kh, sh, sh)
     assert e.value.code == pkv.PKV_EINVAL
     pool.close()
+
+
+@pytest.mark.parametrize("P", [0, 512])
+def test_fp8_decode_score_ramp(P):
+    """8-bit K whose scores climb along each context (K[t] = r(t) u + small noise, every q head
+    of a kv group equal to its unit direction u, r rising to 600): each block's K scale grows
+    with the ramp, so the per-tile scale folded into the score and the softmax rescale both
+    change tile after tile.  The E4M3 decode (two kv heads per wave) matches the oracle on the
+    same codes and scales within 2e-3, lse included."""
+    wl = W.make_workload(5, 8, 2, 128, 16, "bf16", [1, 17, 300, 1000, 4000], seed=91)
+    note(f"8-bit decode on a score ramp, P={P}")
+    g = torch.Generator().manual_seed(92)
+    Hkv, D, bs, NB = wl.num_kv_heads, wl.head_dim, wl.block_size, wl.num_blocks
+    u = torch.randn(Hkv, D, generator=g, dtype=torch.float64)
+    u /= u.norm(dim=1, keepdim=True)
+    q = u.repeat_interleave(wl.num_q_heads // Hkv, dim=0)[None].expand(wl.num_seqs, -1, -1)
+    q = q.to(torch.bfloat16).contiguous().to(DEV)
+    k16 = torch.zeros((NB, Hkv, bs, D), dtype=torch.float64)
+    for s in range(wl.num_seqs):
+        n = int(wl.context_lens[s])
+        t = torch.arange(n)
+        blk = torch.from_numpy(wl.block_tables[s, (t // bs).numpy()].astype(np.int64))
+        r = 600.0 * t.double() / max(n - 1, 1)
+        k16[blk, :, t % bs] = r[:, None, None] * u[None] + 0.05 * torch.randn(n, Hkv, D, generator=g, dtype=torch.float64)
+    k16 = k16.to(torch.bfloat16).to(DEV)
+    v16 = W.fill_normal_(torch.empty_like(k16), 93)
+    kc = torch.empty(k16.shape, dtype=torch.uint8, device=DEV)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((NB, Hkv), dtype=torch.float32, device=DEV)
+    vs = torch.empty_like(ks)
+    items = torch.stack([torch.arange(NB, dtype=torch.int32, device=DEV)] * 2
+                        + [torch.full((NB,), bs, dtype=torch.int32, device=DEV)], dim=1).contiguous()
+    pkv.quantize_fp8(items, k16, v16, kc, vc, ks, vs)
+    tab = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(DEV)
+    ctx = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(DEV)
+    lse = torch.empty((wl.num_seqs, wl.num_q_heads), device=DEV)
+    out = pkv.decode_fp8(q, kc, vc, ks, vs, tab, ctx, wl.scale, wl.max_context_len, partition_size=P, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = ref_fp8(wl, q, kc, vc, ks, vs)
+    compare(out, lse, ro, rl, f"8-bit ramp P={P}")
