@@ -293,7 +293,7 @@ int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t tabl
  * sequence-major, cut into chunks of C tiles; the grid's waves take the chunks
  * in turn.  (With 8-bit K/V and an even kv head count a wave takes two
  * adjacent kv heads of each tile: the list then runs over (sequence, kv head
- * pair, tile), and both heads of a pair share the pair's segments.)  Balanced mode (partition_size 0): C = max(8, ceil(tiles / waves)),
+ * pair, tile), and both heads of a pair share the pair's segments.)  Balanced mode (partition_size 0): C = max(4, ceil(tiles / waves)),
  * so every wave gets the same share whatever the lengths.  Fixed mode
  * (partition_size P > 0): C = P / 16 and each (sequence, kv head) is padded to
  * whole chunks, so a chunk is exactly the partition [p P, min((p + 1) P, len)).

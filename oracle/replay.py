@@ -42,7 +42,7 @@ What is replayed, from the definitions:
     -- cut into chunks of C tiles.  With a
     fixed partition size P, C = P / 16 and pt_s = ceil(nt_s / C) * C (so a
     chunk is the partition [p*P, min((p+1)*P, n)) of one (s, g)); balanced,
-    pt_s = nt_s and C = max(8, ceil(T / W)) for W waves and T tiles in all.
+    pt_s = nt_s and C = max(4, ceil(T / W)) for W waves and T tiles in all.
     A segment is the part of one chunk inside one (s, g); its slot is the
     chunk index minus first(s, g) // C.  Segments are listed in (s, g, slot)
     order.
@@ -328,7 +328,7 @@ class PoolReplay:
 
 
 TILE = 16
-MIN_CHUNK = 8
+MIN_CHUNK = 4
 
 
 def plan(context_lens: Sequence[int], num_kv_heads: int, partition_size: int, num_waves: int = 1,

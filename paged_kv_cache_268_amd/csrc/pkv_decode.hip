@@ -63,7 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
-constexpr int kMinChunk = 8;           // balanced split: at least 8 tiles (128 tokens) per chunk
+constexpr int kMinChunk = 4;           // balanced split: at least 4 tiles (64 tokens) per chunk
 constexpr int kMergeWidePairs = 1024;  // merge: a workgroup per pair up to this many pairs...
 constexpr int kMergeWideSegments = 32; // ...or for fixed partitions with more slots than this
 constexpr float kLog2e = 1.4426950408889634f;

@@ -960,7 +960,7 @@ int kv_validate_tables(int32_t n_seqs, const int32_t* block_tables, int32_t tabl
 namespace {
 
 constexpr int32_t kTile = pkv::kTileTokens;
-constexpr int32_t kMinChunk = 8;            // must equal the kernel's balanced-split minimum
+constexpr int32_t kMinChunk = 4;            // must equal the kernel's balanced-split minimum
 
 struct Plan {
     int32_t part_size = 0;                  // 0 = balanced split

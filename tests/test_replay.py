@@ -180,15 +180,18 @@ def test_plan_fixed_partitions():
 
 def test_plan_balanced_worked_example():
     # Two sequences of 40 and 200 tokens, one kv head: 3 + 13 = 16 tiles.
-    # 2 waves -> C = max(8, 8) = 8 tiles: chunk 0 = tiles 0..7, chunk 1 = 8..15.
+    # 2 waves -> C = max(4, 8) = 8 tiles: chunk 0 = tiles 0..7, chunk 1 = 8..15.
     # Sequence 0 (tiles 0..2) is whole in chunk 0; sequence 1 starts at tile 3:
     # its tiles 0..4 are in chunk 0 (slot 0), tiles 5..12 in chunk 1 (slot 1).
     items = R.plan([40, 200], num_kv_heads=1, partition_size=0, num_waves=2)
     assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200)]
-    # Many waves: the chunk never drops below 8 tiles (128 tokens).
+    # Many waves: the chunk never drops below 4 tiles (64 tokens).  Chunks 0..3 are list
+    # positions 0-3, 4-7, 8-11, 12-15: sequence 1 (positions 3..15) gets its tile 0 in
+    # chunk 0, tiles 1-4, 5-8 and 9-12 in chunks 1, 2, 3 (tokens 16, 80, 144 apart).
     items = R.plan([40, 200], num_kv_heads=1, partition_size=0, num_waves=1000)
-    assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 80), (1, 0, 1, 80, 200)]
-    # One wave: C = max(8, 34) = 34 tiles, everything in one chunk, every (seq, head) whole.
+    assert items == [(0, 0, 0, 0, 40), (1, 0, 0, 0, 16), (1, 0, 1, 16, 80), (1, 0, 2, 80, 144),
+                     (1, 0, 3, 144, 200)]
+    # One wave: C = max(4, 34) = 34 tiles, everything in one chunk, every (seq, head) whole.
     items = R.plan([40, 200, 0, 7], num_kv_heads=2, partition_size=0, num_waves=1)
     assert items == [(0, 0, 0, 0, 40), (0, 1, 0, 0, 40), (1, 0, 0, 0, 200), (1, 1, 0, 0, 200),
                      (3, 0, 0, 0, 7), (3, 1, 0, 0, 7)]
@@ -446,7 +449,7 @@ def test_append_tokens_all_or_nothing():
 
 def test_segment_rows_worked_examples():
     """Balanced: lengths 5, 700, 40, two kv heads, 4 waves: 1 + 44 + 3 tiles per kv head, T = 96,
-    C = max(8, 24) = 24.  Pair (1, 1) starts at list position 46 and spans chunks 1, 2, 3; its
+    C = max(4, 24) = 24.  Pair (1, 1) starts at list position 46 and spans chunks 1, 2, 3; its
     pair index is 3, so its rows are 4, 5, 6.  Fixed P = 128 (C = 8 tiles): lengths 300, 40 pad to
     24 and 8 tiles; pair (0, 1) starts at 24 (chunks 3, 4, 5, pair 1: rows 4, 5, 6), pair (1, 1) at
     56 (chunk 7, pair 3: row 10)."""
